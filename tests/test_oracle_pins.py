@@ -1,0 +1,309 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each check compares the oracle with something it does not compute the same
+way: a pure-Python brute force on tiny inputs, torch's own RMSNorm and
+scaled-dot-product attention (fp64, CPU) with autograd, central finite
+differences, closed forms of special inputs, invariants of softmax, and values
+printed on the pages (tests/golden/).  tests/test_oracle_mutants.py checks that
+plausible mistakes planted in the oracle fail at least one of these.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as A
+from oracle import schedule as S
+
+EPS = 1e-6
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_force_fwd(q, k, v, window, causal, eps):
+    """Triple loop over (b, h, i) with explicit per-key visibility tests."""
+    B, T, H, D = q.shape
+    o = np.zeros((B, T, H, v.shape[3]))
+    lse = np.zeros((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            def normed(x):
+                ms = sum(float(t) * float(t) for t in x) / len(x)
+                return [float(t) / math.sqrt(ms + eps) for t in x]
+            qn = [normed(q[b, t, h]) for t in range(T)]
+            kn = [normed(k[b, t, h]) for t in range(T)]
+            for i in range(T):
+                keys = []
+                for j in range(T):
+                    if causal:
+                        ok = j <= i and (window < 0 or i - j <= window)
+                    else:
+                        ok = window < 0 or abs(i - j) <= window
+                    if ok:
+                        keys.append(j)
+                s = [sum(a * c for a, c in zip(qn[i], kn[j])) / math.sqrt(D) for j in keys]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = sum(e)
+                lse[b, h, i] = m + math.log(z)
+                for jj, j in enumerate(keys):
+                    o[b, i, h] += (e[jj] / z) * v[b, j, h]
+    return o, lse
+
+
+@pytest.mark.parametrize("T,D,W,causal", [
+    (1, 4, 0, True), (7, 4, 0, True), (9, 8, 3, True), (12, 4, 1, True),
+    (11, 8, 10, True), (11, 8, 11, True), (10, 4, -1, True), (13, 8, 5, False),
+    (8, 4, -1, False),
+])
+def test_fwd_matches_brute_force(T, D, W, causal):
+    q, k, v = (_rand((2, T, 2, D), s) for s in (1, 2, 3))
+    o, lse = oracle.attention_fwd(q, k, v, W, causal, EPS)
+    ob, lb = brute_force_fwd(q, k, v, W, causal, EPS)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-13)
+
+
+def test_n_visible_brute_force_and_closed_form():
+    for T in (1, 2, 5, 16, 33):
+        for W in (-1, 0, 1, 3, T - 2, T - 1, T, T + 5):
+            if W < -1:
+                continue
+            brute = sum(1 for i in range(T) for j in range(T)
+                        if j <= i and (W < 0 or i - j <= W))
+            closed = sum((i if W < 0 else min(i, W)) + 1 for i in range(T))
+            assert oracle.n_visible(T, W) == brute == closed
+            brute_nc = sum(1 for i in range(T) for j in range(T) if W < 0 or abs(i - j) <= W)
+            assert oracle.n_visible(T, W, causal=False) == brute_nc
+
+
+def test_n_visible_workload_sizes():
+    # closed form sum_i (min(i, W) + 1) at the five workloads' shapes
+    assert oracle.n_visible(128, 64) == 6240
+    assert oracle.n_visible(2048, 1024) == 1574400
+    assert oracle.n_visible(2048, 2048) == 2098176 == 2048 * 2049 // 2
+    assert oracle.n_visible(8192, 4096) == 25171968
+    assert oracle.n_visible(8192, 8192) == 33558528 == 8192 * 8193 // 2
+
+
+# ---------------------------------------------------------- library routines
+
+def test_rms_norm_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = _rand((5, 7, 3, 16), 4, 3.0)
+    for eps in (1e-6, 1e-2, 0.5):
+        xh, r = oracle.rms_norm(x, eps)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (16,), eps=eps).numpy()
+        np.testing.assert_allclose(xh, ref, rtol=1e-14, atol=1e-14)
+        ms = np.mean(x * x, axis=-1)
+        np.testing.assert_allclose(np.mean(xh * xh, axis=-1), ms / (ms + eps), rtol=1e-13)
+
+
+def _torch_reference(q, k, v, do, window, causal, eps):
+    """RMSNorm + scaled_dot_product_attention with a boolean band mask, fp64 CPU."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    B, T, H, D = q.shape
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    qn = F.rms_norm(qt, (D,), eps=eps).transpose(1, 2)
+    kn = F.rms_norm(kt, (D,), eps=eps).transpose(1, 2)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    if causal:
+        mask = (j <= i) & ((i - j <= window) if window >= 0 else torch.ones(T, T, dtype=torch.bool))
+    else:
+        mask = (abs(i - j) <= window) if window >= 0 else torch.ones(T, T, dtype=torch.bool)
+    o = F.scaled_dot_product_attention(qn, kn, vt.transpose(1, 2), attn_mask=mask)
+    o = o.transpose(1, 2)
+    o.backward(torch.tensor(do))
+    return o.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("T,D,W,causal", [
+    (40, 16, 7, True), (40, 16, 0, True), (40, 16, -1, True), (33, 8, 39, True),
+    (24, 16, 5, False), (64, 32, 31, True),
+])
+def test_fwd_bwd_match_torch_sdpa(T, D, W, causal):
+    q, k, v, do = (_rand((2, T, 3, D), s) for s in (5, 6, 7, 8))
+    o_ref, dq_ref, dk_ref, dv_ref = _torch_reference(q, k, v, do, W, causal, EPS)
+    o, _ = oracle.attention_fwd(q, k, v, W, causal, EPS)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, W, causal, EPS)
+    for a, b in ((o, o_ref), (dq, dq_ref), (dk, dk_ref), (dv, dv_ref)):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+# -------------------------------------------------------- finite differences
+
+@pytest.mark.parametrize("W,causal", [(5, True), (-1, True), (3, False)])
+def test_bwd_matches_finite_differences(W, causal):
+    T, D = 16, 8
+    q, k, v, do = (_rand((1, T, 1, D), s) for s in (9, 10, 11, 12))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, W, causal, EPS)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention_fwd(qq, kk, vv, W, causal, EPS)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.max(np.abs(num - grad)) / np.max(np.abs(grad))
+        assert err < 1e-7, (which, err)
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("W", [0, 1, 4, 17, -1])
+def test_identical_keys_closed_form(W):
+    """All keys equal: P is uniform over the visible keys, so o_i is the mean of
+    the visible values, lse_i = s_i + ln(#visible keys) and dq = 0."""
+    T, D = 24, 16
+    q, v, do = (_rand((1, T, 2, D), s) for s in (13, 14, 15))
+    k = np.broadcast_to(_rand((1, 1, 2, D), 16), (1, T, 2, D)).copy()
+    o, lse = oracle.attention_fwd(q, k, v, W, True, EPS)
+    dq, _, _ = oracle.attention_bwd(q, k, v, do, W, True, EPS)
+    qh, _ = oracle.rms_norm(q, EPS)
+    kh, _ = oracle.rms_norm(k[:, :1], EPS)
+    for h in range(2):
+        for i in range(T):
+            n = (i if W < 0 else min(i, W)) + 1
+            s_i = float(qh[0, i, h] @ kh[0, 0, h]) / math.sqrt(D)
+            assert abs(lse[0, h, i] - (s_i + math.log(n))) < 1e-12
+            np.testing.assert_allclose(o[0, i, h], v[0, i - n + 1:i + 1, h].mean(axis=0),
+                                       rtol=0, atol=1e-13)
+    assert np.max(np.abs(dq)) < 1e-12
+
+
+def test_window_zero_is_identity():
+    """W = 0: each query sees only itself, so o = v, lse_i = s_ii, dv = dO, dq = dk = 0."""
+    T, D = 20, 16
+    q, k, v, do = (_rand((2, T, 2, D), s) for s in (17, 18, 19, 20))
+    o, lse = oracle.attention_fwd(q, k, v, 0, True, EPS)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0, True, EPS)
+    assert np.array_equal(o, v)
+    qh, _ = oracle.rms_norm(q, EPS)
+    kh, _ = oracle.rms_norm(k, EPS)
+    diag = np.einsum("bthd,bthd->bht", qh, kh) / math.sqrt(D)
+    np.testing.assert_allclose(lse, diag, rtol=0, atol=1e-14)
+    assert np.array_equal(dv, do)
+    assert np.max(np.abs(dq)) < 1e-13 and np.max(np.abs(dk)) < 1e-13
+
+
+@pytest.mark.parametrize("W,causal", [(6, True), (-1, True), (4, False)])
+def test_one_hot_value_marks_visibility(W, causal):
+    """v_{j*} = e_0 and all other values 0: o_{i,0} = P_{i,j*}, positive iff visible."""
+    T, D = 30, 8
+    q, k = _rand((1, T, 1, D), 21), _rand((1, T, 1, D), 22)
+    mask = A.visible_mask(T, W, causal)
+    for jstar in (0, 5, 17, T - 1):
+        v = np.zeros((1, T, 1, D))
+        v[0, jstar, 0, 0] = 1.0
+        o, _ = oracle.attention_fwd(q, k, v, W, causal, EPS)
+        assert np.array_equal(o[0, :, 0, 0] > 0, mask[:, jstar])
+        assert np.all(o[0, :, 0, 1:] == 0)
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("W,causal", [(0, True), (5, True), (-1, True), (3, False)])
+def test_softmax_rows_and_exact_zeros(W, causal):
+    T, D = 50, 16
+    q, k = _rand((1, T, 1, D), 23, 4.0), _rand((1, T, 1, D), 24, 4.0)
+    p, lse = oracle.probabilities(q, k, 0, 0, W, causal, EPS)
+    mask = A.visible_mask(T, W, causal)
+    assert np.all(p[~mask] == 0.0)
+    assert np.all(p[mask] > 0) and np.all(p[mask] <= 1.0)
+    assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-14
+    s = oracle.scores(q, k, 0, 0, W, causal, EPS)
+    np.testing.assert_allclose(lse, np.log(np.sum(np.exp(np.where(mask, s, -np.inf)), axis=1)),
+                               rtol=0, atol=1e-12)
+
+
+def test_logit_bound():
+    """QK-norm bounds every scaled logit by sqrt(D), whatever the input scale."""
+    for D, scale in ((8, 1e-3), (64, 1.0), (128, 300.0)):
+        q, k = _rand((1, 64, 1, D), 25, scale), _rand((1, 64, 1, D), 26, scale)
+        k[0, 10] = q[0, 40] * 7.0   # an aligned pair reaches close to the bound
+        s = oracle.scores(q, k, 0, 0, -1, True, EPS)
+        fin = s[np.isfinite(s)]
+        assert np.all(np.abs(fin) < math.sqrt(D))
+        # parallel q and k: s = sqrt(D) * sqrt(ms_q/(ms_q+eps)) * sqrt(ms_k/(ms_k+eps))
+        mq = np.mean(q[0, 40, 0] ** 2)
+        mk = np.mean(k[0, 10, 0] ** 2)
+        want = math.sqrt(D) * math.sqrt(mq / (mq + EPS)) * math.sqrt(mk / (mk + EPS))
+        assert abs(s[40, 10] - want) < 1e-12
+
+
+def test_large_window_equals_full_causal():
+    T, D = 37, 8
+    q, k, v, do = (_rand((1, T, 2, D), s) for s in (27, 28, 29, 30))
+    ref = oracle.attention_fwd(q, k, v, -1, True, EPS)
+    refb = oracle.attention_bwd(q, k, v, do, -1, True, EPS)
+    for W in (T - 1, T, 4 * T):
+        o, lse = oracle.attention_fwd(q, k, v, W, True, EPS)
+        assert np.array_equal(o, ref[0]) and np.array_equal(lse, ref[1])
+        for a, b in zip(oracle.attention_bwd(q, k, v, do, W, True, EPS), refb):
+            assert np.array_equal(a, b)
+
+
+def test_sampled_rows_match_full():
+    T, D, W = 70, 16, 9
+    q, k, v, do = (_rand((2, T, 2, D), s) for s in (31, 32, 33, 34))
+    o, lse = oracle.attention_fwd(q, k, v, W, True, EPS)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, W, True, EPS)
+    rows = [0, 3, 9, 10, 45, T - 1]
+    for b, h in ((0, 0), (1, 1)):
+        orow, lrow = oracle.fwd_rows(q, k, v, b, h, rows, W, True, EPS)
+        np.testing.assert_allclose(orow, o[b, rows, h], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lrow, lse[b, h, rows], rtol=0, atol=1e-14)
+        sq, sk, sv = oracle.bwd_rows(q, k, v, do, b, h, rows, rows, W, True, EPS)
+        np.testing.assert_allclose(sq, dq[b, rows, h], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sk, dk[b, rows, h], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sv, dv[b, rows, h], rtol=0, atol=1e-12)
+
+
+def test_invalid_window_rejected():
+    with pytest.raises(ValueError):
+        A.visible_mask(8, -2)
+
+
+# ------------------------------------------------------- values on the pages
+
+def test_window_schedule_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "window_schedule.json")))
+    for c in g["cases"]:
+        w = S.layer_windows(c["pattern"], c["n_layer"], c["seq_len"])
+        assert w == c["windows"]
+        assert [i for i, x in enumerate(w) if x == c["seq_len"]] == c["global_layers"]
+
+
+def test_window_schedule_rules():
+    assert S.layer_windows("SSSS", 4, 2048) == [1024, 1024, 1024, 2048]   # last forced L
+    assert S.layer_windows("L", 3, 512) == [512, 512, 512]
+    assert S.layer_windows("sl", 5, 1000) == [500, 1000, 500, 1000, 1000]
+    assert S.layer_windows("SSSL", 4, 8192) == [4096, 4096, 4096, 8192]
+    with pytest.raises(ValueError):
+        S.layer_windows("SXL", 4, 2048)
+
+
+def test_flops_per_token_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "flops_per_token.json")))
+    pc = g["param_counts"]
+    assert sum(v for k, v in pc.items() if k != "total") == pc["total"]
+    windows = S.layer_windows(g["pattern"], g["n_layer"], g["seq_len"])
+    f = S.flops_per_token(pc["transformer_matrices"], pc["lm_head"], g["n_head"],
+                          g["head_dim"], windows, g["seq_len"])
+    assert f == g["flops_per_token"]

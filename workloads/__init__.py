@@ -1,0 +1,110 @@
+"""Seeded synthetic workloads: shapes, seeds and value distributions only.
+
+This module is shared by the oracle side and the HIP side of the tests and the
+bench. It holds no attention arithmetic: it draws Gaussian tensors from a seed,
+rounds them to bf16 and names the five workloads. Each side turns a layer
+pattern into windows with its own code.
+
+The shapes are those of the pages' training run: the model config line of
+"自主AI研究员Autoresearch彻夜炼丹" (watermelonwater.tech) gives sequence_len 2048,
+n_head = n_kv_head = 4, n_embd 512 (so head_dim 128) and window_pattern SSSL; the
+tutorial "Autoresearch 深度教程" (gitee brotherddc/autoresearch) §10.1 gives the
+device batch 128 and the per-layer window rule.  The pages train on real text
+activations, which are not available; seeded N(0, sigma^2) bf16 tensors of the
+same shapes stand in for them.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Tuple
+
+import numpy as np
+
+EPS = 1e-6
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even. Inputs are finite."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def gaussian_bf16(shape: Tuple[int, ...], rng: np.random.Generator, sigma: float = 1.0) -> np.ndarray:
+    """Draw N(0, sigma^2) in fp32 and round to bf16; returns the uint16 bit patterns."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x = x * np.float32(sigma)
+    return round_to_bf16_bits(x)
+
+
+@dataclass
+class LayerInputs:
+    """bf16 bit patterns (uint16) in the [B, T, H, D] layout."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+
+    def as_f32(self):
+        return tuple(bf16_bits_to_f32(t) for t in (self.q, self.k, self.v, self.do))
+
+
+def make_layer_inputs(B: int, T: int, H: int, D: int, seed: int,
+                      sigma_qkv: float = 1.0, sigma_do: float = 1.0) -> LayerInputs:
+    """Q, K, V then dO, drawn in that order from one default_rng(seed) stream."""
+    rng = np.random.default_rng(seed)
+    shape = (B, T, H, D)
+    q = gaussian_bf16(shape, rng, sigma_qkv)
+    k = gaussian_bf16(shape, rng, sigma_qkv)
+    v = gaussian_bf16(shape, rng, sigma_qkv)
+    do = gaussian_bf16(shape, rng, sigma_do)
+    return LayerInputs(q, k, v, do)
+
+
+@dataclass
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    pattern: str              # per-layer pattern, e.g. "SSSL"; "W<n>" rows use an explicit window
+    n_layer: int
+    seed0: int
+    sigma_qkv: float = 1.0
+    sigma_do: float = 1.0
+    explicit_window: int | None = None   # for the single-layer configs
+    eps: float = EPS
+    notes: str = ""
+
+    def seed(self, layer: int) -> int:
+        return self.seed0 + layer
+
+
+WORKLOADS: List[Workload] = [
+    Workload("tiny", B=1, T=128, H=2, D=64, pattern="S", n_layer=1, seed0=0,
+             explicit_window=64,
+             notes="parity case the oracle finishes in seconds; window 64 = T/2"),
+    Workload("s_layer", B=8, T=2048, H=4, D=128, pattern="S", n_layer=1, seed0=1,
+             explicit_window=1024, notes="one sliding-window layer, window T/2"),
+    Workload("l_layer", B=8, T=2048, H=4, D=128, pattern="L", n_layer=1, seed0=2,
+             explicit_window=2048, notes="one full-causal layer, window T"),
+    Workload("sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=1000,
+             notes="depth-8 SSSL stack: 8 independent layers, throughput summed"),
+    Workload("long", B=4, T=8192, H=8, D=128, pattern="SSSL", n_layer=4, seed0=2000,
+             sigma_qkv=2.0 ** 0.5,
+             notes="one SSSL period at T=8192; Q/K/V variance 2, dO variance 1"),
+]
+
+
+def workload(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)

@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of QK-RMSNorm causal sliding-window attention, forward + backward,
+on one MI355X, through the C ABI of libswattn.
+
+A step is one pass of the whole hot path over one batch: the forward of every
+layer of the workload, then the backward of every layer in reverse order.  The
+default workload is the depth-8 SSSL stack (8 independent layers, windows
+1024 x3, 2048, 1024 x3, 2048; B=64, T=2048, H=4, D=128, bf16), the shape of the
+pages' 5-minute training run.  Inputs are synthetic, seeded and already in HBM
+when the timed region starts.
+
+Effective FLOPs (F14): 14 * D * N_vis per (batch, head) and layer, N_vis the
+number of visible (query, key) pairs: 4 D for the forward (QK^T, PV) and 10 D
+for the backward with recomputation (QK^T, dP, dV, dQ, dK).  Masked pairs,
+extra recomputation and the RMSNorm arithmetic are not credited.
+
+    python bench.py [--steps K] [--warmup W] [--workload sssl_stack]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (AMD's published figure)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "attn fwd+bwd effective TFLOP/s & % bf16 MFMA peak, T=2048 H=4 D=128 SSSL"
+
+# algorithmic work credited to each kernel, per visible pair (FLOPs = c * D * N_vis)
+# or per launch bytes for the memory-bound passes
+KERNELS = {
+    0: ("k_scale", "hbm"),
+    1: ("attn_fwd", "mfma"),
+    2: ("bwd_prep", "hbm"),
+    3: ("bwd_dkdv", "mfma"),
+    4: ("bwd_dq", "mfma"),
+}
+FLOPS_PER_PAIR_D = {1: 4, 3: 8, 4: 2}
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sliding_window_causal_qk_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_units(kid, B, T, H, D, n_vis):
+    """(amount, unit) of algorithmic work of one launch of kernel `kid`."""
+    E = B * T * H * D
+    if kid in FLOPS_PER_PAIR_D:
+        return FLOPS_PER_PAIR_D[kid] * D * n_vis * B * H, "flop"
+    if kid == 0:   # read K, write the key scales
+        return 2 * E + 4 * B * H * T, "byte"
+    # bwd_prep: read q, k, o, dO; write q_hat and three [B, H, T] fp32 rows
+    return 4 * 2 * E + 2 * E + 3 * 4 * B * H * T, "byte"
+
+
+def cpu_baseline(wl, windows, budget_s):
+    """Time the fp64 oracle (as it stands) on (batch, head) slices of the
+    workload's layers, cycling through the layer windows, for about budget_s."""
+    import numpy as np
+    import oracle
+    from workloads import make_layer_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    flops = 0.0
+    n = 0
+    dt = 0.0
+    layer = 0
+    while dt < budget_s:
+        W = windows[layer % len(windows)]
+        inp = make_layer_inputs(1, wl.T, 1, wl.D, wl.seed(layer), wl.sigma_qkv, wl.sigma_do)
+        q, k, v, do = inp.as_f32()
+        ts = time.perf_counter()
+        oracle.attention_fwd(q, k, v, W, True, wl.eps)
+        oracle.attention_bwd(q, k, v, do, W, True, wl.eps)
+        dt += time.perf_counter() - ts
+        flops += 14 * wl.D * oracle.n_visible(wl.T, W)
+        n += 1
+        layer += 1
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n} (batch, head) slices of T={wl.T}, D={wl.D} cycling through the layer "
+                   f"windows {sorted(set(windows))}, fp64 numpy forward + backward, {dt:.1f} s "
+                   f"of oracle time; F14 credited per slice"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sssl_stack")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this attention path has no multi-GPU mode: every (batch, head) is independent, so a "
+              "data-parallel run is N independent copies of the one-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sliding_window_causal_qk_amd as sw
+    from workloads import make_layer_inputs_device, workload
+
+    wl = workload(args.workload)
+    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    if wl.explicit_window is not None:
+        windows = [wl.explicit_window] * wl.n_layer
+    else:
+        windows = sw.layer_windows(wl.pattern, wl.n_layer, T)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {wl.name}: B={B} T={T} H={H} D={D} windows={windows}", file=sys.stderr, flush=True)
+
+    layers = []
+    for l, W in enumerate(windows):
+        q, k, v, do = make_layer_inputs_device(B, T, H, D, wl.seed(l), wl.sigma_qkv, wl.sigma_do, dev)
+        layers.append(dict(
+            W=W, q=q, k=k, v=v, do=do,
+            o=torch.empty_like(q), lse=torch.empty((B, H, T), dtype=torch.float32, device=dev),
+            dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+            wsf=torch.empty(sw.fwd_workspace_bytes(B, T, H, D), dtype=torch.uint8, device=dev),
+            wsb=torch.empty(sw.bwd_workspace_bytes(B, T, H, D), dtype=torch.uint8, device=dev),
+            n_vis=sw.visible_pairs(T, W),
+        ))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for L in layers:
+            sw.attn_fwd(L["q"], L["k"], L["v"], L["W"], True, wl.eps,
+                        out=L["o"], lse=L["lse"], workspace=L["wsf"], stream=stream)
+        for L in reversed(layers):
+            sw.attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], L["W"], True, wl.eps,
+                        dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["wsb"], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    lib = sw.lib()
+    sw.check(lib.attn_profile_enable(1), "attn_profile_enable")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    import ctypes
+    per_kernel = {}
+    for kid, (name, bound) in KERNELS.items():
+        tot = ctypes.c_double()
+        cnt = ctypes.c_longlong()
+        sw.check(lib.attn_profile_read(kid, ctypes.byref(tot), ctypes.byref(cnt)), "attn_profile_read")
+        if cnt.value == 0:
+            continue
+        work = 0.0
+        unit = None
+        for L in layers:
+            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"])
+            work += amt * args.steps
+        secs = tot.value * 1e-3
+        if unit == "flop":
+            achieved, u, peak = work / secs / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
+        else:
+            achieved, u, peak = work / secs / 1e9, "GB/s", PEAK_HBM_GBS
+        per_kernel[name] = dict(avg_us=tot.value * 1e3 / cnt.value, launches=cnt.value,
+                                total_ms_per_step=tot.value / args.steps, bound=bound,
+                                achieved=achieved, unit=u, peak=peak, frac=achieved / peak,
+                                work_per_launch=work / cnt.value, work_unit=unit)
+    sw.check(lib.attn_profile_enable(0), "attn_profile_enable")
+
+    flops_step = sum(14 * D * L["n_vis"] * B * H for L in layers)
+    flops12_step = sum(12 * D * L["n_vis"] * B * H for L in layers)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    dom_name = max(per_kernel, key=lambda n: per_kernel[n]["total_ms_per_step"])
+    dom = per_kernel[dom_name]
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if os.path.exists(tf):
+        try:
+            rec = json.load(open(tf))
+            if rec.get("sources_sha") == kernel_sources_sha() and dom_name in rec.get("kernels", {}):
+                traffic = rec["kernels"][dom_name].get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 3),
+                "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
+                "traffic": traffic,
+                "work_per_launch": dom["work_per_launch"], "work_unit": dom["work_unit"],
+                "avg_launch_us": round(dom["avg_us"], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, windows, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "D": D, "pattern": wl.pattern,
+                   "n_layer": len(windows), "windows": windows, "eps": wl.eps,
+                   "flop_convention": "F14 = 14*D*N_vis per (batch, head, layer)",
+                   "flops_per_step": flops_step, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "value_f12": round(flops12_step / (ms_per_step * 1e-3) / 1e12, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in per_kernel.items()},
+        "kernel_sources_sha": kernel_sources_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * swattn — causal sliding-window attention with RMSNorm on Q and K, forward
+ * and backward, for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation is the attention of the single-GPU training step described in
+ * the pages on karpathy/autoresearch:
+ *   - "Autoresearch 深度教程：AI 自主训练研究指南" (gitee brotherddc/autoresearch),
+ *     §5.2.2: each layer attends through a (W, 0) window, W = T/2 for "S"
+ *     layers and W = T for "L" layers, pattern "SSSL", last layer always "L";
+ *     §5.2.1: the window is handed to FlashAttention-3;
+ *     §7.3: `norm(x)` is an RMSNorm over the last axis with no weight.
+ *   - okx.com line-by-line review of karpathy/autoresearch: queries and keys
+ *     are RMS-normalised right before the attention product (QK-norm).
+ *
+ * For every batch b and head h, with x[t] the D-vector of position t:
+ *   q_hat = q / sqrt(mean(q^2) + eps),  k_hat likewise (unit gain)
+ *   key j is visible to query i  iff  0 <= i - j <= W   (W = -1: unbounded)
+ *   s_ij  = q_hat_i . k_hat_j / sqrt(D)
+ *   o_i   = sum_j softmax_j(s_ij) v_j,   lse_i = ln sum_j exp(s_ij)
+ * The softmax scale 1/sqrt(D) is FlashAttention's default; the pages state no
+ * other.
+ *
+ * Layout: q, k, v, o, dout, dq, dk, dv are contiguous bf16 [B, T, H, D]
+ * (row-major; element (b, t, h, d) at ((b*T + t)*H + h)*D + d), the layout the
+ * tutorial's CausalSelfAttention views its projections in.  lse is fp32
+ * [B, H, T].  All tensor and workspace pointers are DEVICE pointers owned by
+ * the caller and must be 16-byte aligned (workspaces 256-byte aligned).
+ * Outputs are overwritten, never accumulated, and must not alias inputs.
+ *
+ * Threading / streams: calls are asynchronous on `stream` (a hipStream_t; NULL
+ * means the default stream).  The library allocates no device memory, does
+ * not synchronise, and keeps no mutable global state apart from the opt-in
+ * timing counters below; concurrent calls on
+ * different streams are safe if their buffers are disjoint.
+ *
+ * Errors: every argument check runs on the host before any HIP call; a
+ * rejected call returns its status and touches nothing.  A failed launch
+ * returns ATTN_ERR_HIP.  Faults during execution surface at the caller's next
+ * synchronisation, as for any asynchronous HIP work.
+ */
+#ifndef SWATTN_H
+#define SWATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad eps / window, misalignment */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_bytes */
+  ATTN_ERR_HIP = 4          /* a HIP launch failed */
+};
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* attn_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int attn_version(void);
+
+/*
+ * Per-layer windows ("Autoresearch 深度教程" §5.2.2).  Layer l takes the
+ * character pattern[l % strlen(pattern)]: 'S' gives seq_len / 2, 'L' gives
+ * seq_len (either case accepted); the last layer is always seq_len.  Writes
+ * n_layer ints to windows_out (host memory).
+ * Returns ATTN_ERR_INVALID_ARG for a NULL/empty pattern, a character other
+ * than S/L, n_layer < 1, seq_len < 1 or a NULL windows_out.
+ */
+int attn_layer_windows(const char* pattern, int n_layer, int seq_len, int* windows_out);
+
+/*
+ * Number of visible (query, key) pairs of one (batch, head) slice of length T
+ * under `window` (-1 = unbounded), causal only.  Returns -1 for T < 0 or
+ * window < -1.  This is the pair count the effective FLOP figures use.
+ */
+long long attn_visible_pairs(int T, int window);
+
+/*
+ * Band tile enumeration used by the kernels.  The rows of a (T x T)
+ * query-by-key grid are cut into blocks of `rows` (queries if by_key == 0,
+ * keys if by_key == 1) and the other axis into blocks of `cols`.  For every
+ * row block r (n = ceil(T / rows) of them) writes, to host arrays of length n:
+ *   first[r], last[r] : the first and last column block the kernels visit
+ *                       (last < first when none),
+ *   n_partial[r]      : how many of the visited blocks need the element mask,
+ *   n_empty[r]        : how many of the visited blocks hold no visible pair.
+ * Returns ATTN_ERR_INVALID_ARG for T < 1, window < -1, rows/cols < 1 or NULL
+ * arrays.
+ */
+int attn_band_tiles(int T, int window, int rows, int cols, int by_key,
+                    int* first, int* last, int* n_partial, int* n_empty);
+
+/* Bytes of device workspace attn_fwd needs (fp32 [B, H, T] key scales). */
+size_t attn_fwd_workspace_bytes(int B, int T, int H, int D);
+
+/*
+ * Forward.  q, k, v: bf16 [B, T, H, D] (inputs).  o: bf16 [B, T, H, D]
+ * (output).  lse: fp32 [B, H, T] (output; natural log of the sum of exp of the
+ * scaled logits of each query row; keep it for attn_bwd).
+ * window: W >= 0 keys to the left (W >= T - 1 is full causal), or -1 for full
+ * causal.  causal must be 1 (0 returns ATTN_ERR_UNSUPPORTED: the pages never
+ * use bidirectional attention).  eps: RMSNorm epsilon, finite and > 0.
+ * D must be 64 or 128 (else ATTN_ERR_UNSUPPORTED).  B*T*H*D must stay below
+ * 2^31 (else ATTN_ERR_UNSUPPORTED).  B, T or H equal to 0 is an empty problem:
+ * returns ATTN_OK and touches nothing (pointers may then be NULL).
+ * workspace: device memory of at least attn_fwd_workspace_bytes(B, T, H, D)
+ * bytes, 256-byte aligned, contents ignored and clobbered.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             void* workspace, size_t workspace_bytes,
+             int B, int T, int H, int D, int window, int causal, float eps,
+             void* stream);
+
+/* Bytes of device workspace attn_bwd needs. */
+size_t attn_bwd_workspace_bytes(int B, int T, int H, int D);
+
+/*
+ * Backward.  Inputs: q, k, v, o (from attn_fwd), lse (from attn_fwd,
+ * unchanged), dout = dL/do: bf16 [B, T, H, D] / fp32 [B, H, T].
+ * Outputs: dq, dk, dv: bf16 [B, T, H, D], gradients with respect to the
+ * PRE-norm q and k and to v.  window, causal, eps, B, T, H, D must equal the
+ * forward call's; the same rules and status codes apply.  workspace: at least
+ * attn_bwd_workspace_bytes(B, T, H, D) bytes of device memory, 256-byte
+ * aligned, clobbered.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int B, int T, int H, int D, int window, int causal, float eps,
+             void* stream);
+
+/*
+ * Opt-in per-kernel timing, a measurement aid (not part of the operation).
+ * While enabled, every kernel launch of attn_fwd / attn_bwd is bracketed by
+ * two HIP events recorded on the launch stream.  Kernel ids: 0 k_scale
+ * (key-scale pre-pass of the forward), 1 attn_fwd (forward attention),
+ * 2 bwd_prep (Delta, q_hat, scales), 3 bwd_dkdv (dK and dV), 4 bwd_dq (dQ).
+ *   attn_profile_enable(on): clears the totals and starts (on != 0) or stops
+ *     recording; returns ATTN_ERR_HIP if waiting on earlier events failed.
+ *   attn_profile_read(kernel, total_ms, launches): waits for the recorded
+ *     events and returns the summed milliseconds and launch count of that
+ *     kernel since the last enable; ATTN_ERR_INVALID_ARG for a bad id or NULL.
+ *   attn_kernel_name(kernel): the kernel's name ("unknown" if out of range).
+ * This is the library's only mutable global state; it is mutex-protected.
+ */
+int attn_profile_enable(int on);
+int attn_profile_read(int kernel, double* total_ms, long long* launches);
+const char* attn_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWATTN_H */

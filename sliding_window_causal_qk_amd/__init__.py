@@ -1,0 +1,157 @@
+"""MI355X (gfx950) causal sliding-window attention with RMSNorm on Q and K.
+
+Thin binding over libswattn.so (include/swattn.h): argument marshalling only.
+Every step of the attention runs in the HIP kernels; PyTorch provides device
+memory and the current stream.
+
+    from sliding_window_causal_qk_amd import attention, layer_windows
+    windows = layer_windows("SSSL", n_layer=8, seq_len=2048)   # [1024, ..., 2048]
+    o = attention(q, k, v, window=windows[l])                    # autograd-aware
+
+q, k, v: bf16 CUDA tensors [B, T, H, D] (contiguous), D in {64, 128}.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import List, Optional, Tuple
+
+from ._lib import (  # noqa: F401
+    ATTN_ERR_HIP, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_OK,
+    EXPORTS, LIB_PATH, SwattnError, check, lib, status_string,
+)
+
+__all__ = [
+    "attention", "attn_fwd", "attn_bwd", "layer_windows", "visible_pairs", "band_tiles",
+    "fwd_workspace_bytes", "bwd_workspace_bytes", "SwattnError",
+]
+
+
+def layer_windows(pattern: str, n_layer: int, seq_len: int) -> List[int]:
+    out = (ctypes.c_int * max(n_layer, 1))()
+    check(lib().attn_layer_windows(pattern.encode(), n_layer, seq_len, out), "attn_layer_windows")
+    return list(out[:n_layer])
+
+
+def visible_pairs(T: int, window: int) -> int:
+    n = lib().attn_visible_pairs(T, window)
+    if n < 0:
+        raise SwattnError(ATTN_ERR_INVALID_ARG, "attn_visible_pairs")
+    return int(n)
+
+
+def band_tiles(T: int, window: int, rows: int, cols: int, by_key: bool = False):
+    """Per row block: (first, last, n_partial, n_empty) column blocks visited."""
+    n = max((T + rows - 1) // rows, 1) if rows > 0 else 1
+    arrs = [(ctypes.c_int * n)() for _ in range(4)]
+    check(lib().attn_band_tiles(T, window, rows, cols, int(by_key), *arrs), "attn_band_tiles")
+    return [tuple(a[i] for a in arrs) for i in range((T + rows - 1) // rows)]
+
+
+def fwd_workspace_bytes(B: int, T: int, H: int, D: int) -> int:
+    return int(lib().attn_fwd_workspace_bytes(B, T, H, D))
+
+
+def bwd_workspace_bytes(B: int, T: int, H: int, D: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, T, H, D))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_tensor(t, name, shape=None, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the HIP kernels are the only path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _ptr(t) -> Optional[int]:
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
+             out=None, lse=None, workspace=None, stream=None) -> Tuple["object", "object"]:
+    """Forward through the C ABI.  Returns (o bf16 [B,T,H,D], lse fp32 [B,H,T])."""
+    torch = _torch()
+    B, T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, n, (B, T, H, D), torch.bfloat16)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor(o, "out", (B, T, H, D), torch.bfloat16)
+    _check_tensor(l, "lse", (B, H, T), torch.float32)
+    nbytes = fwd_workspace_bytes(B, T, H, D)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(),
+                        B, T, H, D, int(window), int(bool(causal)), float(eps), _stream(stream))
+    check(st, "attn_fwd")
+    return o, l
+
+
+def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float = 1e-6, *,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward through the C ABI.  Returns (dq, dk, dv), bf16 [B,T,H,D]."""
+    torch = _torch()
+    B, T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(t, n, (B, T, H, D), torch.bfloat16)
+    _check_tensor(lse, "lse", (B, H, T), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(t, n, (B, T, H, D), torch.bfloat16)
+    nbytes = bwd_workspace_bytes(B, T, H, D)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                        _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(),
+                        B, T, H, D, int(window), int(bool(causal)), float(eps), _stream(stream))
+    check(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def _make_function():
+    torch = _torch()
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, window, causal, eps):
+            o, lse = attn_fwd(q, k, v, window, causal, eps)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.cfg = (window, causal, eps)
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            window, causal, eps = ctx.cfg
+            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), window, causal, eps)
+            return dq, dk, dv, None, None, None
+
+    return _Attention
+
+
+_fn = None
+
+
+def attention(q, k, v, window: int, causal: bool = True, eps: float = 1e-6):
+    """Autograd-aware QK-RMSNorm causal sliding-window attention (HIP kernels)."""
+    global _fn
+    if _fn is None:
+        _fn = _make_function()
+    return _fn.apply(q, k, v, window, causal, eps)

@@ -1,0 +1,65 @@
+// Device-side building blocks for the gfx950 (CDNA4) attention kernels:
+// vector types, bf16 packing, 16-byte loads, the 32x32x16 bf16 MFMA and the
+// XCD-aware workgroup remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D = 16 * (number of k-steps of the 32x32x16 MFMA); rows of D bf16 values.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// acc + lo + hi of a packed bf16 pair (one v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t pk, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+}
+
+// C[32x32] += A[32x16] * B[16x32], bf16 inputs, fp32 accumulate.
+// Operand layout (lane l, g = l / 32, c = l % 32): A supplies row c, B column c,
+// each as 8 consecutive k values of the k-group g; C lane l holds column c,
+// rows 8 * (r / 4) + 4 * g + (r % 4) for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that each
+// XCD walks one contiguous range of logical ids (neighbouring tiles of the same
+// (batch, head) then share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  if ((nblk & 7) != 0) return bid;
+  return (bid & 7) * (nblk >> 3) + (bid >> 3);
+}
+
+// Column position of key/query offset x (0..15) inside a transposed 16-column
+// group, arranged so that the 8 values one lane feeds to an MFMA k-step are
+// contiguous: k-group 0 takes offsets {0..3, 8..11}, k-group 1 {4..7, 12..15}.
+__device__ __forceinline__ int tpos16(int x) { return ((x >> 2) & 1) * 8 + (x >> 3) * 4 + (x & 3); }
+
+}  // namespace swattn

@@ -1,0 +1,45 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+// Arguments are validated by the caller (swattn.hip) before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace swattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* kscale;  // workspace: [B, H, T]
+  int B, T, H, D;
+  int window;
+  float eps;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  // workspace carve-up
+  void* qhat;     // bf16 [B, T, H, D]: normalised queries
+  float* rq;      // [B, H, T]: 1 / rms(q)
+  float* kscale;  // [B, H, T]: log2(e) / sqrt(D) / rms(k)
+  float* delta;   // [B, H, T]: rowsum(dO * O)
+  int B, T, H, D;
+  int window;
+  float eps;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace swattn

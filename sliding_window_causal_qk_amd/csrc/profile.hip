@@ -1,0 +1,99 @@
+// Opt-in per-kernel timing: when enabled, every kernel launch is bracketed by
+// two HIP events recorded on the launch stream; attn_profile_read waits for
+// them and sums the elapsed times per kernel.  Disabled (the default), the
+// hooks cost one relaxed atomic load per launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/swattn.h"
+#include "profile.h"
+
+namespace swattn {
+namespace {
+
+struct Rec {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+std::atomic<bool> g_on{false};
+std::mutex g_mu;
+std::vector<Rec> g_recs;
+double g_total_ms[kNumKernels];
+long long g_count[kNumKernels];
+
+const char* kNames[kNumKernels] = {"k_scale", "attn_fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"};
+
+// fold finished records into the totals; returns false on a HIP error
+bool drain() {
+  bool ok = true;
+  for (Rec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) {
+      ok = false;
+    } else {
+      g_total_ms[r.kernel] += ms;
+      g_count[r.kernel] += 1;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_recs.clear();
+  return ok;
+}
+
+}  // namespace
+
+ProfToken prof_begin(int kernel, hipStream_t stream) {
+  ProfToken t{-1, nullptr, nullptr, stream};
+  if (!g_on.load(std::memory_order_relaxed)) return t;
+  if (hipEventCreate(&t.start) != hipSuccess) return t;
+  if (hipEventCreate(&t.stop) != hipSuccess) {
+    (void)hipEventDestroy(t.start);
+    return t;
+  }
+  (void)hipEventRecord(t.start, stream);
+  t.kernel = kernel;
+  return t;
+}
+
+void prof_end(const ProfToken& t) {
+  if (t.kernel < 0) return;
+  (void)hipEventRecord(t.stop, t.stream);
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_recs.push_back(Rec{t.kernel, t.start, t.stop});
+}
+
+}  // namespace swattn
+
+extern "C" {
+
+int attn_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(swattn::g_mu);
+  bool ok = swattn::drain();
+  for (int i = 0; i < swattn::kNumKernels; ++i) {
+    swattn::g_total_ms[i] = 0.0;
+    swattn::g_count[i] = 0;
+  }
+  swattn::g_on.store(on != 0);
+  return ok ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_profile_read(int kernel, double* total_ms, long long* launches) {
+  if (kernel < 0 || kernel >= swattn::kNumKernels || !total_ms || !launches) return ATTN_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(swattn::g_mu);
+  bool ok = swattn::drain();
+  *total_ms = swattn::g_total_ms[kernel];
+  *launches = swattn::g_count[kernel];
+  return ok ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_kernel_name(int kernel) {
+  if (kernel < 0 || kernel >= swattn::kNumKernels) return "unknown";
+  return swattn::kNames[kernel];
+}
+
+}  // extern "C"

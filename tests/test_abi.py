@@ -1,0 +1,185 @@
+"""Host-side checks of libswattn.so that need no GPU: the library loads, exports
+every symbol include/swattn.h declares, its integer helpers (layer windows,
+visible-pair count, band tile enumeration) agree bit-exactly with the oracle,
+and every invalid argument is rejected before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as A
+import sliding_window_causal_qk_amd as sw
+from sliding_window_causal_qk_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swattn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(_lib.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.attn_version() >= 100
+
+
+def test_status_strings():
+    for s, name in ((0, "ATTN_OK"), (1, "ATTN_ERR_INVALID_ARG"), (2, "ATTN_ERR_UNSUPPORTED"),
+                    (3, "ATTN_ERR_WORKSPACE"), (4, "ATTN_ERR_HIP")):
+        assert sw.status_string(s) == name
+    assert sw.status_string(99) == "ATTN_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("pattern", ["SSSL", "L", "S", "SL", "SLLL", "SSSS", "sssl", "LS"])
+@pytest.mark.parametrize("n_layer", [1, 2, 4, 7, 8, 12])
+@pytest.mark.parametrize("T", [1, 2, 513, 2048, 8192])
+def test_layer_windows_match_oracle(pattern, n_layer, T):
+    assert sw.layer_windows(pattern, n_layer, T) == oracle.layer_windows(pattern, n_layer, T)
+
+
+def test_layer_windows_golden(golden_dir):
+    import json
+    g = json.load(open(os.path.join(golden_dir, "window_schedule.json")))
+    for c in g["cases"]:
+        assert sw.layer_windows(c["pattern"], c["n_layer"], c["seq_len"]) == c["windows"]
+
+
+@pytest.mark.parametrize("bad", [("", 4, 2048), ("SXL", 4, 2048), ("SSSL", 0, 2048), ("SSSL", 4, 0)])
+def test_layer_windows_rejects(bad):
+    with pytest.raises(sw.SwattnError):
+        sw.layer_windows(*bad)
+
+
+def test_visible_pairs_match_oracle():
+    for T in (0, 1, 2, 3, 17, 64, 127, 128, 129, 1000):
+        for W in (-1, 0, 1, 5, T // 2, T - 1, T, T + 3):
+            if W < -1:
+                continue
+            assert sw.visible_pairs(T, W) == (oracle.n_visible(T, W) if T > 0 else 0), (T, W)
+    for T, W, n in ((128, 64, 6240), (2048, 1024, 1574400), (2048, 2048, 2098176),
+                    (8192, 4096, 25171968), (8192, 8192, 33558528)):
+        assert sw.visible_pairs(T, W) == n == oracle.n_visible(T, W)
+    with pytest.raises(sw.SwattnError):
+        sw.visible_pairs(10, -2)
+
+
+def _brute_tiles(T, W, rows, cols, by_key):
+    m = A.visible_mask(T, W)   # [query, key]
+    if by_key:
+        m = m.T
+    nr, nc = math.ceil(T / rows), math.ceil(T / cols)
+    out = []
+    for r in range(nr):
+        blocks = []
+        for cb in range(nc):
+            blk = np.zeros((rows, cols), dtype=bool)
+            sub = m[r * rows:(r + 1) * rows, cb * cols:(cb + 1) * cols]
+            blk[:sub.shape[0], :sub.shape[1]] = sub
+            blocks.append((blk.any(), blk.all()))
+        vis = [i for i, (a, _) in enumerate(blocks) if a]
+        if not vis:
+            out.append((0, -1, 0, 0))
+            continue
+        first, last = vis[0], vis[-1]
+        assert vis == list(range(first, last + 1))   # the band is contiguous
+        npart = sum(1 for i in range(first, last + 1) if not blocks[i][1])
+        out.append((first, last, npart, 0))
+    return out
+
+
+@pytest.mark.parametrize("T,W", [(1, 0), (100, 0), (100, 7), (128, 64), (130, 64), (200, -1),
+                                 (257, 128), (300, 299), (333, 31), (512, 256)])
+@pytest.mark.parametrize("rows,cols,by_key", [(128, 64, False), (64, 128, True), (32, 64, False),
+                                              (16, 16, False), (64, 64, True)])
+def test_band_tiles_match_mask(T, W, rows, cols, by_key):
+    assert sw.band_tiles(T, W, rows, cols, by_key) == _brute_tiles(T, W, rows, cols, by_key)
+
+
+# ------------------------------------------------------ argument validation
+# Fake device addresses: validation must reject these calls before any HIP
+# call, so they are never dereferenced.
+P = 0x10000
+ALIGNED = [P + i * 0x1000000 for i in range(12)]
+
+
+def _fwd(**kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3], lse=ALIGNED[4],
+             ws=ALIGNED[5], wsb=1 << 40, B=2, T=64, H=2, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["wsb"],
+                               a["B"], a["T"], a["H"], a["D"], a["window"], a["causal"],
+                               a["eps"], None)
+
+
+def _bwd(**kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3], lse=ALIGNED[4],
+             do=ALIGNED[5], dq=ALIGNED[6], dk=ALIGNED[7], dv=ALIGNED[8], ws=ALIGNED[9],
+             wsb=1 << 40, B=2, T=64, H=2, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                               a["dk"], a["dv"], a["ws"], a["wsb"], a["B"], a["T"], a["H"],
+                               a["D"], a["window"], a["causal"], a["eps"], None)
+
+
+INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(lse=None),
+    dict(q=P + 2), dict(v=P + 8),
+    dict(B=-1), dict(T=-5), dict(H=-1), dict(D=0), dict(D=-64),
+    dict(eps=0.0), dict(eps=-1e-6), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(window=-2), dict(causal=2), dict(causal=-1),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID, ids=[str(k) for k in INVALID])
+def test_fwd_invalid(kw):
+    assert _fwd(**kw) == _lib.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", INVALID + [dict(do=None), dict(dq=None), dict(dk=P + 4)],
+                         ids=[str(k) for k in INVALID + [dict(do=None), dict(dq=None), dict(dk=P + 4)]])
+def test_bwd_invalid(kw):
+    assert _bwd(**kw) == _lib.ATTN_ERR_INVALID_ARG
+
+
+def test_aliasing_rejected():
+    assert _fwd(o=ALIGNED[0]) == _lib.ATTN_ERR_INVALID_ARG
+    assert _bwd(dq=ALIGNED[1]) == _lib.ATTN_ERR_INVALID_ARG
+    assert _bwd(dv=ALIGNED[6]) == _lib.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(D=32), dict(causal=0),
+                                dict(B=1 << 12, T=1 << 12, H=8, D=128)])
+def test_unsupported(kw):
+    assert _fwd(**kw) == _lib.ATTN_ERR_UNSUPPORTED
+    assert _bwd(**kw) == _lib.ATTN_ERR_UNSUPPORTED
+
+
+def test_workspace_checks():
+    need_f = sw.fwd_workspace_bytes(2, 64, 2, 64)
+    need_b = sw.bwd_workspace_bytes(2, 64, 2, 64)
+    assert need_f >= 2 * 2 * 64 * 4
+    assert need_b >= 2 * 64 * 2 * 64 * 2 + 3 * 2 * 2 * 64 * 4
+    assert _fwd(ws=None) == _lib.ATTN_ERR_WORKSPACE
+    assert _fwd(wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE
+    assert _fwd(ws=P + 16) == _lib.ATTN_ERR_WORKSPACE
+    assert _bwd(ws=None) == _lib.ATTN_ERR_WORKSPACE
+    assert _bwd(wsb=need_b - 1) == _lib.ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(H=0)])
+def test_empty_problem_is_ok_and_touches_nothing(kw):
+    nulls = dict(q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0)
+    assert _fwd(**kw, **nulls) == _lib.ATTN_OK
+    assert _bwd(**kw, **nulls, do=None, dq=None, dk=None, dv=None) == _lib.ATTN_OK

@@ -108,3 +108,23 @@ def workload(name: str) -> Workload:
         if w.name == name:
             return w
     raise KeyError(name)
+
+
+def make_layer_inputs_device(B: int, T: int, H: int, D: int, seed: int,
+                             sigma_qkv: float = 1.0, sigma_do: float = 1.0, device="cuda"):
+    """Same recipe drawn on the GPU (torch's Philox stream, not numpy's): N(0, sigma^2)
+    in fp32, rounded to bf16 (round to nearest even), Q, K, V then dO from one
+    generator seeded with `seed`.  For timing runs, where only the distribution
+    matters; the parity tests use make_layer_inputs, which the oracle also reads."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shape = (B, T, H, D)
+    out = []
+    for sigma in (sigma_qkv, sigma_qkv, sigma_qkv, sigma_do):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        out.append(x.to(torch.bfloat16))
+        del x
+    return tuple(out)

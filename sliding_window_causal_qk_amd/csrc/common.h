@@ -49,6 +49,49 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// ---- buffer loads: a descriptor covers one (batch, head) slice from a given
+// row on; loads past its num_records (checked on the per-lane offset) return
+// zero, which pads ragged tails without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // dword 3 of a raw gfx9-family buffer descriptor
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long nbytes) {
+  const int n = nbytes <= 0 ? 0 : (nbytes >= 0x7fffffffLL ? 0x7fffffff : (int)nbytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcFlags);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload8(rsrc_t r, int voff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+}
+__device__ __forceinline__ float bload4f(rsrc_t r, int voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
+__device__ __forceinline__ void bstore8(u32x2 v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
+__device__ __forceinline__ void bstore4f(float v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, 0);
+}
+
+// Wave-uniform value moved to a scalar register.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// ---- transposed LDS reads (ds_read_b64_tr_b16).  In each group of 16 lanes,
+// lane i receives slot j = element (i % 4) of the 8-byte chunk addressed by lane
+// (i / 4 + 4 j) of the group.  tr4x16 reads a 4 (rows) x 16 (columns) bf16 block
+// of a row-major LDS array: lane i of the group gets the column `col0 + i`, rows
+// row0 .. row0 + 3, as two packed bf16 pairs.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#define SW_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
+  const SW_LDS bf16x4* q = (const SW_LDS bf16x4*)(p);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<SW_LDS bf16x4*>(q)));
+}
+
 // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that each
 // XCD walks one contiguous range of logical ids (neighbouring tiles of the same
 // (batch, head) then share that XCD's L2).

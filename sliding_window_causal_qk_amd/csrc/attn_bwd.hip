@@ -78,72 +78,58 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   }
 }
 
-// Shared staging helper: 4 consecutive rows x one 16-byte chunk per item.
-// Writes the rows row-major (pitch RP) and, optionally, transposed (pitch TP)
-// with the tpos16 column order the MFMA k-steps read.
-template <int D, int ROWS>
-struct Stage {
+// Staging of a tile of ROWS rows (row-major, pitch P bf16) through registers:
+// thread -> rows tid / CH + (256 / CH) p, 16-byte chunk tid % CH.  The
+// descriptor starts at the tile's first row, so rows past T load as zero.
+template <int D, int ROWS, int P>
+struct RowStage {
   static constexpr int CH = D / 8;
-  static constexpr int QUADS = ROWS / 4;
-  static constexpr int ITEMS = QUADS * CH;
-  static constexpr int PASS = (ITEMS + 255) / 256;
-
-  u32x4 r[PASS][4];
-
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, size_t base, size_t rs,
-                                       int row0, int T, int tid) {
+  static constexpr int RPP = 256 / CH;
+  static constexpr int PASSES = ROWS / RPP;
+  u32x4 r[PASSES];
+  __device__ __forceinline__ void load(rsrc_t rs_tile, int rs_elems, int tid) {
 #pragma unroll
-    for (int p = 0; p < PASS; ++p) {
-      const int idx = tid + 256 * p;
-      const int quad = idx % QUADS, dch = idx / QUADS;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = row0 + 4 * quad + e;
-        r[p][e] = (idx < ITEMS && t < T) ? ld16(src + base + (size_t)t * rs + 8 * dch)
-                                         : u32x4{0, 0, 0, 0};
-      }
-    }
+    for (int p = 0; p < PASSES; ++p)
+      r[p] = bload16(rs_tile, ((tid / CH + RPP * p) * rs_elems + 8 * (tid % CH)) * 2);
   }
-
-  template <bool ROWMAJOR, bool TRANS>
-  __device__ __forceinline__ void store(uint16_t* rowmaj, int RP, uint16_t* trans, int TP,
-                                        int tid) const {
+  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
 #pragma unroll
-    for (int p = 0; p < PASS; ++p) {
-      const int idx = tid + 256 * p;
-      if (idx >= ITEMS) continue;
-      const int quad = idx % QUADS, dch = idx / QUADS;
-      if (ROWMAJOR) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st16(rowmaj + (4 * quad + e) * RP + 8 * dch, r[p][e]);
-      }
-      if (TRANS) {
-        const int col = (quad >> 2) * 16 + tpos16((4 * quad) & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t r0 = r[p][0][e], r1 = r[p][1][e], r2 = r[p][2][e], r3 = r[p][3][e];
-          u32x2 lo = {__builtin_amdgcn_perm(r1, r0, 0x05040100u), __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
-          u32x2 hi = {__builtin_amdgcn_perm(r1, r0, 0x07060302u), __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
-          st8(trans + (8 * dch + 2 * e) * TP + col, lo);
-          st8(trans + (8 * dch + 2 * e + 1) * TP + col, hi);
-        }
-      }
-    }
+    for (int p = 0; p < PASSES; ++p) st16(lds + (tid / CH + RPP * p) * P + 8 * (tid % CH), r[p]);
   }
 };
 
+// A-operand of a 32x32x16 MFMA whose k index runs along the rows of a row-major
+// LDS tile (two transposing reads): lane (g, c) gets column col0 + c of rows
+// row0 + 4 g + {0,1,2,3} and row0 + 8 + 4 g + {0,1,2,3}, i.e. element j is row
+// row0 + 4 g + (j % 4) + 8 (j / 4) -- the k order of probabilities held in the
+// C layout of a previous product.  `off` is the per-lane part from tr_off().
+__device__ __forceinline__ int tr_off(int lane, int P) {
+  const int li = lane & 15, g = lane >> 5;
+  return (4 * g + (li >> 2)) * P + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+}
+__device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int off, int row0, int col0, int P) {
+  const u32x2 lo = lds_tr4(tile + off + row0 * P + col0);
+  const u32x2 hi = lds_tr4(tile + off + (row0 + 8) * P + col0);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // ------------------------------------------------------------------ dK / dV
+// Workgroup: 4 waves; wave w owns keys j0 + 32 w + c.  Query blocks of 64
+// rows (q_hat and dO, row-major, double-buffered in LDS) stream through the
+// band.  Per block: S = Q_hat K^T and dP = dO V^T (keys in lanes, queries in
+// registers), P and dS in registers, then dV^T += dO^T P and dK_hat^T +=
+// Q_hat^T dS with the transposed operands read straight from the row-major
+// tiles.
 template <int D>
 struct DkdvCfg {
   static constexpr int BNK = 128;       // keys per workgroup (32 per wave)
   static constexpr int BMQ = 64;        // queries per step
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int RP = D + 8;      // row-major pitch
-  static constexpr int TP = BMQ + 8;    // transposed pitch
-  static constexpr int Q_LDS = BMQ * RP;
-  static constexpr int QT_LDS = D * TP;
-  static constexpr int LDS_BYTES = (2 * Q_LDS + 2 * QT_LDS) * 2 + 2 * BMQ * 4;
+  static constexpr int P = D + 24;      // row pitch (bf16): odd multiple of 16 bytes
+  static constexpr int T_LDS = BMQ * P;
+  static constexpr int STAGE = 2 * T_LDS * 2 + 2 * BMQ * 4;
+  static constexpr int LDS_BYTES = 2 * STAGE;
 };
 
 template <int D>
@@ -155,12 +141,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     int T, int H, int W) {
   using C = DkdvCfg<D>;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* dOs = Qs + C::Q_LDS;
-  uint16_t* QTs = dOs + C::Q_LDS;
-  uint16_t* dOTs = QTs + C::QT_LDS;
-  float* Ls = reinterpret_cast<float*>(dOTs + C::QT_LDS);
-  float* Dls = Ls + C::BMQ;
 
   const int nkt = (T + C::BNK - 1) / C::BNK;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -170,20 +150,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int j0 = kt * C::BNK;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const size_t rs = (size_t)H * D;
-  const size_t base = ((size_t)b * T) * rs + (size_t)h * D;
+  const int w = uniform(tid >> 6);
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int rs = H * D;
+  const long long rsb = 2LL * rs;
+  const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
+  const size_t sbase = ((size_t)b * T * H + h) * D;
   const size_t sb = (size_t)bh * T;
 
-  // ---- owned key / value rows (kv = j0 + 32 w + c), B operands of S and dP
-  const int kj = j0 + 32 * w + c;
+  // ---- owned key / value rows (kv = kw0 + c), B operands of S and dP
+  const int kw0 = j0 + 32 * w;
+  const int kj = kw0 + c;
   u32x4 kf[C::KS], vf[C::KS];
+  {
+    const rsrc_t rk = make_rsrc(k + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
+    const rsrc_t rv = make_rsrc(v + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    kf[ks] = kj < T ? ld16(k + base + (size_t)kj * rs + 16 * ks + 8 * g) : u32x4{0, 0, 0, 0};
-    vf[ks] = kj < T ? ld16(v + base + (size_t)kj * rs + 16 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks] = bload16(rk, (c * rs + 16 * ks + 8 * g) * 2);
+      vf[ks] = bload16(rv, (c * rs + 16 * ks + 8 * g) * 2);
+    }
   }
-  const float ksc = kj < T ? kscale[sb + kj] : 0.f;
+  const rsrc_t rstat_k = make_rsrc(kscale + sb, 4LL * T);
+  const float ksc = bload4f(rstat_k, kj * 4);
 
   f32x16 acc_dv[C::NB], acc_dk[C::NB];
 #pragma unroll
@@ -193,128 +182,147 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const bool any = q_range(j0, j0 + C::BNK - 1, T, W, &q_lo, &q_hi);
   const int qb0 = any ? q_lo / C::BMQ : 0, qb1 = any ? q_hi / C::BMQ : -1;
 
-  Stage<D, C::BMQ> sq, sdo;
+  RowStage<D, C::BMQ, C::P> sq, sdo;
   float lreg = 0.f;
+  const rsrc_t rl = make_rsrc(lse + sb, 4LL * T);
+  const rsrc_t rd = make_rsrc(delta + sb, 4LL * T);
+  const uint16_t* qh_s = qhat + sbase;
+  const uint16_t* do_s = dout + sbase;
   auto load_blk = [&](int qb) {
     const int r0 = qb * C::BMQ;
-    sq.load(qhat, base, rs, r0, T, tid);
-    sdo.load(dout, base, rs, r0, T, tid);
-    if (tid < C::BMQ) {
-      const int t = r0 + tid;
-      lreg = t < T ? lse[sb + t] * kLog2e : 0.f;
-    } else if (tid < 2 * C::BMQ) {
-      const int t = r0 + tid - C::BMQ;
-      lreg = t < T ? delta[sb + t] : 0.f;
-    }
+    sq.load(make_rsrc(qh_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
+    sdo.load(make_rsrc(do_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
+    if (tid < C::BMQ) lreg = bload4f(rl, (r0 + tid) * 4) * kLog2e;
+    else if (tid < 2 * C::BMQ) lreg = bload4f(rd, (r0 + tid - C::BMQ) * 4);
+  };
+  auto store_blk = [&](int buf) {
+    uint16_t* Qs = reinterpret_cast<uint16_t*>(smem + buf * C::STAGE);
+    sq.store(Qs, tid);
+    sdo.store(Qs + C::T_LDS, tid);
+    if (tid < 2 * C::BMQ) reinterpret_cast<float*>(Qs + 2 * C::T_LDS)[tid] = lreg;
   };
 
-  if (qb0 <= qb1) load_blk(qb0);
+  const int a_off = c * C::P + 8 * g;        // row-major A operands (16-byte reads)
+  const int t_off = tr_off(lane, C::P);      // transposed A operands
+  // visibility on partial blocks: 0 <= q - kj <= lim, lim = min(W, T - 1 - kj)
+  const int lim = imin(W, T - 1 - kj);
+
+  if (qb0 <= qb1) {
+    load_blk(qb0);
+    store_blk(0);
+  }
+  __syncthreads();
   for (int qb = qb0; qb <= qb1; ++qb) {
-    __syncthreads();
-    sq.template store<true, true>(Qs, C::RP, QTs, C::TP, tid);
-    sdo.template store<true, true>(dOs, C::RP, dOTs, C::TP, tid);
-    if (tid < 2 * C::BMQ) Ls[tid] = lreg;  // Ls and Dls are contiguous
-    __syncthreads();
+    const int buf = (qb - qb0) & 1;
     if (qb < qb1) load_blk(qb + 1);
 
     const int q0 = qb * C::BMQ;
-    const int cls = tile_class(q0, q0 + C::BMQ - 1, j0 + 32 * w, j0 + 32 * w + 31, T, W);
-    if (cls == TILE_EMPTY) continue;
+    const int cls = uniform(tile_class(q0, q0 + C::BMQ - 1, kw0, kw0 + 31, T, W));
+    if (cls != TILE_EMPTY) {
+      const uint16_t* Qs = reinterpret_cast<const uint16_t*>(smem + buf * C::STAGE);
+      const uint16_t* dOs = Qs + C::T_LDS;
+      const float* Ls = reinterpret_cast<const float*>(Qs + 2 * C::T_LDS);
+      const float* Dls = Ls + C::BMQ;
 
-    u32x4 pf[C::BMQ / 16], dsf[C::BMQ / 16];
+      u32x4 pf[C::BMQ / 16], dsf[C::BMQ / 16];
 #pragma unroll
-    for (int mb = 0; mb < C::BMQ / 32; ++mb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int mb = 0; mb < C::BMQ / 32; ++mb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        s = mfma32(ld16(Qs + (32 * mb + c) * C::RP + 16 * ks + 8 * g), kf[ks], s);
-        dp = mfma32(ld16(dOs + (32 * mb + c) * C::RP + 16 * ks + 8 * g), vf[ks], dp);
-      }
-      // lane (g, c), register r: query q0 + 32 mb + 8 (r/4) + 4 g + r%4, key kj
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int ql = 32 * mb + 8 * q4 + 4 * g;
-        f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
-        f32x4 d4 = *reinterpret_cast<const f32x4*>(Dls + ql);
-        float p[4], ds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pe = __builtin_amdgcn_exp2f(s[4 * q4 + e] * ksc - l4[e]);
-          if (cls == TILE_PARTIAL && !visible(q0 + ql + e, kj, T, W)) pe = 0.f;
-          p[e] = pe;
-          ds[e] = pe * (dp[4 * q4 + e] - d4[e]);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          s = mfma32(ld16(Qs + a_off + 32 * mb * C::P + 16 * ks), kf[ks], s);
+          dp = mfma32(ld16(dOs + a_off + 32 * mb * C::P + 16 * ks), vf[ks], dp);
         }
-        const int st = 2 * mb + (q4 >> 1), el = 2 * (q4 & 1);
-        pf[st][el] = pack_bf16(p[0], p[1]);
-        pf[st][el + 1] = pack_bf16(p[2], p[3]);
-        dsf[st][el] = pack_bf16(ds[0], ds[1]);
-        dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
+        // lane (g, c), register r: query q0 + 32 mb + 8 (r/4) + 4 g + r%4, key kj
+        const int t0 = q0 + 32 * mb + 4 * g - kj;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ql = 32 * mb + 8 * q4 + 4 * g;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dls + ql);
+          float p[4], ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[4 * q4 + e] * ksc - l4[e]);
+          if (cls == TILE_PARTIAL) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              p[e] = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp[4 * q4 + e] - d4[e]);
+          const int st = 2 * mb + (q4 >> 1), el = 2 * (q4 & 1);
+          pf[st][el] = pack_bf16(p[0], p[1]);
+          pf[st][el + 1] = pack_bf16(p[2], p[3]);
+          dsf[st][el] = pack_bf16(ds[0], ds[1]);
+          dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
+        }
+      }
+      // dV^T[d, kv] += dO^T[d, q] P[q, kv];  dK_hat^T[d, kv] += Q_hat^T[d, q] dS[q, kv]
+#pragma unroll
+      for (int s2 = 0; s2 < C::BMQ / 16; ++s2) {
+#pragma unroll
+        for (int n = 0; n < C::NB; ++n) {
+          acc_dv[n] = mfma32(tr_operand(dOs, t_off, 16 * s2, 32 * n, C::P), pf[s2], acc_dv[n]);
+          acc_dk[n] = mfma32(tr_operand(Qs, t_off, 16 * s2, 32 * n, C::P), dsf[s2], acc_dk[n]);
+        }
       }
     }
-    // dV^T[d, kv] += dO^T[d, q] P[q, kv];  dK_hat^T[d, kv] += Q_hat^T[d, q] dS[q, kv]
-#pragma unroll
-    for (int s = 0; s < C::BMQ / 16; ++s) {
-#pragma unroll
-      for (int n = 0; n < C::NB; ++n) {
-        acc_dv[n] = mfma32(ld16(dOTs + (32 * n + c) * C::TP + 16 * s + 8 * g), pf[s], acc_dv[n]);
-        acc_dk[n] = mfma32(ld16(QTs + (32 * n + c) * C::TP + 16 * s + 8 * g), dsf[s], acc_dk[n]);
-      }
-    }
+    if (qb < qb1) store_blk(buf ^ 1);
+    __syncthreads();
   }
 
   // ---- epilogue: lane (g, c) holds key kj, d = 32 n + 8 q4 + 4 g + e
-  if (kj < T) {
-    const float rk = ksc * (sqrtf((float)D) / kLog2e);
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const uint16_t* krow = k + base + (size_t)kj * rs;
-    float dot = 0.f;
-    f32x16 khat[C::NB];
+  const float rk = ksc * (sqrtf((float)D) / kLog2e);
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  const rsrc_t rkr = make_rsrc(k + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
+  float dot = 0.f;
+  f32x16 khat[C::NB];
 #pragma unroll
-    for (int n = 0; n < C::NB; ++n)
+  for (int n = 0; n < C::NB; ++n)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2 kk = ld8(krow + 32 * n + 8 * q4 + 4 * g);
-        float x[4] = {bf_lo(kk[0]), bf_hi(kk[0]), bf_lo(kk[1]), bf_hi(kk[1])};
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const u32x2 kk = bload8(rkr, (c * rs + 32 * n + 8 * q4 + 4 * g) * 2);
+      const float x[4] = {bf_lo(kk[0]), bf_hi(kk[0]), bf_lo(kk[1]), bf_hi(kk[1])};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          khat[n][4 * q4 + e] = x[e] * rk;
-          acc_dk[n][4 * q4 + e] *= inv_sqrt_d;
-          dot += acc_dk[n][4 * q4 + e] * khat[n][4 * q4 + e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        khat[n][4 * q4 + e] = x[e] * rk;
+        acc_dk[n][4 * q4 + e] *= inv_sqrt_d;
+        dot += acc_dk[n][4 * q4 + e] * khat[n][4 * q4 + e];
       }
-    dot += __shfl_xor(dot, 32);
-    const float mean = dot * (1.0f / D);
-    uint16_t* dkrow = dk + base + (size_t)kj * rs;
-    uint16_t* dvrow = dv + base + (size_t)kj * rs;
+    }
+  dot += __shfl_xor(dot, 32);
+  const float mean = dot * (1.0f / D);
+  const rsrc_t rdk = make_rsrc(dk + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
+  const rsrc_t rdv = make_rsrc(dv + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
 #pragma unroll
-    for (int n = 0; n < C::NB; ++n)
+  for (int n = 0; n < C::NB; ++n)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * n + 8 * q4 + 4 * g;
-        float y[4];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int off = (c * rs + 32 * n + 8 * q4 + 4 * g) * 2;
+      float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean);
-        st8(dkrow + d, u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
-        st8(dvrow + d, u32x2{pack_bf16(acc_dv[n][4 * q4 + 0], acc_dv[n][4 * q4 + 1]),
-                             pack_bf16(acc_dv[n][4 * q4 + 2], acc_dv[n][4 * q4 + 3])});
-      }
-  }
-  // (the two lanes of a key row share kj, so the partner exchange above always
-  //  pairs two active lanes)
+      for (int e = 0; e < 4; ++e) y[e] = rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean);
+      bstore8(u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])}, rdk, off);
+      bstore8(u32x2{pack_bf16(acc_dv[n][4 * q4 + 0], acc_dv[n][4 * q4 + 1]),
+                    pack_bf16(acc_dv[n][4 * q4 + 2], acc_dv[n][4 * q4 + 3])}, rdv, off);
+    }
 }
 
 // ------------------------------------------------------------------ dQ
+// Workgroup: 4 waves; wave w owns queries i0 + 32 w + c.  Key tiles of 64 rows
+// (K, V row-major, double-buffered) stream through the band.  Per tile:
+// S^T = K Q_hat^T and dP^T = V dO^T (queries in lanes), dS scaled by each
+// key's kscale, then dQ^T += K^T dS^T with K^T read transposed from the tile.
 template <int D>
 struct DqCfg {
   static constexpr int BM = 128;   // queries per workgroup (32 per wave)
   static constexpr int BN = 64;    // keys per step
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int RP = D + 8;
-  static constexpr int TP = BN + 8;
-  static constexpr int K_LDS = BN * RP;
-  static constexpr int KT_LDS = D * TP;
-  static constexpr int LDS_BYTES = (2 * K_LDS + KT_LDS) * 2 + BN * 4;
+  static constexpr int P = D + 24;
+  static constexpr int T_LDS = BN * P;
+  static constexpr int STAGE = 2 * T_LDS * 2 + BN * 4;
+  static constexpr int LDS_BYTES = 2 * STAGE;
 };
 
 template <int D>
@@ -326,10 +334,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const float* __restrict__ kscale, uint16_t* __restrict__ dq, int T, int H, int W) {
   using C = DqCfg<D>;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Vs = Ks + C::K_LDS;
-  uint16_t* KTs = Vs + C::K_LDS;
-  float* KSs = reinterpret_cast<float*>(KTs + C::KT_LDS);
 
   const int nqt = (T + C::BM - 1) / C::BM;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -339,20 +343,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const int i0 = qt * C::BM;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const size_t rs = (size_t)H * D;
-  const size_t base = ((size_t)b * T) * rs + (size_t)h * D;
+  const int w = uniform(tid >> 6);
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int rs = H * D;
+  const long long rsb = 2LL * rs;
+  const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
+  const size_t sbase = ((size_t)b * T * H + h) * D;
   const size_t sb = (size_t)bh * T;
 
-  const int qi = i0 + 32 * w + c;
+  const int qw0 = i0 + 32 * w;
+  const int qi = qw0 + c;
   u32x4 qf[C::KS], df[C::KS];
+  {
+    const rsrc_t rq_ = make_rsrc(qhat + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+    const rsrc_t rdo = make_rsrc(dout + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    qf[ks] = qi < T ? ld16(qhat + base + (size_t)qi * rs + 16 * ks + 8 * g) : u32x4{0, 0, 0, 0};
-    df[ks] = qi < T ? ld16(dout + base + (size_t)qi * rs + 16 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < C::KS; ++ks) {
+      qf[ks] = bload16(rq_, (c * rs + 16 * ks + 8 * g) * 2);
+      df[ks] = bload16(rdo, (c * rs + 16 * ks + 8 * g) * 2);
+    }
   }
-  const float lq = qi < T ? lse[sb + qi] * kLog2e : 0.f;
-  const float dlt = qi < T ? delta[sb + qi] : 0.f;
+  const rsrc_t rstat_l = make_rsrc(lse + sb, 4LL * T);
+  const rsrc_t rstat_d = make_rsrc(delta + sb, 4LL * T);
+  const float lq = bload4f(rstat_l, qi * 4) * kLog2e;
+  const float dlt = bload4f(rstat_d, qi * 4);
 
   f32x16 acc[C::NB];
 #pragma unroll
@@ -362,97 +376,116 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   kv_range(i0, i0 + C::BM - 1, T, W, &kv_lo, &kv_hi);
   const int jt0 = kv_lo / C::BN, jt1 = kv_hi / C::BN;
 
-  Stage<D, C::BN> sk, sv;
+  RowStage<D, C::BN, C::P> sk, sv;
   float ksreg = 0.f;
+  const rsrc_t rks = make_rsrc(kscale + sb, 4LL * T);
+  const uint16_t* k_s = k + sbase;
+  const uint16_t* v_s = v + sbase;
   auto load_tile = [&](int jt) {
     const int r0 = jt * C::BN;
-    sk.load(k, base, rs, r0, T, tid);
-    sv.load(v, base, rs, r0, T, tid);
-    if (tid < C::BN) {
-      const int t = r0 + tid;
-      ksreg = t < T ? kscale[sb + t] : 0.f;
-    }
+    sk.load(make_rsrc(k_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
+    sv.load(make_rsrc(v_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
+    if (tid < C::BN) ksreg = bload4f(rks, (r0 + tid) * 4);
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + buf * C::STAGE);
+    sk.store(Ks, tid);
+    sv.store(Ks + C::T_LDS, tid);
+    if (tid < C::BN) reinterpret_cast<float*>(Ks + 2 * C::T_LDS)[tid] = ksreg;
   };
 
-  if (jt0 <= jt1) load_tile(jt0);
+  const int a_off = c * C::P + 8 * g;
+  const int t_off = tr_off(lane, C::P);
+
+  if (jt0 <= jt1) {
+    load_tile(jt0);
+    store_tile(0);
+  }
+  __syncthreads();
   for (int jt = jt0; jt <= jt1; ++jt) {
-    __syncthreads();
-    sk.template store<true, true>(Ks, C::RP, KTs, C::TP, tid);
-    sv.template store<true, false>(Vs, C::RP, nullptr, 0, tid);
-    if (tid < C::BN) KSs[tid] = ksreg;
-    __syncthreads();
+    const int buf = (jt - jt0) & 1;
     if (jt < jt1) load_tile(jt + 1);
 
     const int j0 = jt * C::BN;
-    const int cls = tile_class(i0 + 32 * w, i0 + 32 * w + 31, j0, j0 + C::BN - 1, T, W);
-    if (cls == TILE_EMPTY) continue;
+    const int cls = uniform(tile_class(qw0, qw0 + 31, j0, j0 + C::BN - 1, T, W));
+    if (cls != TILE_EMPTY) {
+      const uint16_t* Ks = reinterpret_cast<const uint16_t*>(smem + buf * C::STAGE);
+      const uint16_t* Vs = Ks + C::T_LDS;
+      const float* KSs = reinterpret_cast<const float*>(Ks + 2 * C::T_LDS);
 
-    u32x4 dsf[C::BN / 16];
+      u32x4 dsf[C::BN / 16];
+      const int t0 = j0 + 4 * g + W - qi;  // key kv visible iff 0 <= kv - (qi - W) <= W
 #pragma unroll
-    for (int mb = 0; mb < C::BN / 32; ++mb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int mb = 0; mb < C::BN / 32; ++mb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        s = mfma32(ld16(Ks + (32 * mb + c) * C::RP + 16 * ks + 8 * g), qf[ks], s);
-        dp = mfma32(ld16(Vs + (32 * mb + c) * C::RP + 16 * ks + 8 * g), df[ks], dp);
-      }
-      // lane (g, c), register r: key j0 + 32 mb + 8 (r/4) + 4 g + r%4, query qi
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int jl = 32 * mb + 8 * q4 + 4 * g;
-        f32x4 k4 = *reinterpret_cast<const f32x4*>(KSs + jl);
-        float ds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pe = __builtin_amdgcn_exp2f(s[4 * q4 + e] * k4[e] - lq);
-          if (cls == TILE_PARTIAL && !visible(qi, j0 + jl + e, T, W)) pe = 0.f;
-          ds[e] = pe * (dp[4 * q4 + e] - dlt) * k4[e];
+        for (int ks = 0; ks < C::KS; ++ks) {
+          s = mfma32(ld16(Ks + a_off + 32 * mb * C::P + 16 * ks), qf[ks], s);
+          dp = mfma32(ld16(Vs + a_off + 32 * mb * C::P + 16 * ks), df[ks], dp);
         }
-        const int st = 2 * mb + (q4 >> 1), el = 2 * (q4 & 1);
-        dsf[st][el] = pack_bf16(ds[0], ds[1]);
-        dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
+        // lane (g, c), register r: key j0 + 32 mb + 8 (r/4) + 4 g + r%4, query qi
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int jl = 32 * mb + 8 * q4 + 4 * g;
+          const f32x4 k4 = *reinterpret_cast<const f32x4*>(KSs + jl);
+          float p[4], ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[4 * q4 + e] * k4[e] - lq);
+          if (cls == TILE_PARTIAL) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              p[e] = ((unsigned)(t0 + 32 * mb + 8 * q4 + e) <= (unsigned)W) ? p[e] : 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp[4 * q4 + e] - dlt) * k4[e];
+          const int st = 2 * mb + (q4 >> 1), el = 2 * (q4 & 1);
+          dsf[st][el] = pack_bf16(ds[0], ds[1]);
+          dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
+        }
+      }
+      // dQ^T[d, q] += K^T[d, kv] (dS kscale)^T[kv, q]
+#pragma unroll
+      for (int s2 = 0; s2 < C::BN / 16; ++s2)
+#pragma unroll
+        for (int n = 0; n < C::NB; ++n)
+          acc[n] = mfma32(tr_operand(Ks, t_off, 16 * s2, 32 * n, C::P), dsf[s2], acc[n]);
+    }
+    if (jt < jt1) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past T dropped)
+  const rsrc_t rstat_q = make_rsrc(rq + sb, 4LL * T);
+  const float r = bload4f(rstat_q, qi * 4);
+  const rsrc_t rqr = make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+  float dot = 0.f;
+  f32x16 xh[C::NB];
+#pragma unroll
+  for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const u32x2 qq = bload8(rqr, (c * rs + 32 * n + 8 * q4 + 4 * g) * 2);
+      const float x[4] = {bf_lo(qq[0]), bf_hi(qq[0]), bf_lo(qq[1]), bf_hi(qq[1])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xh[n][4 * q4 + e] = x[e] * r;
+        acc[n][4 * q4 + e] *= (1.0f / kLog2e);
+        dot += acc[n][4 * q4 + e] * xh[n][4 * q4 + e];
       }
     }
-    // dQ^T[d, q] += K^T[d, kv] (dS kscale)^T[kv, q]
+  dot += __shfl_xor(dot, 32);
+  const float mean = dot * (1.0f / D);
+  const rsrc_t rdq = make_rsrc(dq + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
 #pragma unroll
-    for (int s = 0; s < C::BN / 16; ++s)
+  for (int n = 0; n < C::NB; ++n)
 #pragma unroll
-      for (int n = 0; n < C::NB; ++n)
-        acc[n] = mfma32(ld16(KTs + (32 * n + c) * C::TP + 16 * s + 8 * g), dsf[s], acc[n]);
-  }
-
-  // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q
-  if (qi < T) {
-    const float r = rq[sb + qi];
-    const uint16_t* qrow = q + base + (size_t)qi * rs;
-    float dot = 0.f;
-    f32x16 xh[C::NB];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float y[4];
 #pragma unroll
-    for (int n = 0; n < C::NB; ++n)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2 qq = ld8(qrow + 32 * n + 8 * q4 + 4 * g);
-        float x[4] = {bf_lo(qq[0]), bf_hi(qq[0]), bf_lo(qq[1]), bf_hi(qq[1])};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xh[n][4 * q4 + e] = x[e] * r;
-          acc[n][4 * q4 + e] *= (1.0f / kLog2e);
-          dot += acc[n][4 * q4 + e] * xh[n][4 * q4 + e];
-        }
-      }
-    dot += __shfl_xor(dot, 32);
-    const float mean = dot * (1.0f / D);
-    uint16_t* dqrow = dq + base + (size_t)qi * rs;
-#pragma unroll
-    for (int n = 0; n < C::NB; ++n)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = r * (acc[n][4 * q4 + e] - xh[n][4 * q4 + e] * mean);
-        st8(dqrow + 32 * n + 8 * q4 + 4 * g, u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
-      }
-  }
+      for (int e = 0; e < 4; ++e) y[e] = r * (acc[n][4 * q4 + e] - xh[n][4 * q4 + e] * mean);
+      bstore8(u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])}, rdq,
+              (c * rs + 32 * n + 8 * q4 + 4 * g) * 2);
+    }
 }
 
 template <int D>
@@ -483,6 +516,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   }
   {
     using C = DqCfg<D>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(bwd_dq_kernel<D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
     const int nqt = (a.T + C::BM - 1) / C::BM;
     ProfToken t2 = prof_begin(K_BWD_DQ, stream);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,

@@ -62,8 +62,8 @@ def algorithmic_units(kid, B, T, H, D, n_vis):
         return FLOPS_PER_PAIR_D[kid] * D * n_vis * B * H, "flop"
     if kid == 0:   # read K, write the key scales
         return 2 * E + 4 * B * H * T, "byte"
-    # bwd_prep: read q, k, o, dO; write q_hat and three [B, H, T] fp32 rows
-    return 4 * 2 * E + 2 * E + 3 * 4 * B * H * T, "byte"
+    # bwd_prep: read q, k, o, dO and lse; write q_hat and four [B, H, T] fp32 rows
+    return 4 * 2 * E + 2 * E + 5 * 4 * B * H * T, "byte"
 
 
 def cpu_baseline(wl, windows, budget_s):

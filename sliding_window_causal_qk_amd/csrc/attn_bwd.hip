@@ -20,6 +20,8 @@
 //   bwd_dq:    a workgroup owns 128 queries (32 per wave) and walks the key
 //              tiles of its band, recomputing S and dP; the RMSNorm backward
 //              of Q runs in the epilogue.  No atomics: dQ is deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "band.h"
 #include "kernels.h"
@@ -33,7 +35,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
     uint16_t* __restrict__ qhat, float* __restrict__ rq, float* __restrict__ kscale,
-    float* __restrict__ delta, int nrows, int T, int H, float eps) {
+    float* __restrict__ delta, const float* __restrict__ lse, float* __restrict__ lse2,
+    int nrows, int T, int H, float eps) {
   constexpr int LPR = D / 8;
   const int tid = blockIdx.x * 256 + threadIdx.x;
   const int row = tid / LPR;
@@ -74,6 +77,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
       rq[s] = r;
       kscale[s] = (1.0f / sqrtf(ssk * (1.0f / D) + eps)) * (kLog2e / sqrtf((float)D));
       delta[s] = dot;
+      lse2[s] = lse[s] * kLog2e;
     }
   }
 }
@@ -114,29 +118,37 @@ __device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int off, int r
 }
 
 // ------------------------------------------------------------------ dK / dV
-// Workgroup: 4 waves; wave w owns keys j0 + 32 w + c.  Query blocks of 64
-// rows (q_hat and dO, row-major, double-buffered in LDS) stream through the
-// band.  Per block: S = Q_hat K^T and dP = dO V^T (keys in lanes, queries in
-// registers), P and dS in registers, then dV^T += dO^T P and dK_hat^T +=
-// Q_hat^T dS with the transposed operands read straight from the row-major
-// tiles.
+// Workgroup: 4 waves; wave w owns keys j0 + 32 w + c.  Query blocks of 32
+// rows (q_hat, dO and their lse, Delta) stream through the band in four LDS
+// buffers filled by direct-to-LDS loads issued three steps ahead.  Per block i:
+//   A(i): S = Q_hat K^T and dP = dO V^T    (keys in lanes, queries in registers)
+//   B(i): P = exp2(S kscale - lse log2 e), dS = P (dP - Delta)      (VALU)
+//   C(i): dV^T += dO^T P, dK_hat^T += Q_hat^T dS  (transposed operands read
+//         straight from the row-major tiles)
+// The loop issues A(i+1) and C(i) back to back, then B(i+1): the softmax of
+// the next block runs on the VALU while the matrix cores still work through
+// C(i), and LDS reads for both products are in flight together.
 template <int D>
 struct DkdvCfg {
   static constexpr int BNK = 128;       // keys per workgroup (32 per wave)
-  static constexpr int BMQ = 64;        // queries per step
+  static constexpr int BMQ = 32;        // queries per step
+  static constexpr int NBUF = 4;
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
   static constexpr int P = D + 24;      // row pitch (bf16): odd multiple of 16 bytes
-  static constexpr int T_LDS = BMQ * P;
-  static constexpr int STAGE = 2 * T_LDS * 2 + 2 * BMQ * 4;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  using Tile = DmaTile<D, BMQ, P>;
+  static constexpr int DO_B = Tile::BYTES;          // dO tile after the q_hat tile
+  static constexpr int ST_B = 2 * Tile::BYTES;      // lse2 (256 B), Delta (256 B), 2 spare
+  static constexpr int STAGE = ST_B + 1024;
+  static constexpr int LDS_BYTES = NBUF * STAGE;
+  static constexpr int NPS = 2 * Tile::NIW + 1;     // direct loads per wave per step
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qhat, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ lse2, const float* __restrict__ delta,
     const float* __restrict__ kscale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     int T, int H, int W) {
   using C = DkdvCfg<D>;
@@ -180,95 +192,131 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   int q_lo, q_hi;
   const bool any = q_range(j0, j0 + C::BNK - 1, T, W, &q_lo, &q_hi);
-  const int qb0 = any ? q_lo / C::BMQ : 0, qb1 = any ? q_hi / C::BMQ : -1;
+  const int qb0 = any ? q_lo / C::BMQ : 0;
+  const int nsteps = any ? q_hi / C::BMQ - qb0 + 1 : 0;
 
-  RowStage<D, C::BMQ, C::P> sq, sdo;
-  float lreg = 0.f;
-  const rsrc_t rl = make_rsrc(lse + sb, 4LL * T);
-  const rsrc_t rd = make_rsrc(delta + sb, 4LL * T);
+  // ---- direct-to-LDS staging of one step into the buffer at byte offset `base`
+  typename C::Tile tile;
+  tile.init(w, lane, rs);
+  // stats: wave 0 loads lse2, wave 1 Delta, waves 2 and 3 a spare (out of range)
+  const rsrc_t rstat = make_rsrc(w == 0 ? lse2 + sb : delta + sb, w < 2 ? 4LL * T : 0);
   const uint16_t* qh_s = qhat + sbase;
   const uint16_t* do_s = dout + sbase;
-  auto load_blk = [&](int qb) {
-    const int r0 = qb * C::BMQ;
-    sq.load(make_rsrc(qh_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
-    sdo.load(make_rsrc(do_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
-    if (tid < C::BMQ) lreg = bload4f(rl, (r0 + tid) * 4) * kLog2e;
-    else if (tid < 2 * C::BMQ) lreg = bload4f(rd, (r0 + tid - C::BMQ) * 4);
+  auto issue_step = [&](int step, int base) {
+    const int r0 = (qb0 + step) * C::BMQ;
+    tile.issue(make_rsrc(qh_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base, w);
+    tile.issue(make_rsrc(do_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base + C::DO_B, w);
+    dma_row4(rstat, smem, base + C::ST_B + 256 * w, (r0 + lane) * 4);
   };
-  auto store_blk = [&](int buf) {
-    uint16_t* Qs = reinterpret_cast<uint16_t*>(smem + buf * C::STAGE);
-    sq.store(Qs, tid);
-    sdo.store(Qs + C::T_LDS, tid);
-    if (tid < 2 * C::BMQ) reinterpret_cast<float*>(Qs + 2 * C::T_LDS)[tid] = lreg;
+  auto cls_of = [&](int step) {
+    const int q0 = (qb0 + step) * C::BMQ;
+    return uniform(tile_class(q0, q0 + C::BMQ - 1, kw0, kw0 + 31, T, W));
   };
 
-  const int a_off = c * C::P + 8 * g;        // row-major A operands (16-byte reads)
-  const int t_off = tr_off(lane, C::P);      // transposed A operands
+  // per-lane byte offsets inside a stage buffer
+  const int a_off = 2 * (c * C::P + 8 * g);          // row-major A operands (16-byte reads)
+  const int t_off = 2 * tr_off(lane, C::P);          // transposed A operands
+  const int l_off = C::ST_B + 16 * g;                // lse2 / Delta of the lane's query quads
   // visibility on partial blocks: 0 <= q - kj <= lim, lim = min(W, T - 1 - kj)
   const int lim = imin(W, T - 1 - kj);
 
-  if (qb0 <= qb1) {
-    load_blk(qb0);
-    store_blk(0);
-  }
-  __syncthreads();
-  for (int qb = qb0; qb <= qb1; ++qb) {
-    const int buf = (qb - qb0) & 1;
-    if (qb < qb1) load_blk(qb + 1);
+  f32x16 s_acc, dp_acc;
+  u32x4 pf[2], dsf[2];
 
-    const int q0 = qb * C::BMQ;
-    const int cls = uniform(tile_class(q0, q0 + C::BMQ - 1, kw0, kw0 + 31, T, W));
-    if (cls != TILE_EMPTY) {
-      const uint16_t* Qs = reinterpret_cast<const uint16_t*>(smem + buf * C::STAGE);
-      const uint16_t* dOs = Qs + C::T_LDS;
-      const float* Ls = reinterpret_cast<const float*>(Qs + 2 * C::T_LDS);
-      const float* Dls = Ls + C::BMQ;
-
-      u32x4 pf[C::BMQ / 16], dsf[C::BMQ / 16];
+  // A: scores and dP of one step
+  auto stage_a = [&](int base) {
+    const int va = base + a_off;
+    s_acc = f32x16{};
+    dp_acc = f32x16{};
 #pragma unroll
-      for (int mb = 0; mb < C::BMQ / 32; ++mb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int ks = 0; ks < C::KS; ++ks) {
+      s_acc = mfma32(lds16(smem, va + 32 * ks), kf[ks], s_acc);
+      dp_acc = mfma32(lds16(smem, va + C::DO_B + 32 * ks), vf[ks], dp_acc);
+    }
+  };
+  // B: probabilities and dS of one step (lane (g, c), register r: query
+  // q0 + 8 (r/4) + 4 g + r%4, key kj)
+  auto stage_b = [&](int base, int step, int cls) {
+    const int vl = base + l_off;
+    const int t0 = (qb0 + step) * C::BMQ + 4 * g - kj;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          s = mfma32(ld16(Qs + a_off + 32 * mb * C::P + 16 * ks), kf[ks], s);
-          dp = mfma32(ld16(dOs + a_off + 32 * mb * C::P + 16 * ks), vf[ks], dp);
-        }
-        // lane (g, c), register r: query q0 + 32 mb + 8 (r/4) + 4 g + r%4, key kj
-        const int t0 = q0 + 32 * mb + 4 * g - kj;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 l4 = lds16f(smem, vl + 32 * q4);
+      const f32x4 d4 = lds16f(smem, vl + 256 + 32 * q4);
+      float p[4], ds[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ql = 32 * mb + 8 * q4 + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + ql);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dls + ql);
-          float p[4], ds[4];
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * ksc - l4[e]);
+      if (cls == TILE_PARTIAL) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[4 * q4 + e] * ksc - l4[e]);
-          if (cls == TILE_PARTIAL) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              p[e] = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp[4 * q4 + e] - d4[e]);
-          const int st = 2 * mb + (q4 >> 1), el = 2 * (q4 & 1);
-          pf[st][el] = pack_bf16(p[0], p[1]);
-          pf[st][el + 1] = pack_bf16(p[2], p[3]);
-          dsf[st][el] = pack_bf16(ds[0], ds[1]);
-          dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
-        }
+        for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
       }
-      // dV^T[d, kv] += dO^T[d, q] P[q, kv];  dK_hat^T[d, kv] += Q_hat^T[d, q] dS[q, kv]
 #pragma unroll
-      for (int s2 = 0; s2 < C::BMQ / 16; ++s2) {
+      for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp_acc[4 * q4 + e] - d4[e]);
+      const int st = q4 >> 1, el = 2 * (q4 & 1);
+      pf[st][el] = pack_bf16(p[0], p[1]);
+      pf[st][el + 1] = pack_bf16(p[2], p[3]);
+      dsf[st][el] = pack_bf16(ds[0], ds[1]);
+      dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
+    }
+  };
+  // C: dV^T[d, kv] += dO^T[d, q] P[q, kv];  dK_hat^T[d, kv] += Q_hat^T[d, q] dS[q, kv]
+  // (element j of a k-step s2 is query 16 s2 + 4 g + (j % 4) + 8 (j / 4))
+  auto stage_c = [&](int base) {
+    const int vt = base + t_off;
 #pragma unroll
-        for (int n = 0; n < C::NB; ++n) {
-          acc_dv[n] = mfma32(tr_operand(dOs, t_off, 16 * s2, 32 * n, C::P), pf[s2], acc_dv[n]);
-          acc_dk[n] = mfma32(tr_operand(Qs, t_off, 16 * s2, 32 * n, C::P), dsf[s2], acc_dk[n]);
-        }
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int n = 0; n < C::NB; ++n) {
+        constexpr int R8 = 2 * 8 * C::P;
+        const int o = 2 * (16 * s2 * C::P + 32 * n);
+        const u32x2 a0 = lds_tr4b(smem, vt + C::DO_B + o), a1 = lds_tr4b(smem, vt + C::DO_B + o + R8);
+        const u32x2 b0 = lds_tr4b(smem, vt + o), b1 = lds_tr4b(smem, vt + o + R8);
+        acc_dv[n] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[s2], acc_dv[n]);
+        acc_dk[n] = mfma32(u32x4{b0[0], b0[1], b1[0], b1[1]}, dsf[s2], acc_dk[n]);
       }
     }
-    if (qb < qb1) store_blk(buf ^ 1);
+  };
+  // C runs every step (empty steps carry zero P and dS), which keeps the
+  // accumulators in one register class across the loop
+  auto zero_pds = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pf[i] = dsf[i] = u32x4{0, 0, 0, 0};
+  };
+
+  // ---- prologue: steps 0..3 issued; wait for 0 and 1; A(0), B(0).
+  // Buffers rotate: step i lives in buffer i % 4.
+  int b0 = 0, b1 = C::STAGE, b2 = 2 * C::STAGE, b3 = 3 * C::STAGE;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nsteps) issue_step(i, i * C::STAGE);
+  if (nsteps >= 4) wait_vmcnt<2 * C::NPS>();
+  else if (nsteps == 3) wait_vmcnt<C::NPS>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  const int cls0 = nsteps > 0 ? cls_of(0) : TILE_EMPTY;
+  if (cls0 != TILE_EMPTY) {
+    stage_a(b0);
+    stage_b(b0, 0, cls0);
+  } else {
+    zero_pds();
+  }
+
+  for (int it = 0; it < nsteps; ++it) {
+    const int cls_next = (it + 1 < nsteps) ? cls_of(it + 1) : TILE_EMPTY;
+    if (cls_next != TILE_EMPTY) stage_a(b1);
+    stage_c(b0);
+    if (cls_next != TILE_EMPTY) stage_b(b1, it + 1, cls_next);
+    else zero_pds();
+    // step it + 2 must have landed before the barrier; step it + 3 may stay in flight
+    if (it + 3 < nsteps) wait_vmcnt<C::NPS>();
+    else wait_vmcnt<0>();
     __syncthreads();
+    if (it + 4 < nsteps) issue_step(it + 4, b0);   // buffer of step it, consumed
+    const int t = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = b3;
+    b3 = t;
   }
 
   // ---- epilogue: lane (g, c) holds key kj, d = 32 n + 8 q4 + 4 g + e
@@ -495,8 +543,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   ProfToken t0 = prof_begin(K_BWD_PREP, stream);
   hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(nblk_p), dim3(256), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.o,
-                     (const uint16_t*)a.dout, (uint16_t*)a.qhat, a.rq, a.kscale, a.delta, nrows,
-                     a.T, a.H, a.eps);
+                     (const uint16_t*)a.dout, (uint16_t*)a.qhat, a.rq, a.kscale, a.delta, a.lse,
+                     a.lse2, nrows, a.T, a.H, a.eps);
   prof_end(t0);
   const int W = eff_window(a.T, a.window);
   {
@@ -510,7 +558,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(nkt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
                        (const uint16_t*)a.qhat, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, (const float*)a.delta,
+                       (const uint16_t*)a.dout, (const float*)a.lse2, (const float*)a.delta,
                        (const float*)a.kscale, (uint16_t*)a.dk, (uint16_t*)a.dv, a.T, a.H, W);
     prof_end(t1);
   }

@@ -92,6 +92,69 @@ __device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<SW_LDS bf16x4*>(q)));
 }
 
+// LDS accesses at a per-lane byte address plus a compile-time displacement,
+// which the compiler folds into the instruction's offset field.
+__device__ __forceinline__ u32x4 lds16(const unsigned char* smem, int addr) {
+  return *reinterpret_cast<const u32x4*>(smem + addr);
+}
+__device__ __forceinline__ f32x4 lds16f(const unsigned char* smem, int addr) {
+  return *reinterpret_cast<const f32x4*>(smem + addr);
+}
+__device__ __forceinline__ u32x2 lds_tr4b(const unsigned char* smem, int addr) {
+  return lds_tr4(reinterpret_cast<const uint16_t*>(smem + addr));
+}
+
+// ---- direct-to-LDS tiles.  A buffer_load ... lds instruction writes the 16
+// bytes of lane l at LDS (M0 base + 16 l), i.e. one contiguous KiB per wave.
+// DmaTile fills a tile of R rows of D bf16 stored with a padded row pitch of
+// P bf16 (P * 2 an odd multiple of 16 bytes, so row-wise and transposed LDS
+// reads avoid bank conflicts): LDS chunk q (16 bytes) of the tile holds row
+// q / CPR, chunk q % CPR of the source; pad chunks and rows past R read out of
+// the descriptor's range, i.e. zero.  The tile is covered by NI wave
+// instructions (a multiple of 4, so each wave of a 256-thread workgroup issues
+// the same number, NIW); wave w issues instructions w, w + 4, ...
+template <int D, int R, int P>
+struct DmaTile {
+  static constexpr int CPR = P / 8;
+  static constexpr int NCH = R * CPR;
+  static constexpr int NI = ((NCH + 63) / 64 + 3) / 4 * 4;
+  static constexpr int NIW = NI / 4;
+  static constexpr int BYTES = NI * 1024;
+  static_assert((P * 2) % 16 == 0, "pitch must be a whole number of 16-byte chunks");
+
+  int voff[NIW];   // per-lane byte offset into the source, per instruction
+
+  // rs: source row stride in elements
+  __device__ __forceinline__ void init(int w, int lane, int rs) {
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int q = 64 * (w + 4 * i) + lane;
+      const int r = q / CPR, ch = q % CPR;
+      voff[i] = (r < R && ch < D / 8) ? (r * rs + 8 * ch) * 2 : 0x7ffffff0;
+    }
+  }
+  // rs_tile: descriptor starting at the tile's first source row;
+  // lds_base: byte offset of the tile in dynamic LDS (wave-uniform)
+  __device__ __forceinline__ void issue(rsrc_t rs_tile, unsigned char* smem, int lds_base, int w) const {
+#pragma unroll
+    for (int i = 0; i < NIW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs_tile, (SW_LDS void*)(smem + lds_base + 1024 * (w + 4 * i)), 16, voff[i], 0, 0, 0);
+  }
+};
+
+// One 64-lane 4-byte direct-to-LDS load (256 bytes at lds_base + 4 lane).
+__device__ __forceinline__ void dma_row4(rsrc_t r, unsigned char* smem, int lds_base, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SW_LDS void*)(smem + lds_base), 4, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Workgroups are handed to the 8 XCDs round-robin by id.  Remap so that each
 // XCD walks one contiguous range of logical ids (neighbouring tiles of the same
 // (batch, head) then share that XCD's L2).

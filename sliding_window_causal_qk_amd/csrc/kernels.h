@@ -34,6 +34,7 @@ struct BwdArgs {
   float* rq;      // [B, H, T]: 1 / rms(q)
   float* kscale;  // [B, H, T]: log2(e) / sqrt(D) / rms(k)
   float* delta;   // [B, H, T]: rowsum(dO * O)
+  float* lse2;    // [B, H, T]: lse * log2(e)
   int B, T, H, D;
   int window;
   float eps;

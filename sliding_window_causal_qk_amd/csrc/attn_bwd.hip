@@ -208,11 +208,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     tile.issue(make_rsrc(do_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base + C::DO_B, w);
     dma_row4(rstat, smem, base + C::ST_B + 256 * w, (r0 + lane) * 4);
   };
-  auto cls_of = [&](int step) {
-    const int q0 = (qb0 + step) * C::BMQ;
-    return uniform(tile_class(q0, q0 + C::BMQ - 1, kw0, kw0 + 31, T, W));
-  };
-
   // per-lane byte offsets inside a stage buffer
   const int a_off = 2 * (c * C::P + 8 * g);          // row-major A operands (16-byte reads)
   const int t_off = 2 * tr_off(lane, C::P);          // transposed A operands
@@ -235,8 +230,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
   // B: probabilities and dS of one step (lane (g, c), register r: query
-  // q0 + 8 (r/4) + 4 g + r%4, key kj)
-  auto stage_b = [&](int base, int step, int cls) {
+  // q0 + 8 (r/4) + 4 g + r%4, key kj).  MASKED is a compile-time flag so each
+  // loop version is one straight-line block the scheduler can interleave.
+  auto stage_b = [&](int base, int step, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int vl = base + l_off;
     const int t0 = (qb0 + step) * C::BMQ + 4 * g - kj;
 #pragma unroll
@@ -246,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       float p[4], ds[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * ksc - l4[e]);
-      if (cls == TILE_PARTIAL) {
+      if (MASKED) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
       }
@@ -293,20 +290,50 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   else if (nsteps == 3) wait_vmcnt<C::NPS>();
   else wait_vmcnt<0>();
   __syncthreads();
-  const int cls0 = nsteps > 0 ? cls_of(0) : TILE_EMPTY;
-  if (cls0 != TILE_EMPTY) {
+  const std::integral_constant<bool, true> masked{};
+  const std::integral_constant<bool, false> unmasked{};
+  if (nsteps > 0) {
     stage_a(b0);
-    stage_b(b0, 0, cls0);
+    stage_b(b0, 0, masked);
   } else {
     zero_pds();
   }
 
-  for (int it = 0; it < nsteps; ++it) {
-    const int cls_next = (it + 1 < nsteps) ? cls_of(it + 1) : TILE_EMPTY;
-    if (cls_next != TILE_EMPTY) stage_a(b1);
+  // One pipelined step: A(it+1), C(it), B(it+1), then the hand-off of the
+  // buffers.  The instruction order inside a step is fixed with schedule
+  // groups: A(it+1)'s reads and MFMAs first, then C(it)'s MFMAs with their
+  // transposed reads, with B(it+1)'s VALU work slotted between.
+  // (valid for it + 1 < nsteps; the last step only runs C)
+  auto step_body = [&](int it, auto masked_c) {
+    // A: keep 8 LDS reads in flight ahead of the MFMAs (LDS latency is several
+    // MFMA issue slots)
+    stage_a(b1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::KS - 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);   // A stays ahead of C and B
+    // C with B: transposed reads four MFMAs ahead, softmax VALU between MFMAs
     stage_c(b0);
-    if (cls_next != TILE_EMPTY) stage_b(b1, it + 1, cls_next);
-    else zero_pds();
+    stage_b(b1, it + 1, masked_c);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * C::NB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+    // keep B's results inside this step (the compiler would otherwise sink the
+    // softmax below the barrier, away from the MFMAs it should overlap)
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
     // step it + 2 must have landed before the barrier; step it + 3 may stay in flight
     if (it + 3 < nsteps) wait_vmcnt<C::NPS>();
     else wait_vmcnt<0>();
@@ -317,7 +344,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     b1 = b2;
     b2 = b3;
     b3 = t;
+  };
+
+  // Steps whose B needs the element mask (some key of the workgroup outside
+  // some query's window) sit at both ends of the band; the middle runs the
+  // unmasked body.  `full_lo .. full_hi` are the steps visible in full to every
+  // key of the workgroup: q0 >= j0 + BNK - 1 and q0 + BMQ - 1 <= j0 + W, q0 + BMQ <= T.
+  const int kv_last = imin(j0 + C::BNK - 1, T - 1);
+  int full_lo = 0, full_hi = -1;
+  if (nsteps > 0) {
+    const int qf0 = kv_last;                                  // first fully causal query
+    const int qf1 = imin(j0 + W, T) - (C::BMQ - 1);           // last start of a fully inside step
+    full_lo = imax(0, (qf0 + C::BMQ - 1) / C::BMQ - qb0);
+    full_hi = qf1 >= 0 ? qf1 / C::BMQ - qb0 : -1;
+    full_hi = imin(full_hi, nsteps - 1);
   }
+  // body of step `it` prepares B(it + 1): unmasked iff step it + 1 is full
+  const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // it in [u0, u1] -> unmasked
+  const int nloop = nsteps - 1;   // steps with a successor
+  int it = 0;
+  for (; it < imin(u0, nloop); ++it) step_body(it, masked);
+  for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
+  for (; it < nloop; ++it) step_body(it, masked);
+  if (nsteps > 0) stage_c(b0);
 
   // ---- epilogue: lane (g, c) holds key kj, d = 32 n + 8 q4 + 4 g + e
   const float rk = ksc * (sqrtf((float)D) / kLog2e);

@@ -136,7 +136,7 @@ struct DkdvCfg {
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
   static constexpr int P = D + 24;      // row pitch (bf16): odd multiple of 16 bytes
-  using Tile = DmaTile<D, BMQ, P>;
+  using Tile = DmaTile<D, BMQ, P, 0>;
   static constexpr int DO_B = Tile::BYTES;          // dO tile after the q_hat tile
   static constexpr int ST_B = 2 * Tile::BYTES;      // lse2 (256 B), Delta (256 B), 2 spare
   static constexpr int STAGE = ST_B + 1024;
@@ -406,27 +406,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ dQ
-// Workgroup: 4 waves; wave w owns queries i0 + 32 w + c.  Key tiles of 64 rows
-// (K, V row-major, double-buffered) stream through the band.  Per tile:
-// S^T = K Q_hat^T and dP^T = V dO^T (queries in lanes), dS scaled by each
-// key's kscale, then dQ^T += K^T dS^T with K^T read transposed from the tile.
+// Workgroup: 4 waves; wave w owns queries i0 + 32 w + c.  Key blocks of 32
+// rows (K, V and their kscale) stream through the band in three LDS buffers
+// filled by direct-to-LDS loads one step ahead.  Per block i:
+//   A(i): S^T = K Q_hat^T and dP^T = V dO^T   (queries in lanes, keys in registers)
+//   B(i): dS' = exp2(S^T kscale - lse log2 e) (dP^T - Delta) kscale      (VALU)
+//   C(i): dQ^T += K^T dS'^T   (K^T read transposed from the row-major K tile)
+// As in the dK/dV kernel the loop issues A(i+1), C(i), then B(i+1).  The
+// kernel fits two waves per SIMD, so the hardware also overlaps two
+// workgroups' phases.
 template <int D>
 struct DqCfg {
   static constexpr int BM = 128;   // queries per workgroup (32 per wave)
-  static constexpr int BN = 64;    // keys per step
+  static constexpr int BN = 32;    // keys per step
+  static constexpr int NBUF = 3;
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
   static constexpr int P = D + 24;
-  static constexpr int T_LDS = BN * P;
-  static constexpr int STAGE = 2 * T_LDS * 2 + BN * 4;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  using Tile = DmaTile<D, BN, P, 1>;
+  static constexpr int V_B = Tile::BYTES;          // V tile after the K tile
+  static constexpr int ST_B = 2 * Tile::BYTES;     // kscale (256 B), 3 spare
+  static constexpr int STAGE = ST_B + 1024;
+  static constexpr int LDS_BYTES = NBUF * STAGE;
+  static constexpr int NPS = 2 * Tile::NIW + 1;    // direct loads per wave per step
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ qhat,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, const float* __restrict__ rq,
     const float* __restrict__ kscale, uint16_t* __restrict__ dq, int T, int H, int W) {
   using C = DqCfg<D>;
@@ -460,9 +469,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       df[ks] = bload16(rdo, (c * rs + 16 * ks + 8 * g) * 2);
     }
   }
-  const rsrc_t rstat_l = make_rsrc(lse + sb, 4LL * T);
+  const rsrc_t rstat_l = make_rsrc(lse2 + sb, 4LL * T);
   const rsrc_t rstat_d = make_rsrc(delta + sb, 4LL * T);
-  const float lq = bload4f(rstat_l, qi * 4) * kLog2e;
+  const float lq = bload4f(rstat_l, qi * 4);
   const float dlt = bload4f(rstat_d, qi * 4);
 
   f32x16 acc[C::NB];
@@ -471,85 +480,127 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 
   int kv_lo, kv_hi;
   kv_range(i0, i0 + C::BM - 1, T, W, &kv_lo, &kv_hi);
-  const int jt0 = kv_lo / C::BN, jt1 = kv_hi / C::BN;
+  const int jb0 = kv_lo / C::BN;
+  const int nsteps = kv_hi / C::BN - jb0 + 1;
 
-  RowStage<D, C::BN, C::P> sk, sv;
-  float ksreg = 0.f;
-  const rsrc_t rks = make_rsrc(kscale + sb, 4LL * T);
+  // ---- direct-to-LDS staging of one key step
+  typename C::Tile tile;
+  tile.init(w, lane, rs);
+  const rsrc_t rks = make_rsrc(kscale + sb, w == 0 ? 4LL * T : 0);   // wave 0 loads kscale
   const uint16_t* k_s = k + sbase;
   const uint16_t* v_s = v + sbase;
-  auto load_tile = [&](int jt) {
-    const int r0 = jt * C::BN;
-    sk.load(make_rsrc(k_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
-    sv.load(make_rsrc(v_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), rs, tid);
-    if (tid < C::BN) ksreg = bload4f(rks, (r0 + tid) * 4);
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + buf * C::STAGE);
-    sk.store(Ks, tid);
-    sv.store(Ks + C::T_LDS, tid);
-    if (tid < C::BN) reinterpret_cast<float*>(Ks + 2 * C::T_LDS)[tid] = ksreg;
+  auto issue_step = [&](int step, int base) {
+    const int r0 = (jb0 + step) * C::BN;
+    tile.issue(make_rsrc(k_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base, w);
+    tile.issue(make_rsrc(v_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base + C::V_B, w);
+    dma_row4(rks, smem, base + C::ST_B + 256 * w, (r0 + lane) * 4);
   };
 
-  const int a_off = c * C::P + 8 * g;
-  const int t_off = tr_off(lane, C::P);
+  const int a_off = 2 * (c * C::P + 8 * g);
+  const int t_off = 2 * tr_off(lane, C::P);
+  const int k_off = C::ST_B + 16 * g;   // kscale of the lane's key quads
 
-  if (jt0 <= jt1) {
-    load_tile(jt0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int jt = jt0; jt <= jt1; ++jt) {
-    const int buf = (jt - jt0) & 1;
-    if (jt < jt1) load_tile(jt + 1);
+  f32x16 s_acc, dp_acc;
+  u32x4 dsf[2];
 
-    const int j0 = jt * C::BN;
-    const int cls = uniform(tile_class(qw0, qw0 + 31, j0, j0 + C::BN - 1, T, W));
-    if (cls != TILE_EMPTY) {
-      const uint16_t* Ks = reinterpret_cast<const uint16_t*>(smem + buf * C::STAGE);
-      const uint16_t* Vs = Ks + C::T_LDS;
-      const float* KSs = reinterpret_cast<const float*>(Ks + 2 * C::T_LDS);
-
-      u32x4 dsf[C::BN / 16];
-      const int t0 = j0 + 4 * g + W - qi;  // key kv visible iff 0 <= kv - (qi - W) <= W
+  auto stage_a = [&](int base) {
+    const int va = base + a_off;
+    s_acc = f32x16{};
+    dp_acc = f32x16{};
 #pragma unroll
-      for (int mb = 0; mb < C::BN / 32; ++mb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          s = mfma32(ld16(Ks + a_off + 32 * mb * C::P + 16 * ks), qf[ks], s);
-          dp = mfma32(ld16(Vs + a_off + 32 * mb * C::P + 16 * ks), df[ks], dp);
-        }
-        // lane (g, c), register r: key j0 + 32 mb + 8 (r/4) + 4 g + r%4, query qi
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int jl = 32 * mb + 8 * q4 + 4 * g;
-          const f32x4 k4 = *reinterpret_cast<const f32x4*>(KSs + jl);
-          float p[4], ds[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s[4 * q4 + e] * k4[e] - lq);
-          if (cls == TILE_PARTIAL) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              p[e] = ((unsigned)(t0 + 32 * mb + 8 * q4 + e) <= (unsigned)W) ? p[e] : 0.f;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp[4 * q4 + e] - dlt) * k4[e];
-          const int st = 2 * mb + (q4 >> 1), el = 2 * (q4 & 1);
-          dsf[st][el] = pack_bf16(ds[0], ds[1]);
-          dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
-        }
-      }
-      // dQ^T[d, q] += K^T[d, kv] (dS kscale)^T[kv, q]
-#pragma unroll
-      for (int s2 = 0; s2 < C::BN / 16; ++s2)
-#pragma unroll
-        for (int n = 0; n < C::NB; ++n)
-          acc[n] = mfma32(tr_operand(Ks, t_off, 16 * s2, 32 * n, C::P), dsf[s2], acc[n]);
+    for (int ks = 0; ks < C::KS; ++ks) {
+      s_acc = mfma32(lds16(smem, va + 32 * ks), qf[ks], s_acc);
+      dp_acc = mfma32(lds16(smem, va + C::V_B + 32 * ks), df[ks], dp_acc);
     }
-    if (jt < jt1) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+  // lane (g, c), register r: key j0 + 8 (r/4) + 4 g + r%4, query qi
+  auto stage_b = [&](int base, int step, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int vk = base + k_off;
+    const int t0 = (jb0 + step) * C::BN + 4 * g + W - qi;  // kv visible iff 0 <= kv - (qi - W) <= W
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 k4 = lds16f(smem, vk + 32 * q4);
+      float p[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * k4[e] - lq);
+      if (MASKED) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)W) ? p[e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp_acc[4 * q4 + e] - dlt) * k4[e];
+      const int st = q4 >> 1, el = 2 * (q4 & 1);
+      dsf[st][el] = pack_bf16(ds[0], ds[1]);
+      dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
+    }
+  };
+  // dQ^T[d, q] += K^T[d, kv] (dS kscale)^T[kv, q]
+  auto stage_c = [&](int base) {
+    const int vt = base + t_off;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int n = 0; n < C::NB; ++n) {
+        constexpr int R8 = 2 * 8 * C::P;
+        const int o = 2 * (16 * s2 * C::P + 32 * n);
+        const u32x2 a0 = lds_tr4b(smem, vt + o), a1 = lds_tr4b(smem, vt + o + R8);
+        acc[n] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsf[s2], acc[n]);
+      }
+  };
+
+  // ---- prologue: steps 0, 1 in LDS, step 2 in flight; A(0), B(0)
+  int b0 = 0, b1 = C::STAGE, b2 = 2 * C::STAGE;
+  if (nsteps > 0) issue_step(0, b0);
+  if (nsteps > 1) issue_step(1, b1);
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (nsteps > 2) issue_step(2, b2);
+  const std::integral_constant<bool, true> masked{};
+  const std::integral_constant<bool, false> unmasked{};
+  if (nsteps > 0) {
+    stage_a(b0);
+    stage_b(b0, 0, masked);
   }
+
+  auto step_body = [&](int it, auto masked_c) {
+    stage_a(b1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::KS - 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_c(b0);
+    stage_b(b1, it + 1, masked_c);
+    asm volatile("" ::"v"(dsf[0]), "v"(dsf[1]));
+    wait_vmcnt<0>();            // step it + 2 landed
+    __syncthreads();
+    if (it + 3 < nsteps) issue_step(it + 3, b0);   // buffer of step it, consumed
+    const int t = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = t;
+  };
+
+  // steps visible in full to every query of the workgroup: keys kv0 .. kv0 + 31
+  // with kv0 + 31 <= i0 and (i0 + BM - 1) - kv0 <= W (and all inside T)
+  int full_lo = nsteps, full_hi = -1;
+  if (nsteps > 0 && i0 + C::BM - 1 < T) {
+    const int lo_kv = i0 + C::BM - 1 - W;                  // first key visible to every query
+    full_lo = imax(0, (lo_kv + C::BN - 1) / C::BN - jb0);
+    full_hi = (i0 - (C::BN - 1)) >= 0 ? (i0 - (C::BN - 1)) / C::BN - jb0 : -1;
+    full_hi = imin(full_hi, nsteps - 1);
+  }
+  const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // body it prepares B(it + 1)
+  const int nloop = nsteps - 1;
+  int it = 0;
+  for (; it < imin(u0, nloop); ++it) step_body(it, masked);
+  for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
+  for (; it < nloop; ++it) step_body(it, masked);
+  if (nsteps > 0) stage_c(b0);
 
   // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past T dropped)
   const rsrc_t rstat_q = make_rsrc(rq + sb, 4LL * T);
@@ -621,7 +672,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     ProfToken t2 = prof_begin(K_BWD_DQ, stream);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.qhat, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, (const float*)a.lse2,
                        (const float*)a.delta, (const float*)a.rq, (const float*)a.kscale,
                        (uint16_t*)a.dq, a.T, a.H, W);
     prof_end(t2);

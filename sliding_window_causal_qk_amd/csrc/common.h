@@ -113,7 +113,10 @@ __device__ __forceinline__ u32x2 lds_tr4b(const unsigned char* smem, int addr) {
 // the descriptor's range, i.e. zero.  The tile is covered by NI wave
 // instructions (a multiple of 4, so each wave of a 256-thread workgroup issues
 // the same number, NIW); wave w issues instructions w, w + 4, ...
-template <int D, int R, int P>
+// KERNEL only makes the instantiation distinct per kernel: with two kernels
+// calling one instantiation of issue(), the host pass of this ROCm clang emits
+// no launch stub for the second kernel (an undefined symbol at load time).
+template <int D, int R, int P, int KERNEL>
 struct DmaTile {
   static constexpr int CPR = P / 8;
   static constexpr int NCH = R * CPR;

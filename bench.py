@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--workload", default="sssl_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain elementwise copy (torch.neg, fp32) over this many MiB, "
+                         "the reference point for scaling HBM counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -133,6 +136,17 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     print(f"[bench] workload {wl.name}: B={B} T={T} H={H} D={D} windows={windows}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 18          # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)              # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] copy calibration: 2 launches of {args.copy_calibration_mib} MiB read + "
+              f"{args.copy_calibration_mib} MiB written", file=sys.stderr, flush=True)
 
     layers = []
     for l, W in enumerate(windows):

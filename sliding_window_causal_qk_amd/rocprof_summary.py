@@ -1,0 +1,158 @@
+"""Turn rocprofv3 CSV output of a bench.py run into the short text summaries
+kept with the library, and into the per-launch HBM traffic table that
+bench.py reports beside its roofline.
+
+    # kernel durations: rocprofv3 --kernel-trace --stats -f csv -d DIR -- python3 bench.py ...
+    python -m sliding_window_causal_qk_amd.rocprof_summary trace --dir DIR --command "..." --out FILE
+
+    # HBM bytes: two counter runs of bench.py --copy-calibration-mib M (FETCH_SIZE, then WRITE_SIZE)
+    python -m sliding_window_causal_qk_amd.rocprof_summary traffic --fetch DIR1 --write DIR2 \\
+        --copy-mib M --command-fetch "..." --command-write "..." --out-json J --out-text FILE
+
+FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Each is scaled by the
+ratio of the known byte count of the calibration copy (torch.neg over M MiB of
+fp32: M MiB read, M MiB written) to what the same counter reads for it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# kernel symbol fragment -> short name used by bench.py
+SHORT = (("k_scale_kernel", "k_scale"), ("attn_fwd_kernel", "attn_fwd"), ("bwd_prep_kernel", "bwd_prep"),
+         ("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"))
+
+
+def short_name(kernel: str) -> str | None:
+    for frag, name in SHORT:
+        if frag in kernel:
+            return name
+    return None
+
+
+def kernel_sources_sha() -> str:
+    """Same digest as bench.py: every file of the kernel sources, by name."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sliding_window_causal_qk_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        sys.exit(f"no *{suffix} under {d}")
+    return hits[-1]
+
+
+def _rows(path: str):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row: dict, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(f"none of {names} in columns {list(row)}")
+
+
+def trace(args):
+    rows = _rows(_find(args.dir, "kernel_trace.csv"))
+    per = {}
+    for r in rows:
+        name = _col(r, "Kernel_Name", "Kernel-Name", "Name")
+        dur = (int(_col(r, "End_Timestamp", "End-Timestamp")) - int(_col(r, "Start_Timestamp", "Start-Timestamp"))) / 1e3
+        per.setdefault(name, []).append(dur)
+    total = sum(sum(v) for v in per.values())
+    lines = [f"# rocprofv3 kernel trace: {args.title}", "",
+             "Command (from the repository root):", "", "    " + args.command, "",
+             f"{'kernel':<12} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_ms':>9} {'pct':>6}  symbol"]
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{(short_name(name) or '-'):<12} {len(d):>6} {statistics.fmean(d):>9.2f} {min(d):>9.2f} "
+                     f"{max(d):>9.2f} {sum(d) / 1e3:>9.3f} {100 * sum(d) / total:>6.2f}  {name[:90]}")
+    lines += ["", f"kernel sources sha: {kernel_sources_sha()}"]
+    txt = "\n".join(lines) + "\n"
+    if args.out:
+        open(args.out, "w").write(txt)
+    print(txt)
+
+
+def _counter_means(d: str, counter: str):
+    rows = _rows(_find(d, "counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if _col(r, "Counter_Name", "Counter-Name") != counter:
+            continue
+        name = _col(r, "Kernel_Name", "Kernel-Name")
+        per.setdefault(name, []).append(float(_col(r, "Counter_Value", "Counter-Value")))
+    return {k: statistics.fmean(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
+
+
+def traffic(args):
+    fetch, nf = _counter_means(args.fetch, "FETCH_SIZE")
+    write, nw = _counter_means(args.write, "WRITE_SIZE")
+    copy_bytes = args.copy_mib * 1024 * 1024
+    cf = [k for k in fetch if "neg" in k]
+    cw = [k for k in write if "neg" in k]
+    if not cf or not cw:
+        sys.exit("calibration copy (torch.neg) not found in the counter output")
+    f_fac = copy_bytes / (fetch[cf[0]] * 1024.0)
+    w_fac = copy_bytes / (write[cw[0]] * 1024.0)
+    out = {"sources_sha": kernel_sources_sha(), "copy_mib": args.copy_mib,
+           "fetch_factor": f_fac, "write_factor": w_fac,
+           "command_fetch": args.command_fetch, "command_write": args.command_write, "kernels": {}}
+    lines = [f"# HBM traffic per launch from rocprofv3 counters: {args.title}", "",
+             "Commands (from the repository root):", "", "    " + args.command_fetch, "    " + args.command_write, "",
+             f"Calibration: torch.neg over {args.copy_mib} MiB fp32 reads FETCH_SIZE {fetch[cf[0]]:.0f} KiB and "
+             f"WRITE_SIZE {write[cw[0]]:.0f} KiB per launch for {copy_bytes // 1024} KiB each; "
+             f"scale factors {f_fac:.4f} (fetch), {w_fac:.4f} (write).", "",
+             f"{'kernel':<10} {'launches':>8} {'fetch_MB':>10} {'write_MB':>10} {'total_MB':>10}"]
+    for k in fetch:
+        name = short_name(k)
+        if name is None or k not in write:
+            continue
+        fb, wb = fetch[k] * 1024.0 * f_fac, write[k] * 1024.0 * w_fac
+        out["kernels"][name] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                                "bytes_per_launch": fb + wb, "launches": nf[k]}
+        lines.append(f"{name:<10} {nf[k]:>8} {fb / 1e6:>10.1f} {wb / 1e6:>10.1f} {(fb + wb) / 1e6:>10.1f}")
+    lines += ["", f"kernel sources sha: {out['sources_sha']}"]
+    json.dump(out, open(args.out_json, "w"), indent=1)
+    txt = "\n".join(lines) + "\n"
+    open(args.out_text, "w").write(txt)
+    print(txt)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--dir", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--title", default="")
+    t.add_argument("--out")
+    c = sub.add_parser("traffic")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--copy-mib", type=int, required=True)
+    c.add_argument("--command-fetch", required=True)
+    c.add_argument("--command-write", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--out-json", required=True)
+    c.add_argument("--out-text", required=True)
+    a = ap.parse_args()
+    trace(a) if a.mode == "trace" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,7 +94,8 @@ long long attn_visible_pairs(int T, int window);
 int attn_band_tiles(int T, int window, int rows, int cols, int by_key,
                     int* first, int* last, int* n_partial, int* n_empty);
 
-/* Bytes of device workspace attn_fwd needs (fp32 [B, H, T] key scales). */
+/* Bytes of device workspace attn_fwd needs: fp32 [B, H, T] key scales and a
+ * bf16 transposed copy of V, [B, H, D, T rounded up to 64]. */
 size_t attn_fwd_workspace_bytes(int B, int T, int H, int D);
 
 /*

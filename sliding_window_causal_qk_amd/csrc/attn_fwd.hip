@@ -22,13 +22,19 @@
 //  * S^T = K Q^T is formed on the 32x32x16 bf16 MFMA so that each lane owns one
 //    query column: its probabilities are already in the B-operand layout of the
 //    next product O^T = V^T P^T, and row sums are lane-local.
-//  * K and V tiles stay row-major in LDS (double-buffered; one barrier per
-//    tile); the V^T operand of the PV product comes from the gfx950
-//    transposing LDS read (ds_read_b64_tr_b16), two per MFMA.
+//  * The pre-pass also writes V transposed ([B, H, D, T]) with the keys of every
+//    16-key group permuted (tpos16) into the k order of the MFMA operands, so
+//    the V^T operand is one conflict-free 16-byte LDS read per MFMA instead of
+//    two transposing reads.
+//  * K tiles (padded rows) and V^T tiles (xor-swizzled 16-byte chunks) are
+//    copied global -> LDS by direct-to-LDS buffer loads into three rotating
+//    buffers, one step ahead; one barrier per 32-key step.
 //  * Loads go through buffer descriptors rebased per tile: rows past T read as
 //    zero, so ragged tails need no branches; stores past T are dropped.
-//  * Band-aware tile loop: a query tile visits only the key tiles that
-//    intersect its window; fully visible tiles skip the mask.
+//  * Band-aware tile loop: a query tile visits only the key blocks that
+//    intersect its window; fully visible blocks skip the mask.
+#include <type_traits>
+
 #include "common.h"
 #include "band.h"
 #include "kernels.h"
@@ -36,64 +42,114 @@
 
 namespace swattn {
 
-// ------------------------------------------------------------ kscale pre-pass
-// kscale[b, h, t] = log2(e) / sqrt(D) * r(k[b, t, h, :]).  Rows of K are
-// contiguous in [B, T, H, D]; D / 8 lanes share one row (16 bytes each).
+// ------------------------------------------------------------ forward pre-pass
+// One workgroup per (batch, head, block of 64 keys):
+//   kscale[b, h, t] = log2(e) / sqrt(D) * r(k[b, t, h, :])
+//   vt[b, h, d, tpos(t)] = v[b, t, h, d]   (V transposed; inside every group of
+//       16 keys the columns are permuted by tpos16, so that the 8 keys one lane
+//       feeds to an MFMA k-step are one contiguous 16-byte chunk)
+// Columns of vt past T are written as zero.
 template <int D>
-__global__ __launch_bounds__(256) void k_scale_kernel(const uint16_t* __restrict__ k,
-                                                      float* __restrict__ kscale, int nrows,
-                                                      int T, int H, float eps) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const int tid = blockIdx.x * 256 + threadIdx.x;
-  const int row = tid / LPR;
-  const int part = tid % LPR;
+__global__ __launch_bounds__(256) void fwd_prep_kernel(const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v,
+                                                       float* __restrict__ kscale,
+                                                       uint16_t* __restrict__ vt, int T, int H,
+                                                       int LT, float eps) {
+  constexpr int KB = 64;                 // keys per workgroup
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int TPR = 256 / KB;          // threads per key row (4)
+  constexpr int CPT = CH / TPR;          // chunks per thread
+  constexpr int LP = D + 2;              // LDS pitch (bf16) of the V block: column reads hit distinct banks
+  __shared__ uint32_t vs[KB * LP / 2];
+
+  const int nkb = LT / KB;
+  const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  const int b = bh / H, h = bh % H;
+  const int t0 = kb * KB;
+  const int tid = threadIdx.x;
+  const int rs = H * D;
+  const long long slice_bytes = (long long)(T - 1) * rs * 2 + 2 * D;
+  const size_t sbase = ((size_t)b * T * H + h) * D;
+  const rsrc_t rk = make_rsrc(k + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
+  const rsrc_t rv = make_rsrc(v + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
+
+  // rows: thread -> key t0 + tid / TPR, chunks (tid % TPR) * CPT ...
+  const int r = tid / TPR, part = tid % TPR;
   float ss = 0.f;
-  if (row < nrows) {
-    u32x4 v = ld16(k + (size_t)row * D + part * 8);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = part * CPT + i;
+    const u32x4 kk = bload16(rk, (r * rs + 8 * ch) * 2);
+    const u32x4 vv = bload16(rv, (r * rs + 8 * ch) * 2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float a = bf_lo(v[e]), b = bf_hi(v[e]);
-      ss += a * a + b * b;
+      const float a = bf_lo(kk[e]), bb = bf_hi(kk[e]);
+      ss += a * a + bb * bb;
+      vs[(r * LP + 8 * ch) / 2 + e] = vv[e];
     }
   }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
-  if (row < nrows && part == 0) {
-    const int h = row % H;
-    const int bt = row / H;
-    const int t = bt % T;
-    const int b = bt / T;
-    float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-    kscale[((size_t)b * H + h) * T + t] = r * (kLog2e / sqrtf((float)D));
+  for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
+  if (part == 0 && t0 + r < T) {
+    const float rr = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+    kscale[(size_t)bh * T + t0 + r] = rr * (kLog2e / sqrtf((float)D));
+  }
+  __syncthreads();
+
+  // columns: thread -> (d, 8-key chunk); consecutive threads write consecutive
+  // 16-byte chunks of one row of vt
+  const uint16_t* vsh = reinterpret_cast<const uint16_t*>(vs);
+  uint16_t* vrow = vt + (size_t)bh * D * LT + t0;
+#pragma unroll
+  for (int p = 0; p < D * (KB / 8) / 256; ++p) {
+    const int idx = tid + 256 * p;
+    const int d = idx / (KB / 8), ch = idx % (KB / 8);
+    uint32_t w4[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      // position 8 ch + j holds key tpos16^-1 (tpos16 is an involution)
+      const int k0 = (8 * ch + j) & ~15, x0 = (8 * ch + j) & 15;
+      const uint32_t lo = vsh[(k0 + tpos16(x0)) * LP + d];
+      const uint32_t hi = vsh[(k0 + tpos16(x0 + 1)) * LP + d];
+      w4[j / 2] = lo | (hi << 16);
+    }
+    st16(vrow + (size_t)d * LT + 8 * ch, u32x4{w4[0], w4[1], w4[2], w4[3]});
   }
 }
 
 // ------------------------------------------------------------ forward kernel
-// Workgroup: 4 waves; wave w owns query rows i0 + 32 w .. i0 + 32 w + 31.
-// Key tiles of BN = 64 rows, double-buffered in LDS; each wave forms S^T
-// (64 keys x 32 queries) in two 32x32 blocks, then O^T += V^T P^T.
+// Workgroup: 4 waves; wave w owns queries i0 + 32 w + c.  Key blocks of 32
+// (K rows, V^T columns and kscale) stream through the band in three LDS
+// buffers filled by direct-to-LDS loads one step ahead.  Per block i:
+//   A(i): S^T = K Q_hat^T                      (queries in lanes, keys in registers)
+//   B(i): P = exp2(S^T kscale - sqrt(D) log2 e), masked on edge blocks; row sums
+//   C(i): O^T += V^T P^T                       (V^T from the transposed copy)
+// The loop issues A(i+1), then C(i) interleaved with B(i+1).  Every MFMA
+// operand read from LDS is one conflict-free 16-byte read.
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;
-  static constexpr int BN = 64;
-  static constexpr int KS = D / 16;          // MFMA k-steps over D
-  static constexpr int NB = D / 32;          // 32-wide blocks of D in O^T
-  static constexpr int KP = D + 8;           // K row pitch (bf16): 16-byte reads of 8 rows hit 8 bank groups
-  static constexpr int VP = D + 16;          // V row pitch (bf16): transposed reads of 4 rows hit 4 bank groups
-  static constexpr int K_LDS = BN * KP;
-  static constexpr int V_LDS = BN * VP;
-  static constexpr int STAGE = (K_LDS + V_LDS) * 2 + BN * 4;   // bytes of one buffer
-  static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int CH = D / 8;           // 16-byte chunks per row
-  static constexpr int RPP = 256 / CH;       // rows staged per pass
-  static constexpr int PASSES = BN / RPP;
+  static constexpr int BM = 128;   // queries per workgroup (32 per wave)
+  static constexpr int BN = 32;    // keys per step
+  static constexpr int NBUF = 3;
+  static constexpr int KS = D / 16;
+  static constexpr int NB = D / 32;
+  static constexpr int PK = D + 8;                     // K row pitch (bf16): 16-byte reads conflict-free
+  using KTile = DmaTileV<BN * PK / 8>;
+  using VTile = DmaTileV<D * BN / 8>;                  // D rows of 64 bytes, xor-swizzled chunks
+  static constexpr int V_B = KTile::BYTES;
+  static constexpr int ST_B = V_B + VTile::BYTES;      // kscale (128 bytes used of 256)
+  static constexpr int STAGE = ST_B + 256;
+  static constexpr int LDS_BYTES = NBUF * STAGE;
 };
+
+// Chunk slot of logical chunk ch (0..3) in row r of a transposed 32-column tile.
+__device__ __forceinline__ int vt_slot(int r, int ch) { return ch ^ ((r >> 2) & 3); }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ kscale,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int W, float eps) {
+    const uint16_t* __restrict__ vt, const float* __restrict__ kscale,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int LT, int W, float eps) {
   using C = FwdCfg<D>;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -107,27 +163,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int tid = threadIdx.x;
   const int w = uniform(tid >> 6);
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const int rs = H * D;                                   // row stride (elements) along T
-  const long long rsb = 2LL * rs;                         // ... in bytes
+  const int rs = H * D;
+  const long long rsb = 2LL * rs;
   const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
-  const size_t sbase = ((size_t)b * T * H + h) * D;       // element offset of row 0 of the slice
-  const uint16_t* qs = q + sbase;
-  const uint16_t* ksl = k + sbase;
-  const uint16_t* vsl = v + sbase;
+  const size_t sbase = ((size_t)b * T * H + h) * D;
 
   // ---- query fragment: normalised q row (i0 + 32 w + c), B operand of S^T = K Q^T
   const int qw0 = i0 + 32 * w;
   const int qi = qw0 + c;
   u32x4 qf[C::KS];
   {
-    const rsrc_t rq = make_rsrc(qs + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+    const rsrc_t rq = make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       qf[ks] = bload16(rq, (c * rs + 16 * ks + 8 * g) * 2);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float a = bf_lo(qf[ks][e]), bb = bf_hi(qf[ks][e]);
+        const float a = bf_lo(qf[ks][e]), bb = bf_hi(qf[ks][e]);
         ss += a * a + bb * bb;
       }
     }
@@ -139,119 +192,141 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int e = 0; e < 4; ++e) qf[ks][e] = pack_bf16(bf_lo(qf[ks][e]) * r, bf_hi(qf[ks][e]) * r);
   }
 
-  f32x16 acc_o[C::NB];
+  f32x16 acc[C::NB];
 #pragma unroll
-  for (int n = 0; n < C::NB; ++n) acc_o[n] = f32x16{};
+  for (int n = 0; n < C::NB; ++n) acc[n] = f32x16{};
   float lsum = 0.f;
   const float shift = sqrtf((float)D) * kLog2e;  // fixed softmax shift, log2 units
 
   int kv_lo, kv_hi;
   kv_range(i0, i0 + C::BM - 1, T, W, &kv_lo, &kv_hi);
-  const int jt0 = kv_lo / C::BN, jt1 = kv_hi / C::BN;
+  const int jb0 = kv_lo / C::BN;
+  const int nsteps = kv_hi / C::BN - jb0 + 1;
 
-  // staging: thread -> rows tid / CH + RPP p, 16-byte chunk tid % CH (K and V alike)
-  const int srow = tid / C::CH, sch = tid % C::CH;
-  u32x4 kreg[C::PASSES], vreg[C::PASSES];
-  float ksreg = 0.f;
+  // ---- direct-to-LDS staging of one key step
+  typename C::KTile ktile;
+  ktile.init(w, lane, [&](int qc) {
+    const int r = qc / (C::PK / 8), ch = qc % (C::PK / 8);
+    return (r < C::BN && ch < D / 8) ? (r * rs + 8 * ch) * 2 : -1;
+  });
+  typename C::VTile vtile;
+  vtile.init(w, lane, [&](int qc) {
+    const int r = qc >> 2, s = qc & 3;
+    return (r * LT + 8 * vt_slot(r, s)) * 2;
+  });
   const rsrc_t rks = make_rsrc(kscale + (size_t)bh * T, 4LL * T);
-
-  auto load_tile = [&](int jt) {
-    const int j0 = jt * C::BN;
-    const rsrc_t rk = make_rsrc(ksl + (size_t)j0 * rs, slice_bytes - j0 * rsb);
-    const rsrc_t rv = make_rsrc(vsl + (size_t)j0 * rs, slice_bytes - j0 * rsb);
-#pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      const int off = ((srow + C::RPP * p) * rs + 8 * sch) * 2;
-      kreg[p] = bload16(rk, off);
-      vreg[p] = bload16(rv, off);
-    }
-    if (tid < C::BN) ksreg = bload4f(rks, (j0 + tid) * 4);
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + buf * C::STAGE);
-    uint16_t* Vs = Ks + C::K_LDS;
-    float* KSs = reinterpret_cast<float*>(Vs + C::V_LDS);
-#pragma unroll
-    for (int p = 0; p < C::PASSES; ++p) {
-      st16(Ks + (srow + C::RPP * p) * C::KP + 8 * sch, kreg[p]);
-      st16(Vs + (srow + C::RPP * p) * C::VP + 8 * sch, vreg[p]);
-    }
-    if (tid < C::BN) KSs[tid] = ksreg;
+  const uint16_t* k_s = k + sbase;
+  const uint16_t* vt_s = vt + (size_t)bh * D * LT;
+  const long long vt_bytes = 2LL * D * LT;
+  auto issue_step = [&](int step, int base) {
+    const int j0 = (jb0 + step) * C::BN;
+    ktile.issue(make_rsrc(k_s + (size_t)j0 * rs, slice_bytes - j0 * rsb), smem, base, w);
+    vtile.issue(make_rsrc(vt_s + j0, vt_bytes - 2LL * j0), smem, base + C::V_B, w);
+    if (w == 0) dma_row4(rks, smem, base + C::ST_B, (j0 + lane) * 4);   // wave 0 loads kscale
   };
 
-  // per-lane LDS offsets of the MFMA operands
-  const int k_off = c * C::KP + 8 * g;                                  // K rows, 16-byte reads
-  const int li = lane & 15;
-  const int v_off = (4 * g + (li >> 2)) * C::VP + 16 * ((lane >> 4) & 1) + 4 * (li & 3);  // V^T via tr reads
+  const int a_off = 2 * (c * C::PK + 8 * g);                 // K rows: row c, chunk 2 ks + g
+  const int v_off0 = 64 * c + 16 * vt_slot(c, g);            // V^T rows 32 n + c, chunk g (k-step 0)
+  const int v_off1 = 64 * c + 16 * vt_slot(c, 2 + g);        // ... chunk 2 + g (k-step 1)
+  const int k_off = C::ST_B + 16 * g;                        // kscale of the lane's key quads
 
-  if (jt0 <= jt1) {
-    load_tile(jt0);
-    store_tile(0);
-  }
+  f32x16 s_acc;
+  u32x4 pf[2];
+
+  auto stage_a = [&](int base) {
+    const int va = base + a_off;
+    s_acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) s_acc = mfma32(lds16(smem, va + 32 * ks), qf[ks], s_acc);
+  };
+  // lane (g, c), register r: key j0 + 8 (r/4) + 4 g + r%4, query qi
+  auto stage_b = [&](int base, int step, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int vk = base + k_off;
+    const int t0 = (jb0 + step) * C::BN + 4 * g + W - qi;  // key kv visible iff 0 <= kv - (qi - W) <= W
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 k4 = lds16f(smem, vk + 32 * q4);
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * k4[e] - shift);
+      if (MASKED) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)W) ? p[e] : 0.f;
+      }
+      const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
+      const int st = q4 >> 1, el = 2 * (q4 & 1);
+      pf[st][el] = p01;
+      pf[st][el + 1] = p23;
+      // the row sum adds the bf16-rounded probabilities the PV product uses,
+      // so the output weights sum to one (W = 0 gives o = v exactly)
+      lsum = sum_bf16x2(p01, lsum);
+      lsum = sum_bf16x2(p23, lsum);
+    }
+  };
+  // O^T[d, q] += V^T[d, kv] P^T[kv, q]; element j of k-step s2 is key
+  // 16 s2 + 4 g + (j % 4) + 8 (j / 4), the order of the tpos16 columns
+  auto stage_c = [&](int base) {
+    const int vb = base + C::V_B;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int n = 0; n < C::NB; ++n)
+        acc[n] = mfma32(lds16(smem, vb + (s2 ? v_off1 : v_off0) + 2048 * n), pf[s2], acc[n]);
+  };
+
+  // ---- prologue: steps 0, 1 in LDS, step 2 in flight; A(0), B(0)
+  int b0 = 0, b1 = C::STAGE, b2 = 2 * C::STAGE;
+  if (nsteps > 0) issue_step(0, b0);
+  if (nsteps > 1) issue_step(1, b1);
+  wait_vmcnt<0>();
   __syncthreads();
-  for (int jt = jt0; jt <= jt1; ++jt) {
-    const int buf = (jt - jt0) & 1;
-    if (jt < jt1) load_tile(jt + 1);
-
-    const int j0 = jt * C::BN;
-    const int cls = uniform(tile_class(qw0, qw0 + 31, j0, j0 + C::BN - 1, T, W));
-    if (cls != TILE_EMPTY) {
-      const uint16_t* Ks = reinterpret_cast<const uint16_t*>(smem + buf * C::STAGE);
-      const uint16_t* Vs = Ks + C::K_LDS;
-      const float* KSs = reinterpret_cast<const float*>(Vs + C::V_LDS);
-
-      // S^T blocks: keys j0 + 32 mb + (8 (r/4) + 4 g + r%4), query qi
-      f32x16 st[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        st[mb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          st[mb] = mfma32(ld16(Ks + k_off + 32 * mb * C::KP + 16 * ks), qf[ks], st[mb]);
-      }
-
-      // probabilities (log2 domain, fixed shift), packed to bf16 in MFMA k order
-      u32x4 pf[4];
-      const int t0 = j0 + 4 * g + W - qi;   // key kv visible iff 0 <= kv - (qi - W) <= W
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int jl = 32 * mb + 8 * q4 + 4 * g;
-          const f32x4 ks4 = *reinterpret_cast<const f32x4*>(KSs + jl);
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(st[mb][4 * q4 + e] * ks4[e] - shift);
-          if (cls == TILE_PARTIAL) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              p[e] = ((unsigned)(t0 + 32 * mb + 8 * q4 + e) <= (unsigned)W) ? p[e] : 0.f;
-          }
-          const uint32_t p01 = pack_bf16(p[0], p[1]), p23 = pack_bf16(p[2], p[3]);
-          pf[2 * mb + (q4 >> 1)][2 * (q4 & 1) + 0] = p01;
-          pf[2 * mb + (q4 >> 1)][2 * (q4 & 1) + 1] = p23;
-          // the row sum adds the bf16-rounded probabilities the PV product uses,
-          // so the output weights sum to one (W = 0 gives o = v exactly)
-          lsum = sum_bf16x2(p01, lsum);
-          lsum = sum_bf16x2(p23, lsum);
-        }
-      }
-
-      // O^T[d, q] += V^T[d, keys] P^T[keys, q]; key k-order matches pf:
-      // element j of k-step s is key 16 s + 4 g + (j % 4) + 8 (j / 4)
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-#pragma unroll
-        for (int n = 0; n < C::NB; ++n) {
-          const u32x2 lo = lds_tr4(Vs + v_off + 16 * s2 * C::VP + 32 * n);
-          const u32x2 hi = lds_tr4(Vs + v_off + (16 * s2 + 8) * C::VP + 32 * n);
-          acc_o[n] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[s2], acc_o[n]);
-        }
-      }
-    }
-    if (jt < jt1) store_tile(buf ^ 1);
-    __syncthreads();
+  if (nsteps > 2) issue_step(2, b2);
+  const std::integral_constant<bool, true> masked{};
+  const std::integral_constant<bool, false> unmasked{};
+  if (nsteps > 0) {
+    stage_a(b0);
+    stage_b(b0, 0, masked);
   }
+
+  auto step_body = [&](int it, auto masked_c) {
+    stage_a(b1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < C::KS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_c(b0);
+    stage_b(b1, it + 1, masked_c);
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(lsum));
+    wait_vmcnt<0>();            // step it + 2 landed
+    __syncthreads();
+    if (it + 3 < nsteps) issue_step(it + 3, b0);   // buffer of step it, consumed
+    const int t = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = t;
+  };
+
+  // steps visible in full to every query of the workgroup: keys kv0 .. kv0 + 31
+  // with kv0 + 31 <= i0 and (i0 + BM - 1) - kv0 <= W (and all inside T)
+  int full_lo = nsteps, full_hi = -1;
+  if (nsteps > 0 && i0 + C::BM - 1 < T) {
+    const int lo_kv = i0 + C::BM - 1 - W;                  // first key visible to every query
+    full_lo = imax(0, (lo_kv + C::BN - 1) / C::BN - jb0);
+    full_hi = (i0 - (C::BN - 1)) >= 0 ? (i0 - (C::BN - 1)) / C::BN - jb0 : -1;
+    full_hi = imin(full_hi, nsteps - 1);
+  }
+  const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // body it prepares B(it + 1)
+  const int nloop = nsteps - 1;
+  int it = 0;
+  for (; it < imin(u0, nloop); ++it) step_body(it, masked);
+  for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
+  for (; it < nloop; ++it) step_body(it, masked);
+  if (nsteps > 0) stage_c(b0);
 
   // ---- epilogue: O = O^T / l, lse = shift + ln l  (stores past T are dropped)
   lsum += __shfl_xor(lsum, 32);
@@ -262,8 +337,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d = 32 * n + 8 * q4 + 4 * g;
-      const u32x2 val = {pack_bf16(acc_o[n][4 * q4 + 0] * inv, acc_o[n][4 * q4 + 1] * inv),
-                         pack_bf16(acc_o[n][4 * q4 + 2] * inv, acc_o[n][4 * q4 + 3] * inv)};
+      const u32x2 val = {pack_bf16(acc[n][4 * q4 + 0] * inv, acc[n][4 * q4 + 1] * inv),
+                         pack_bf16(acc[n][4 * q4 + 2] * inv, acc[n][4 * q4 + 3] * inv)};
       bstore8(val, ro, (c * rs + d) * 2);
     }
   if (g == 0) {
@@ -275,12 +350,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 template <int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D>;
-  const int nrows = a.B * a.T * a.H;
-  const int lpr = D / 8;
-  const int nblk_s = (int)(((long long)nrows * lpr + 255) / 256);
+  const int nkb = a.LT / 64;
   ProfToken t0 = prof_begin(K_SCALE, stream);
-  hipLaunchKernelGGL(k_scale_kernel<D>, dim3(nblk_s), dim3(256), 0, stream,
-                     (const uint16_t*)a.k, a.kscale, nrows, a.T, a.H, a.eps);
+  hipLaunchKernelGGL(fwd_prep_kernel<D>, dim3(nkb * a.B * a.H), dim3(256), 0, stream,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.kscale, (uint16_t*)a.vt, a.T,
+                     a.H, a.LT, a.eps);
   prof_end(t0);
   const int nqt = (a.T + C::BM - 1) / C::BM;
   const int nblk = nqt * a.B * a.H;
@@ -292,8 +366,8 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   if (attr != hipSuccess) return attr;
   ProfToken t1 = prof_begin(K_FWD, stream);
   hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nblk), dim3(256), C::LDS_BYTES, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const float*)a.kscale, (uint16_t*)a.o, a.lse, a.T, a.H, W, a.eps);
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.vt,
+                     (const float*)a.kscale, (uint16_t*)a.o, a.lse, a.T, a.H, a.LT, W, a.eps);
   prof_end(t1);
   return hipGetLastError();
 }

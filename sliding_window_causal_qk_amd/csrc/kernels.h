@@ -14,6 +14,8 @@ struct FwdArgs {
   void* o;
   float* lse;
   float* kscale;  // workspace: [B, H, T]
+  void* vt;       // workspace: bf16 [B, H, D, LT], V transposed, keys permuted (tpos16)
+  int LT;         // row length of vt: T rounded up to a multiple of 64
   int B, T, H, D;
   int window;
   float eps;

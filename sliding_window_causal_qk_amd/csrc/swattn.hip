@@ -39,6 +39,10 @@ int check_common(int B, int T, int H, int D, int window, int causal, float eps, 
 
 size_t stats_bytes(int B, int T, int H) { return round_up((size_t)B * H * T * sizeof(float)); }
 
+// Row length of the transposed V copy of the forward: T rounded up to 64.
+int vt_cols(int T) { return (T + 63) / 64 * 64; }
+size_t vt_bytes(int B, int T, int H, int D) { return round_up((size_t)B * H * D * vt_cols(T) * 2); }
+
 }  // namespace
 
 extern "C" {
@@ -109,7 +113,7 @@ int attn_band_tiles(int T, int window, int rows, int cols, int by_key, int* firs
 
 size_t attn_fwd_workspace_bytes(int B, int T, int H, int D) {
   if (B < 0 || T < 0 || H < 0 || D < 1) return 0;
-  return stats_bytes(B, T, H);
+  return stats_bytes(B, T, H) + vt_bytes(B, T, H, D);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int T, int H, int D) {
@@ -135,6 +139,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, v
   swattn::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.kscale = static_cast<float*>(workspace);
+  a.vt = static_cast<char*>(workspace) + stats_bytes(B, T, H);
+  a.LT = vt_cols(T);
   a.B = B; a.T = T; a.H = H; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_fwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

@@ -118,9 +118,13 @@ __device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int off, int r
 }
 
 // ------------------------------------------------------------------ dK / dV
-// Workgroup: 4 waves; wave w owns keys j0 + 32 w + c.  Query blocks of 32
-// rows (q_hat, dO and their lse, Delta) stream through the band in four LDS
-// buffers filled by direct-to-LDS loads issued three steps ahead.  Per block i:
+// Persistent: one workgroup per CU walks a list of key tiles of 128 keys.  In
+// a tile, wave w owns keys j0 + 32 w + c; query blocks of 32 rows (q_hat, dO
+// and their lse, Delta) stream through three LDS buffers filled by
+// direct-to-LDS loads one step ahead, and the stream runs on across tile
+// boundaries, so a tile's first blocks are in LDS when its predecessor ends.
+// The next tile's K and V rows are prefetched into LDS during the current
+// tile.  Per block i:
 //   A(i): S = Q_hat K^T and dP = dO V^T    (keys in lanes, queries in registers)
 //   B(i): P = exp2(S kscale - lse log2 e), dS = P (dP - Delta)      (VALU)
 //   C(i): dV^T += dO^T P, dK_hat^T += Q_hat^T dS  (transposed operands read
@@ -128,20 +132,32 @@ __device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int off, int r
 // The loop issues A(i+1) and C(i) back to back, then B(i+1): the softmax of
 // the next block runs on the VALU while the matrix cores still work through
 // C(i), and LDS reads for both products are in flight together.
+//
+// Tiles are split into 8 contiguous ranges, one per XCD (workgroup b runs on
+// XCD b % 8), so the tiles of one (batch, head) share that XCD's L2; inside a
+// range, round i gives workgroup s the tile i G8 + (s + 7 i) mod G8, which
+// rotates the light tiles of the causal tail through all workgroups.
 template <int D>
 struct DkdvCfg {
-  static constexpr int BNK = 128;       // keys per workgroup (32 per wave)
+  static constexpr int BNK = 128;       // keys per tile (32 per wave)
   static constexpr int BMQ = 32;        // queries per step
-  static constexpr int NBUF = 4;
+  static constexpr int NBUF = 3;
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int P = D + 24;      // row pitch (bf16): odd multiple of 16 bytes
-  using Tile = DmaTile<D, BMQ, P, 0>;
+  static constexpr int P = D + 24;      // q_hat / dO row pitch (bf16): odd multiple of 16 bytes
+  static constexpr int PK = D + 8;      // K / V row pitch in the prefetch region
+  using Tile = DmaTileV<BMQ * P / 8>;
+  using KVTile = DmaTileV<BNK * PK / 8>;
   static constexpr int DO_B = Tile::BYTES;          // dO tile after the q_hat tile
-  static constexpr int ST_B = 2 * Tile::BYTES;      // lse2 (256 B), Delta (256 B), 2 spare
+  static constexpr int ST_B = 2 * Tile::BYTES;      // 4 x 256 B: spare, spare, lse2, Delta
   static constexpr int STAGE = ST_B + 1024;
-  static constexpr int LDS_BYTES = NBUF * STAGE;
-  static constexpr int NPS = 2 * Tile::NIW + 1;     // direct loads per wave per step
+  static constexpr int KV_B = NBUF * STAGE;         // K rows, then V rows of the next tile
+  static constexpr int OP = D + 8;                  // output staging row pitch (bf16)
+  static constexpr int OUT_SLOT = 32 * OP * 2;      // one wave's 32 x D bf16 block
+  static constexpr int XO_B = KV_B + 2 * KVTile::BYTES;   // staging slots of waves 2 and 3
+  static constexpr int LDS_BYTES = XO_B + 2 * OUT_SLOT;
+  static constexpr int NSTORE = 2 * (32 * D / 8 / 64);    // epilogue stores per lane (dK and dV)
+  static_assert(2 * OUT_SLOT <= STAGE, "waves 0 and 1 stage their outputs in a freed step buffer");
 };
 
 template <int D>
@@ -150,16 +166,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const float* __restrict__ kscale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    int T, int H, int W) {
+    int T, int H, int W, int nkt, int ntiles) {
   using C = DkdvCfg<D>;
   extern __shared__ __align__(16) unsigned char smem[];
-
-  const int nkt = (T + C::BNK - 1) / C::BNK;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / nkt;
-  const int kt = lid % nkt;  // causal: the first key blocks see the most queries
-  const int b = bh / H, h = bh % H;
-  const int j0 = kt * C::BNK;
 
   const int tid = threadIdx.x;
   const int w = uniform(tid >> 6);
@@ -167,242 +176,344 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int rs = H * D;
   const long long rsb = 2LL * rs;
   const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
-  const size_t sbase = ((size_t)b * T * H + h) * D;
-  const size_t sb = (size_t)bh * T;
 
-  // ---- owned key / value rows (kv = kw0 + c), B operands of S and dP
-  const int kw0 = j0 + 32 * w;
-  const int kj = kw0 + c;
-  u32x4 kf[C::KS], vf[C::KS];
-  {
-    const rsrc_t rk = make_rsrc(k + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
-    const rsrc_t rv = make_rsrc(v + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      kf[ks] = bload16(rk, (c * rs + 16 * ks + 8 * g) * 2);
-      vf[ks] = bload16(rv, (c * rs + 16 * ks + 8 * g) * 2);
-    }
+  // ---- tile list of this workgroup
+  int xr = 0, ws = blockIdx.x, G8 = gridDim.x, N8 = ntiles;
+  if ((ntiles & 7) == 0 && (gridDim.x & 7) == 0) {
+    xr = blockIdx.x & 7;
+    ws = blockIdx.x >> 3;
+    G8 = gridDim.x >> 3;
+    N8 = ntiles >> 3;
   }
-  const rsrc_t rstat_k = make_rsrc(kscale + sb, 4LL * T);
-  const float ksc = bload4f(rstat_k, kj * 4);
-
-  f32x16 acc_dv[C::NB], acc_dk[C::NB];
-#pragma unroll
-  for (int n = 0; n < C::NB; ++n) { acc_dv[n] = f32x16{}; acc_dk[n] = f32x16{}; }
-
-  int q_lo, q_hi;
-  const bool any = q_range(j0, j0 + C::BNK - 1, T, W, &q_lo, &q_hi);
-  const int qb0 = any ? q_lo / C::BMQ : 0;
-  const int nsteps = any ? q_hi / C::BMQ - qb0 + 1 : 0;
-
-  // ---- direct-to-LDS staging of one step into the buffer at byte offset `base`
-  typename C::Tile tile;
-  tile.init(w, lane, rs);
-  // stats: wave 0 loads lse2, wave 1 Delta, waves 2 and 3 a spare (out of range)
-  const rsrc_t rstat = make_rsrc(w == 0 ? lse2 + sb : delta + sb, w < 2 ? 4LL * T : 0);
-  const uint16_t* qh_s = qhat + sbase;
-  const uint16_t* do_s = dout + sbase;
-  auto issue_step = [&](int step, int base) {
-    const int r0 = (qb0 + step) * C::BMQ;
-    tile.issue(make_rsrc(qh_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base, w);
-    tile.issue(make_rsrc(do_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base + C::DO_B, w);
-    dma_row4(rstat, smem, base + C::ST_B + 256 * w, (r0 + lane) * 4);
+  auto tile_at = [&](int i) {   // i-th tile of this workgroup, or -1
+    const int r = i * G8 + (ws + 7 * i) % G8;
+    return (i * G8 < N8 && r < N8) ? xr * N8 + r : -1;
   };
+  struct TileGeo {
+    int bh, j0, qb0, nsteps;
+  };
+  auto geo = [&](int t) {
+    TileGeo tg;
+    tg.bh = t / nkt;
+    tg.j0 = (t % nkt) * C::BNK;
+    int q_lo, q_hi;
+    const bool any = q_range(tg.j0, tg.j0 + C::BNK - 1, T, W, &q_lo, &q_hi);
+    tg.qb0 = any ? q_lo / C::BMQ : 0;
+    tg.nsteps = any ? q_hi / C::BMQ - tg.qb0 + 1 : 0;
+    return tg;
+  };
+  auto slice_base = [&](int bh) { return ((size_t)(bh / H) * T * H + (bh % H)) * D; };
+
+  // ---- direct-to-LDS staging
+  typename C::Tile tile;
+  tile.init(w, lane, [&](int qc) {
+    const int r = qc / (C::P / 8), ch = qc % (C::P / 8);
+    return (r < C::BMQ && ch < D / 8) ? (r * rs + 8 * ch) * 2 : -1;
+  });
+  typename C::KVTile kvtile;
+  kvtile.init(w, lane, [&](int qc) {
+    const int r = qc / (C::PK / 8), ch = qc % (C::PK / 8);
+    return (ch < D / 8) ? (r * rs + 8 * ch) * 2 : -1;
+  });
+  // The stream of query blocks runs across tiles.  A plan holds the source
+  // of the next block (computed with scalar control flow outside the
+  // scheduled regions); issuing it is branch-free, so the loads interleave
+  // with the MFMAs.  Past the end of the stream a plan has no bytes in range
+  // and its loads write zeros into a free buffer.  Waves 2 and 3 (fewer tile
+  // loads) fetch lse2 and Delta; waves 0 and 1 load into spare slots.
+  struct DmaPlan {
+    const uint16_t* qh;
+    const uint16_t* dO;
+    const float* st;
+    long long nbytes;
+    int nst;
+    int r0;
+  };
+  int dt = 0, ds = 0;                    // the next block: step ds of the dt-th tile
+  TileGeo dgeo;
+  int tcur = tile_at(0);
+  if (tcur >= 0) dgeo = geo(tcur);
+  auto plan_next = [&]() {
+    while (tcur >= 0 && ds >= dgeo.nsteps) {
+      ++dt;
+      ds = 0;
+      tcur = tile_at(dt);
+      if (tcur >= 0) dgeo = geo(tcur);
+    }
+    DmaPlan pl;
+    const bool ok = tcur >= 0;
+    const int bh = ok ? dgeo.bh : 0;
+    const size_t sbase = slice_base(bh);
+    pl.r0 = ok ? (dgeo.qb0 + ds) * C::BMQ : 0;
+    pl.qh = qhat + sbase + (size_t)pl.r0 * rs;
+    pl.dO = dout + sbase + (size_t)pl.r0 * rs;
+    pl.nbytes = ok ? slice_bytes - pl.r0 * rsb : 0;
+    pl.st = (w == 2 ? lse2 : delta) + (size_t)bh * T;
+    pl.nst = (ok && w >= 2) ? 4 * T : 0;
+    if (ok) ++ds;
+    return pl;
+  };
+  auto issue_plan = [&](const DmaPlan& pl, int base) {
+    tile.issue(make_rsrc(pl.qh, pl.nbytes), smem, base, w);
+    tile.issue(make_rsrc(pl.dO, pl.nbytes), smem, base + C::DO_B, w);
+    dma_row4(make_rsrc(pl.st, pl.nst), smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
+  };
+  auto issue_kv = [&](const TileGeo& tg) {
+    const size_t sbase = slice_base(tg.bh);
+    kvtile.issue(make_rsrc(k + sbase + (size_t)tg.j0 * rs, slice_bytes - tg.j0 * rsb), smem, C::KV_B, w);
+    kvtile.issue(make_rsrc(v + sbase + (size_t)tg.j0 * rs, slice_bytes - tg.j0 * rsb), smem,
+                 C::KV_B + C::KVTile::BYTES, w);
+  };
+
   // per-lane byte offsets inside a stage buffer
   const int a_off = 2 * (c * C::P + 8 * g);          // row-major A operands (16-byte reads)
   const int t_off = 2 * tr_off(lane, C::P);          // transposed A operands
-  const int l_off = C::ST_B + 16 * g;                // lse2 / Delta of the lane's query quads
-  // visibility on partial blocks: 0 <= q - kj <= lim, lim = min(W, T - 1 - kj)
-  const int lim = imin(W, T - 1 - kj);
+  const int l_off = C::ST_B + 512 + 16 * g;          // lse2 / Delta of the lane's query quads
+  const int kv_off = C::KV_B + 2 * ((32 * w + c) * C::PK + 8 * g);   // owned K / V row
 
+  // prologue of the stream: K / V rows of the first tile, blocks 0 and 1.
+  // Invariant at a step's start: b0 holds block it, b1 block it + 1, b2 is free.
+  int b0 = 2 * C::STAGE, b1 = 0, b2 = C::STAGE;
+  if (tcur >= 0) issue_kv(dgeo);
+  issue_plan(plan_next(), b1);
+  issue_plan(plan_next(), b2);
+  DmaPlan pnext = plan_next();
+
+  u32x4 kf[C::KS], vf[C::KS];
+  f32x16 acc_dv[C::NB], acc_dk[C::NB];
   f32x16 s_acc, dp_acc;
   u32x4 pf[2], dsf[2];
-
-  // A: scores and dP of one step
-  auto stage_a = [&](int base) {
-    const int va = base + a_off;
-    s_acc = f32x16{};
-    dp_acc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      s_acc = mfma32(lds16(smem, va + 32 * ks), kf[ks], s_acc);
-      dp_acc = mfma32(lds16(smem, va + C::DO_B + 32 * ks), vf[ks], dp_acc);
-    }
-  };
-  // B: probabilities and dS of one step (lane (g, c), register r: query
-  // q0 + 8 (r/4) + 4 g + r%4, key kj).  MASKED is a compile-time flag so each
-  // loop version is one straight-line block the scheduler can interleave.
-  auto stage_b = [&](int base, int step, auto masked_c) {
-    constexpr bool MASKED = decltype(masked_c)::value;
-    const int vl = base + l_off;
-    const int t0 = (qb0 + step) * C::BMQ + 4 * g - kj;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 l4 = lds16f(smem, vl + 32 * q4);
-      const f32x4 d4 = lds16f(smem, vl + 256 + 32 * q4);
-      float p[4], ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * ksc - l4[e]);
-      if (MASKED) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ds[e] = p[e] * (dp_acc[4 * q4 + e] - d4[e]);
-      const int st = q4 >> 1, el = 2 * (q4 & 1);
-      pf[st][el] = pack_bf16(p[0], p[1]);
-      pf[st][el + 1] = pack_bf16(p[2], p[3]);
-      dsf[st][el] = pack_bf16(ds[0], ds[1]);
-      dsf[st][el + 1] = pack_bf16(ds[2], ds[3]);
-    }
-  };
-  // C: dV^T[d, kv] += dO^T[d, q] P[q, kv];  dK_hat^T[d, kv] += Q_hat^T[d, q] dS[q, kv]
-  // (element j of a k-step s2 is query 16 s2 + 4 g + (j % 4) + 8 (j / 4))
-  auto stage_c = [&](int base) {
-    const int vt = base + t_off;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int n = 0; n < C::NB; ++n) {
-        constexpr int R8 = 2 * 8 * C::P;
-        const int o = 2 * (16 * s2 * C::P + 32 * n);
-        const u32x2 a0 = lds_tr4b(smem, vt + C::DO_B + o), a1 = lds_tr4b(smem, vt + C::DO_B + o + R8);
-        const u32x2 b0 = lds_tr4b(smem, vt + o), b1 = lds_tr4b(smem, vt + o + R8);
-        acc_dv[n] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[s2], acc_dv[n]);
-        acc_dk[n] = mfma32(u32x4{b0[0], b0[1], b1[0], b1[1]}, dsf[s2], acc_dk[n]);
-      }
-    }
-  };
-  // C runs every step (empty steps carry zero P and dS), which keeps the
-  // accumulators in one register class across the loop
-  auto zero_pds = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) pf[i] = dsf[i] = u32x4{0, 0, 0, 0};
-  };
-
-  // ---- prologue: steps 0..3 issued; wait for 0 and 1; A(0), B(0).
-  // Buffers rotate: step i lives in buffer i % 4.
-  int b0 = 0, b1 = C::STAGE, b2 = 2 * C::STAGE, b3 = 3 * C::STAGE;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i < nsteps) issue_step(i, i * C::STAGE);
-  if (nsteps >= 4) wait_vmcnt<2 * C::NPS>();
-  else if (nsteps == 3) wait_vmcnt<C::NPS>();
-  else wait_vmcnt<0>();
-  __syncthreads();
   const std::integral_constant<bool, true> masked{};
   const std::integral_constant<bool, false> unmasked{};
-  if (nsteps > 0) {
+
+  for (int ti = 0;; ++ti) {
+    const int t = tile_at(ti);
+    if (t < 0) break;
+    const TileGeo tg = geo(t);
+    const int bh = tg.bh, j0 = tg.j0, qb0 = tg.qb0, nsteps = tg.nsteps;
+    const size_t sbase = slice_base(bh);
+    const int kw0 = j0 + 32 * w;
+    const int kj = kw0 + c;
+
+    // ---- tile prologue: steps 0 and 1 of this tile and its K / V rows have
+    // landed (they are older than the previous tile's dK / dV stores, which
+    // may stay in flight); the buffer of the previous tile's last step takes
+    // step 2
+    if (ti == 0) wait_vmcnt<0>();
+    else wait_vmcnt<C::NSTORE>();
+    __syncthreads();
+    const float ksc = bload4f(make_rsrc(kscale + (size_t)bh * T, 4LL * T), kj * 4);
+    // visibility on partial blocks: 0 <= q - kj <= lim, lim = min(W, T - 1 - kj)
+    const int lim = imin(W, T - 1 - kj);
+    {
+      const int t_ = b0;
+      b0 = b1;
+      b1 = b2;
+      b2 = t_;
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks] = lds16(smem, kv_off + 32 * ks);
+      vf[ks] = lds16(smem, kv_off + C::KVTile::BYTES + 32 * ks);
+    }
+#pragma unroll
+    for (int n = 0; n < C::NB; ++n) { acc_dv[n] = f32x16{}; acc_dk[n] = f32x16{}; }
+    const bool kv_pending = tile_at(ti + 1) >= 0;   // prefetch of the next tile's K / V rows
+
+    // A: scores and dP of one step
+    auto stage_a = [&](int base) {
+      const int va = base + a_off;
+      s_acc = f32x16{};
+      dp_acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        s_acc = mfma32(lds16(smem, va + 32 * ks), kf[ks], s_acc);
+        dp_acc = mfma32(lds16(smem, va + C::DO_B + 32 * ks), vf[ks], dp_acc);
+      }
+    };
+    // B: probabilities and dS of one step (lane (g, c), register r: query
+    // q0 + 8 (r/4) + 4 g + r%4, key kj).  MASKED is a compile-time flag so each
+    // loop version is one straight-line block the scheduler can interleave.
+    auto stage_b = [&](int base, int step, auto masked_c) {
+      constexpr bool MASKED = decltype(masked_c)::value;
+      const int vl = base + l_off;
+      const int tq = (qb0 + step) * C::BMQ + 4 * g - kj;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 l4 = lds16f(smem, vl + 32 * q4);
+        const f32x4 d4 = lds16f(smem, vl + 256 + 32 * q4);
+        float p[4], dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * ksc - l4[e]);
+        if (MASKED) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(tq + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsv[e] = p[e] * (dp_acc[4 * q4 + e] - d4[e]);
+        const int st = q4 >> 1, el = 2 * (q4 & 1);
+        pf[st][el] = pack_bf16(p[0], p[1]);
+        pf[st][el + 1] = pack_bf16(p[2], p[3]);
+        dsf[st][el] = pack_bf16(dsv[0], dsv[1]);
+        dsf[st][el + 1] = pack_bf16(dsv[2], dsv[3]);
+      }
+    };
+    // C: dV^T[d, kv] += dO^T[d, q] P[q, kv];  dK_hat^T[d, kv] += Q_hat^T[d, q] dS[q, kv]
+    // (element j of a k-step s2 is query 16 s2 + 4 g + (j % 4) + 8 (j / 4))
+    auto stage_c = [&](int base) {
+      const int vt = base + t_off;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int n = 0; n < C::NB; ++n) {
+          constexpr int R8 = 2 * 8 * C::P;
+          const int o = 2 * (16 * s2 * C::P + 32 * n);
+          const u32x2 a0 = lds_tr4b(smem, vt + C::DO_B + o), a1 = lds_tr4b(smem, vt + C::DO_B + o + R8);
+          const u32x2 bb0 = lds_tr4b(smem, vt + o), bb1 = lds_tr4b(smem, vt + o + R8);
+          acc_dv[n] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[s2], acc_dv[n]);
+          acc_dk[n] = mfma32(u32x4{bb0[0], bb0[1], bb1[0], bb1[1]}, dsf[s2], acc_dk[n]);
+        }
+      }
+    };
+
     stage_a(b0);
     stage_b(b0, 0, masked);
-  } else {
-    zero_pds();
-  }
 
-  // One pipelined step: A(it+1), C(it), B(it+1), then the hand-off of the
-  // buffers.  The instruction order inside a step is fixed with schedule
-  // groups: A(it+1)'s reads and MFMAs first, then C(it)'s MFMAs with their
-  // transposed reads, with B(it+1)'s VALU work slotted between.
-  // (valid for it + 1 < nsteps; the last step only runs C)
-  auto step_body = [&](int it, auto masked_c) {
-    // A: keep 8 LDS reads in flight ahead of the MFMAs (LDS latency is several
-    // MFMA issue slots)
-    stage_a(b1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // One pipelined step: A(it+1), C(it), B(it+1), then the hand-off of the
+    // buffers.  The instruction order inside a step is fixed with schedule
+    // groups: A(it+1)'s reads and MFMAs first, then C(it)'s MFMAs with their
+    // transposed reads, with B(it+1)'s VALU work slotted between.
+    auto step_body = [&](int it, auto masked_c) {
+      issue_plan(pnext, b2);      // block it + 2 into the free buffer, spread over A
+      stage_a(b1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * C::KS - 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 2 * C::KS - 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);   // A stays ahead of C and B
+      stage_c(b0);
+      stage_b(b1, it + 1, masked_c);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * C::NB - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      // keep B's results inside this step (the compiler would otherwise sink
+      // the softmax below the barrier, away from the MFMAs it should overlap)
+      asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
+      wait_vmcnt<0>();            // block it + 2 has landed
+      __syncthreads();
+      const int t_ = b0;
+      b0 = b1;
+      b1 = b2;
+      b2 = t_;
+      pnext = plan_next();
+    };
+
+    // Steps whose B needs the element mask sit at both ends of the band; the
+    // middle runs the unmasked body.  `full_lo .. full_hi` are the steps
+    // visible in full to every key of the tile: q0 >= j0 + BNK - 1 and
+    // q0 + BMQ - 1 <= j0 + W, q0 + BMQ <= T.
+    const int kv_last = imin(j0 + C::BNK - 1, T - 1);
+    int full_lo = 0, full_hi = -1;
+    if (nsteps > 0) {
+      const int qf0 = kv_last;                                  // first fully causal query
+      const int qf1 = imin(j0 + W, T) - (C::BMQ - 1);           // last start of a fully inside step
+      full_lo = imax(0, (qf0 + C::BMQ - 1) / C::BMQ - qb0);
+      full_hi = qf1 >= 0 ? qf1 / C::BMQ - qb0 : -1;
+      full_hi = imin(full_hi, nsteps - 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);   // A stays ahead of C and B
-    // C with B: transposed reads four MFMAs ahead, softmax VALU between MFMAs
+    // body of step `it` prepares B(it + 1): unmasked iff step it + 1 is full
+    const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // it in [u0, u1] -> unmasked
+    const int nloop = nsteps - 1;   // steps with a successor
+    int it = 0;
+    if (nloop > 0) step_body(it++, masked);
+    if (kv_pending) {   // after a barrier that follows every wave's K / V reads
+      if (nloop == 0) __syncthreads();
+      issue_kv(geo(tile_at(ti + 1)));
+    }
+    for (; it < imin(u0, nloop); ++it) step_body(it, masked);
+    for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
+    for (; it < nloop; ++it) step_body(it, masked);
+    issue_plan(pnext, b2);          // the next tile's block 1 (or later) into the free buffer
+    pnext = plan_next();
     stage_c(b0);
-    stage_b(b1, it + 1, masked_c);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * C::NB - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-    // keep B's results inside this step (the compiler would otherwise sink the
-    // softmax below the barrier, away from the MFMAs it should overlap)
-    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
-    // step it + 2 must have landed before the barrier; step it + 3 may stay in flight
-    if (it + 3 < nsteps) wait_vmcnt<C::NPS>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (it + 4 < nsteps) issue_step(it + 4, b0);   // buffer of step it, consumed
-    const int t = b0;
-    b0 = b1;
-    b1 = b2;
-    b2 = b3;
-    b3 = t;
-  };
 
-  // Steps whose B needs the element mask (some key of the workgroup outside
-  // some query's window) sit at both ends of the band; the middle runs the
-  // unmasked body.  `full_lo .. full_hi` are the steps visible in full to every
-  // key of the workgroup: q0 >= j0 + BNK - 1 and q0 + BMQ - 1 <= j0 + W, q0 + BMQ <= T.
-  const int kv_last = imin(j0 + C::BNK - 1, T - 1);
-  int full_lo = 0, full_hi = -1;
-  if (nsteps > 0) {
-    const int qf0 = kv_last;                                  // first fully causal query
-    const int qf1 = imin(j0 + W, T) - (C::BMQ - 1);           // last start of a fully inside step
-    full_lo = imax(0, (qf0 + C::BMQ - 1) / C::BMQ - qb0);
-    full_hi = qf1 >= 0 ? qf1 / C::BMQ - qb0 : -1;
-    full_hi = imin(full_hi, nsteps - 1);
-  }
-  // body of step `it` prepares B(it + 1): unmasked iff step it + 1 is full
-  const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // it in [u0, u1] -> unmasked
-  const int nloop = nsteps - 1;   // steps with a successor
-  int it = 0;
-  for (; it < imin(u0, nloop); ++it) step_body(it, masked);
-  for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
-  for (; it < nloop; ++it) step_body(it, masked);
-  if (nsteps > 0) stage_c(b0);
-
-  // ---- epilogue: lane (g, c) holds key kj, d = 32 n + 8 q4 + 4 g + e
-  const float rk = ksc * (sqrtf((float)D) / kLog2e);
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-  const rsrc_t rkr = make_rsrc(k + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
-  float dot = 0.f;
-  f32x16 khat[C::NB];
+    // ---- epilogue: lane (g, c) holds key kj, d = 32 n + 8 q4 + 4 g + e.
+    // K of the key in that order comes from kf (d = 16 ks + 8 g + j): the
+    // lane's own kf holds the quads with (q4 & 1) == g, its partner lane c + 32
+    // (or c - 32) the others.
+    const float rk = ksc * (sqrtf((float)D) / kLog2e);
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    float dot = 0.f;
+    f32x16 khat[C::NB];
 #pragma unroll
-  for (int n = 0; n < C::NB; ++n)
+    for (int ks = 0; ks < C::KS; ++ks) {
+      // words (2 g + {0, 1}) of kf[ks]: elements 4 g .. 4 g + 3 of this lane's half
+      const uint32_t send0 = g ? kf[ks][0] : kf[ks][2], send1 = g ? kf[ks][1] : kf[ks][3];
+      const uint32_t got0 = __shfl_xor(send0, 32), got1 = __shfl_xor(send1, 32);
+      const uint32_t own0 = g ? kf[ks][2] : kf[ks][0], own1 = g ? kf[ks][3] : kf[ks][1];
+      // k-step ks covers d = 16 ks .. 16 ks + 15 = n = ks / 2, q4 = 2 (ks % 2) + {0, 1}
+      const int n = ks >> 1, qa = 2 * (ks & 1);
+      // quad q4 = qa + g comes from this lane, q4 = qa + 1 - g from the partner
+      const uint32_t mine[2] = {own0, own1}, other[2] = {got0, got1};
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const u32x2 kk = bload8(rkr, (c * rs + 32 * n + 8 * q4 + 4 * g) * 2);
-      const float x[4] = {bf_lo(kk[0]), bf_hi(kk[0]), bf_lo(kk[1]), bf_hi(kk[1])};
+      for (int hq = 0; hq < 2; ++hq) {
+        const uint32_t* src = (hq == g) ? mine : other;   // quad qa + hq
+        const float x[4] = {bf_lo(src[0]), bf_hi(src[0]), bf_lo(src[1]), bf_hi(src[1])};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        khat[n][4 * q4 + e] = x[e] * rk;
-        acc_dk[n][4 * q4 + e] *= inv_sqrt_d;
-        dot += acc_dk[n][4 * q4 + e] * khat[n][4 * q4 + e];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * (qa + hq) + e;
+          khat[n][r] = x[e] * rk;
+          acc_dk[n][r] *= inv_sqrt_d;
+          dot += acc_dk[n][r] * khat[n][r];
+        }
       }
     }
-  dot += __shfl_xor(dot, 32);
-  const float mean = dot * (1.0f / D);
-  const rsrc_t rdk = make_rsrc(dk + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
-  const rsrc_t rdv = make_rsrc(dv + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
+    dot += __shfl_xor(dot, 32);
+    const float mean = dot * (1.0f / D);
+    // outputs leave through LDS so that every store writes whole rows: the
+    // lane's values (key c, d = 32 n + 8 q4 + 4 g + e) go to a row-major
+    // 32 x D block, then each lane stores 16-byte chunks of 4 rows per
+    // instruction.  Waves 0 and 1 use the buffer of the last step (free after
+    // the barrier), waves 2 and 3 their own slots.
+    __syncthreads();
+    const int slot = w < 2 ? b0 + C::OUT_SLOT * w : C::XO_B + C::OUT_SLOT * (w - 2);
+    const rsrc_t rdk = make_rsrc(dk + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
+    const rsrc_t rdv = make_rsrc(dv + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
 #pragma unroll
-  for (int n = 0; n < C::NB; ++n)
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int off = (c * rs + 32 * n + 8 * q4 + 4 * g) * 2;
-      float y[4];
+      for (int n = 0; n < C::NB; ++n)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean);
-      bstore8(u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])}, rdk, off);
-      bstore8(u32x2{pack_bf16(acc_dv[n][4 * q4 + 0], acc_dv[n][4 * q4 + 1]),
-                    pack_bf16(acc_dv[n][4 * q4 + 2], acc_dv[n][4 * q4 + 3])}, rdv, off);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            y[e] = pass == 0 ? rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean) : acc_dv[n][4 * q4 + e];
+          st8(smem + slot + 2 * (c * C::OP + 32 * n + 8 * q4 + 4 * g),
+              u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
+        }
+      const rsrc_t ro = pass == 0 ? rdk : rdv;
+#pragma unroll
+      for (int i = 0; i < 32 * D / 8 / 64; ++i) {
+        const int idx = lane + 64 * i, r = idx / (D / 8), ch = idx % (D / 8);
+        const u32x4 val = lds16(smem, slot + 2 * (r * C::OP + 8 * ch));
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, (r * rs + 8 * ch) * 2, 0, 0);
+      }
     }
+  }
 }
 
 // ------------------------------------------------------------------ dQ
@@ -655,11 +766,18 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int nkt = (a.T + C::BNK - 1) / C::BNK;
+    const int ntiles = nkt * a.B * a.H;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+      return hipErrorInvalidDevice;
+    const int grid = imin(ncu, ntiles);   // persistent: one workgroup per CU
     ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(nkt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(256), C::LDS_BYTES, stream,
                        (const uint16_t*)a.qhat, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (const float*)a.kscale, (uint16_t*)a.dk, (uint16_t*)a.dv, a.T, a.H, W);
+                       (const float*)a.kscale, (uint16_t*)a.dk, (uint16_t*)a.dv, a.T, a.H, W, nkt,
+                       ntiles);
     prof_end(t1);
   }
   {

@@ -147,17 +147,18 @@ struct DmaTile {
 };
 
 // Direct-to-LDS tile with a per-wave instruction count: the tile's NCH 16-byte
-// chunks take NI = ceil(NCH / 64) wave instructions, wave w issuing w, w + 4, ...
-// (so waves may issue different numbers).  Only for pipelines that wait for
-// all outstanding loads (vmcnt 0).  The LDS region written is NI KiB; lanes
-// past the tile read out of range and write zero there.  Chunk q of the tile
+// chunks take NI = ceil(NCH / 64) wave instructions (so waves may issue
+// different numbers).  Only for pipelines that wait for
+// all outstanding loads (vmcnt 0).  NW waves share the work (wave w issues
+// w, w + NW, ...).  The LDS region written is NI KiB; lanes past the tile read
+// out of range and write zero there.  Chunk q of the tile
 // maps to the source byte offset returned by src(q) (a functor), or to an
 // out-of-range offset when src returns a negative value.
-template <int NCH_>
+template <int NCH_, int NW = 4>
 struct DmaTileV {
   static constexpr int NCH = NCH_;
   static constexpr int NI = (NCH + 63) / 64;
-  static constexpr int NIW = (NI + 3) / 4;
+  static constexpr int NIW = (NI + NW - 1) / NW;
   static constexpr int BYTES = NI * 1024;
   int voff[NIW];
 
@@ -165,7 +166,7 @@ struct DmaTileV {
   __device__ __forceinline__ void init(int w, int lane, F src) {
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
-      const int q = 64 * (w + 4 * i) + lane;
+      const int q = 64 * (w + NW * i) + lane;
       const int o = q < NCH ? src(q) : -1;
       voff[i] = o >= 0 ? o : 0x7ffffff0;
     }
@@ -173,9 +174,9 @@ struct DmaTileV {
   __device__ __forceinline__ void issue(rsrc_t rs_tile, unsigned char* smem, int lds_base, int w) const {
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
-      if (i + 1 < NIW || w + 4 * i < NI)
+      if (i + 1 < NIW || w + NW * i < NI)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs_tile, (SW_LDS void*)(smem + lds_base + 1024 * (w + 4 * i)), 16, voff[i], 0, 0, 0);
+            rs_tile, (SW_LDS void*)(smem + lds_base + 1024 * (w + NW * i)), 16, voff[i], 0, 0, 0);
   }
 };
 

@@ -713,17 +713,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   for (; it < nloop; ++it) step_body(it, masked);
   if (nsteps > 0) stage_c(b0);
 
-  // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past T dropped)
+  // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past
+  // T dropped).  The raw q rows come in and dq goes out through LDS (the step
+  // buffers, free once every wave is past its last product), so global memory
+  // sees whole rows.
+  using RS = RowStage32<D>;
+  static_assert(4 * RS::BYTES <= C::LDS_BYTES, "row staging fits in the step buffers");
   const rsrc_t rstat_q = make_rsrc(rq + sb, 4LL * T);
   const float r = bload4f(rstat_q, qi * 4);
-  const rsrc_t rqr = make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+  __syncthreads();
+  const int slot = RS::BYTES * w;
+  RS::load_rows(smem, slot, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
   float dot = 0.f;
   f32x16 xh[C::NB];
 #pragma unroll
   for (int n = 0; n < C::NB; ++n)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const u32x2 qq = bload8(rqr, (c * rs + 32 * n + 8 * q4 + 4 * g) * 2);
+      const u32x2 qq = RS::get(smem, slot, c, 32 * n + 8 * q4 + 4 * g);
       const float x[4] = {bf_lo(qq[0]), bf_hi(qq[0]), bf_lo(qq[1]), bf_hi(qq[1])};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -734,7 +741,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
   dot += __shfl_xor(dot, 32);
   const float mean = dot * (1.0f / D);
-  const rsrc_t rdq = make_rsrc(dq + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
 #pragma unroll
   for (int n = 0; n < C::NB; ++n)
 #pragma unroll
@@ -742,9 +748,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       float y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = r * (acc[n][4 * q4 + e] - xh[n][4 * q4 + e] * mean);
-      bstore8(u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])}, rdq,
-              (c * rs + 32 * n + 8 * q4 + 4 * g) * 2);
+      RS::put(smem, slot, c, 32 * n + 8 * q4 + 4 * g, u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
     }
+  RS::store_rows(smem, slot, make_rsrc(dq + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
 }
 
 template <int D>

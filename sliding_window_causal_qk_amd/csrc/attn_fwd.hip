@@ -331,16 +331,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // ---- epilogue: O = O^T / l, lse = shift + ln l  (stores past T are dropped)
   lsum += __shfl_xor(lsum, 32);
   const float inv = 1.0f / lsum;
-  const rsrc_t ro = make_rsrc(o + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+  // O leaves through LDS (the step buffers are free once every wave is past
+  // its last product) so that global memory sees whole rows
+  using RS = RowStage32<D>;
+  static_assert(4 * RS::BYTES <= C::LDS_BYTES, "output staging fits in the step buffers");
+  __syncthreads();
+  const int slot = RS::BYTES * w;
 #pragma unroll
   for (int n = 0; n < C::NB; ++n)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * n + 8 * q4 + 4 * g;
-      const u32x2 val = {pack_bf16(acc[n][4 * q4 + 0] * inv, acc[n][4 * q4 + 1] * inv),
-                         pack_bf16(acc[n][4 * q4 + 2] * inv, acc[n][4 * q4 + 3] * inv)};
-      bstore8(val, ro, (c * rs + d) * 2);
-    }
+    for (int q4 = 0; q4 < 4; ++q4)
+      RS::put(smem, slot, c, 32 * n + 8 * q4 + 4 * g,
+              u32x2{pack_bf16(acc[n][4 * q4 + 0] * inv, acc[n][4 * q4 + 1] * inv),
+                    pack_bf16(acc[n][4 * q4 + 2] * inv, acc[n][4 * q4 + 3] * inv)});
+  RS::store_rows(smem, slot, make_rsrc(o + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
   if (g == 0) {
     const rsrc_t rl = make_rsrc(lse + (size_t)bh * T, 4LL * T);
     bstore4f(sqrtf((float)D) + __logf(lsum), rl, qi * 4);

@@ -180,6 +180,42 @@ struct DmaTileV {
   }
 };
 
+// Row-major LDS staging of one wave's 32 x D block of bf16 values.  The MFMA
+// C layout gives lane (g, c) row c, columns 32 n + 8 q4 + 4 g + {0..3}: stored
+// straight to global memory those are 8-byte pieces spread over 32 rows.
+// Through LDS, global memory sees whole rows instead: 16-byte chunks, four
+// rows per wave instruction.  The pitch D + 8 keeps both the 8-byte
+// scattered accesses and the 16-byte row accesses free of bank conflicts.
+template <int D>
+struct RowStage32 {
+  static constexpr int OP = D + 8;
+  static constexpr int BYTES = 32 * OP * 2;
+  static constexpr int NCHUNK = 32 * D / 8 / 64;   // 16-byte chunks per lane
+  // 8-byte piece of row c at column col (a multiple of 4)
+  static __device__ __forceinline__ void put(unsigned char* smem, int slot, int c, int col, u32x2 v) {
+    st8(smem + slot + 2 * (c * OP + col), v);
+  }
+  static __device__ __forceinline__ u32x2 get(const unsigned char* smem, int slot, int c, int col) {
+    return ld8(smem + slot + 2 * (c * OP + col));
+  }
+  // global rows (row stride rs elements, descriptor at row 0) <-> staging
+  static __device__ __forceinline__ void store_rows(const unsigned char* smem, int slot, rsrc_t r, int rs, int lane) {
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) {
+      const int idx = lane + 64 * i, row = idx / (D / 8), ch = idx % (D / 8);
+      __builtin_amdgcn_raw_buffer_store_b128(ld16(smem + slot + 2 * (row * OP + 8 * ch)), r,
+                                             (row * rs + 8 * ch) * 2, 0, 0);
+    }
+  }
+  static __device__ __forceinline__ void load_rows(unsigned char* smem, int slot, rsrc_t r, int rs, int lane) {
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) {
+      const int idx = lane + 64 * i, row = idx / (D / 8), ch = idx % (D / 8);
+      st16(smem + slot + 2 * (row * OP + 8 * ch), bload16(r, (row * rs + 8 * ch) * 2));
+    }
+  }
+};
+
 // One 64-lane 4-byte direct-to-LDS load (256 bytes at lds_base + 4 lane).
 __device__ __forceinline__ void dma_row4(rsrc_t r, unsigned char* smem, int lds_base, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SW_LDS void*)(smem + lds_base), 4, voff, 0, 0, 0);

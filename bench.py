@@ -37,9 +37,9 @@ METRIC = "attn fwd+bwd effective TFLOP/s & % bf16 MFMA peak, T=2048 H=4 D=128 SS
 # algorithmic work credited to each kernel, per visible pair (FLOPs = c * D * N_vis)
 # or per launch bytes for the memory-bound passes
 KERNELS = {
-    0: ("k_scale", "hbm"),
+    0: ("fwd_prep", "hbm"),
     1: ("attn_fwd", "mfma"),
-    2: ("bwd_prep", "hbm"),
+    2: ("bwd_kscale", "hbm"),
     3: ("bwd_dkdv", "mfma"),
     4: ("bwd_dq", "mfma"),
 }
@@ -60,10 +60,11 @@ def algorithmic_units(kid, B, T, H, D, n_vis):
     E = B * T * H * D
     if kid in FLOPS_PER_PAIR_D:
         return FLOPS_PER_PAIR_D[kid] * D * n_vis * B * H, "flop"
-    if kid == 0:   # read K, write the key scales
-        return 2 * E + 4 * B * H * T, "byte"
-    # bwd_prep: read q, k, o, dO and lse; write q_hat and four [B, H, T] fp32 rows
-    return 4 * 2 * E + 2 * E + 5 * 4 * B * H * T, "byte"
+    if kid == 0:   # read K and V, write the key scales and V^T (rows padded to a multiple of 64)
+        LT = (T + 63) // 64 * 64
+        return 2 * E + 2 * E + 4 * B * H * T + 2 * B * H * D * LT, "byte"
+    # bwd_kscale: read K, write the key scales
+    return 2 * E + 4 * B * H * T, "byte"
 
 
 def cpu_baseline(wl, windows, budget_s):

@@ -137,9 +137,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 /*
  * Opt-in per-kernel timing, a measurement aid (not part of the operation).
  * While enabled, every kernel launch of attn_fwd / attn_bwd is bracketed by
- * two HIP events recorded on the launch stream.  Kernel ids: 0 k_scale
- * (key-scale pre-pass of the forward), 1 attn_fwd (forward attention),
- * 2 bwd_prep (Delta, q_hat, scales), 3 bwd_dkdv (dK and dV), 4 bwd_dq (dQ).
+ * two HIP events recorded on the launch stream.  Kernel ids: 0 fwd_prep
+ * (key scales and transposed V, the pre-pass of the forward), 1 attn_fwd
+ * (forward attention),
+ * 2 bwd_kscale (key scales of the backward), 3 bwd_dkdv (dK and dV),
+ * 4 bwd_dq (dQ, with q_hat, Delta and lse log2(e) for bwd_dkdv).
  *   attn_profile_enable(on): clears the totals and starts (on != 0) or stops
  *     recording; returns ATTN_ERR_HIP if waiting on earlier events failed.
  *   attn_profile_read(kernel, total_ms, launches): waits for the recorded

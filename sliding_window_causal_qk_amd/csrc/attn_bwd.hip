@@ -12,14 +12,16 @@
 //       (gradient of the unit-gain RMSNorm that the okx.com review and
 //        "Autoresearch 深度教程" §7.3 place on q and k before the product)
 //
-// Kernels:
-//   bwd_prep:  Delta, r_q, q_hat (bf16, to the workspace) and kscale for K.
-//   bwd_dkdv:  a workgroup owns 128 keys (32 per wave) and walks the query
-//              blocks of its band; dV^T and dK_hat^T stay in registers; the
-//              RMSNorm backward of K runs in the epilogue.
-//   bwd_dq:    a workgroup owns 128 queries (32 per wave) and walks the key
-//              tiles of its band, recomputing S and dP; the RMSNorm backward
-//              of Q runs in the epilogue.  No atomics: dQ is deterministic.
+// Kernels, in launch order:
+//   bwd_kscale: kscale = log2(e) / sqrt(D) / rms(k) for every key.
+//   bwd_dq:     a workgroup owns 128 queries (32 per wave): it normalises its
+//               queries, computes Delta = dO . o and writes q_hat, Delta and
+//               lse log2(e) for bwd_dkdv, then walks the key tiles of its band,
+//               recomputing S and dP; the RMSNorm backward of Q runs in the
+//               epilogue.  No atomics: dQ is deterministic.
+//   bwd_dkdv:   persistent; a tile is 128 keys (32 per wave) walking the query
+//               blocks of its band; dV^T and dK_hat^T stay in registers; the
+//               RMSNorm backward of K runs in the epilogue.
 #include <type_traits>
 
 #include "common.h"
@@ -29,78 +31,33 @@
 
 namespace swattn {
 
-// ------------------------------------------------------------------ prep
+// ------------------------------------------------------------------ key scales
+// kscale[b, h, t] = log2(e) / sqrt(D) * r(k[b, t, h, :]) for the backward
+// kernels.  D / 8 lanes share one key row (16 bytes each).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-    uint16_t* __restrict__ qhat, float* __restrict__ rq, float* __restrict__ kscale,
-    float* __restrict__ delta, const float* __restrict__ lse, float* __restrict__ lse2,
-    int nrows, int T, int H, float eps) {
+__global__ __launch_bounds__(256) void bwd_kscale_kernel(const uint16_t* __restrict__ k,
+                                                         float* __restrict__ kscale, int nrows,
+                                                         int T, int H, float eps) {
   constexpr int LPR = D / 8;
   const int tid = blockIdx.x * 256 + threadIdx.x;
   const int row = tid / LPR;
   const int part = tid % LPR;
-  float ssq = 0.f, ssk = 0.f, dot = 0.f;
-  u32x4 qv = {0, 0, 0, 0};
+  float ss = 0.f;
   if (row < nrows) {
-    const size_t off = (size_t)row * D + part * 8;
-    qv = ld16(q + off);
-    u32x4 kv = ld16(k + off), ov = ld16(o + off), dv = ld16(dout + off);
+    const u32x4 kv = ld16(k + (size_t)row * D + part * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float a = bf_lo(qv[e]), b = bf_hi(qv[e]);
-      ssq += a * a + b * b;
-      a = bf_lo(kv[e]); b = bf_hi(kv[e]);
-      ssk += a * a + b * b;
-      dot += bf_lo(ov[e]) * bf_lo(dv[e]) + bf_hi(ov[e]) * bf_hi(dv[e]);
+      const float a = bf_lo(kv[e]), b = bf_hi(kv[e]);
+      ss += a * a + b * b;
     }
   }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) {
-    ssq += __shfl_xor(ssq, m, LPR);
-    ssk += __shfl_xor(ssk, m, LPR);
-    dot += __shfl_xor(dot, m, LPR);
-  }
-  if (row < nrows) {
-    const float r = 1.0f / sqrtf(ssq * (1.0f / D) + eps);
-    u32x4 qh;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) qh[e] = pack_bf16(bf_lo(qv[e]) * r, bf_hi(qv[e]) * r);
-    st16(qhat + (size_t)row * D + part * 8, qh);
-    if (part == 0) {
-      const int h = row % H;
-      const int bt = row / H;
-      const int t = bt % T;
-      const int b = bt / T;
-      const size_t s = ((size_t)b * H + h) * T + t;
-      rq[s] = r;
-      kscale[s] = (1.0f / sqrtf(ssk * (1.0f / D) + eps)) * (kLog2e / sqrtf((float)D));
-      delta[s] = dot;
-      lse2[s] = lse[s] * kLog2e;
-    }
+  for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
+  if (row < nrows && part == 0) {
+    const int h = row % H, bt = row / H, t = bt % T, b = bt / T;
+    kscale[((size_t)b * H + h) * T + t] = (1.0f / sqrtf(ss * (1.0f / D) + eps)) * (kLog2e / sqrtf((float)D));
   }
 }
-
-// Staging of a tile of ROWS rows (row-major, pitch P bf16) through registers:
-// thread -> rows tid / CH + (256 / CH) p, 16-byte chunk tid % CH.  The
-// descriptor starts at the tile's first row, so rows past T load as zero.
-template <int D, int ROWS, int P>
-struct RowStage {
-  static constexpr int CH = D / 8;
-  static constexpr int RPP = 256 / CH;
-  static constexpr int PASSES = ROWS / RPP;
-  u32x4 r[PASSES];
-  __device__ __forceinline__ void load(rsrc_t rs_tile, int rs_elems, int tid) {
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-      r[p] = bload16(rs_tile, ((tid / CH + RPP * p) * rs_elems + 8 * (tid % CH)) * 2);
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) st16(lds + (tid / CH + RPP * p) * P + 8 * (tid % CH), r[p]);
-  }
-};
 
 // A-operand of a 32x32x16 MFMA whose k index runs along the rows of a row-major
 // LDS tile (two transposing reads): lane (g, c) gets column col0 + c of rows
@@ -110,11 +67,6 @@ struct RowStage {
 __device__ __forceinline__ int tr_off(int lane, int P) {
   const int li = lane & 15, g = lane >> 5;
   return (4 * g + (li >> 2)) * P + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-}
-__device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int off, int row0, int col0, int P) {
-  const u32x2 lo = lds_tr4(tile + off + row0 * P + col0);
-  const u32x2 hi = lds_tr4(tile + off + (row0 + 8) * P + col0);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // ------------------------------------------------------------------ dK / dV
@@ -544,11 +496,11 @@ struct DqCfg {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ qhat,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
-    const float* __restrict__ delta, const float* __restrict__ rq,
-    const float* __restrict__ kscale, uint16_t* __restrict__ dq, int T, int H, int W) {
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ kscale, uint16_t* __restrict__ qhat, float* __restrict__ delta,
+    float* __restrict__ lse2, uint16_t* __restrict__ dq, int T, int H, int W, float eps) {
   using C = DqCfg<D>;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -568,22 +520,56 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const size_t sbase = ((size_t)b * T * H + h) * D;
   const size_t sb = (size_t)bh * T;
 
+  // ---- the backward's per-query preparation, for this kernel and the dK/dV
+  // kernel that runs after it: r_q and q_hat = q r_q (bf16), Delta = dO . o,
+  // lse log2(e).  Lane (g, c) holds query qw0 + c, d = 16 ks + 8 g + 0..7.
   const int qw0 = i0 + 32 * w;
   const int qi = qw0 + c;
+  using RS = RowStage32<D>;
+  static_assert(4 * RS::BYTES <= C::LDS_BYTES, "row staging fits in the step buffers");
   u32x4 qf[C::KS], df[C::KS];
+  float r_q, dlt;
   {
-    const rsrc_t rq_ = make_rsrc(qhat + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+    const rsrc_t rqr = make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
     const rsrc_t rdo = make_rsrc(dout + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+    const rsrc_t ror = make_rsrc(o + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
+    float ss = 0.f, dd = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      qf[ks] = bload16(rq_, (c * rs + 16 * ks + 8 * g) * 2);
+      qf[ks] = bload16(rqr, (c * rs + 16 * ks + 8 * g) * 2);
       df[ks] = bload16(rdo, (c * rs + 16 * ks + 8 * g) * 2);
+      const u32x4 of = bload16(ror, (c * rs + 16 * ks + 8 * g) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf_lo(qf[ks][e]), bb = bf_hi(qf[ks][e]);
+        ss += a * a + bb * bb;
+        dd += bf_lo(df[ks][e]) * bf_lo(of[e]) + bf_hi(df[ks][e]) * bf_hi(of[e]);
+      }
     }
+    ss += __shfl_xor(ss, 32);
+    dd += __shfl_xor(dd, 32);
+    r_q = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+    dlt = dd;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[ks][e] = pack_bf16(bf_lo(qf[ks][e]) * r_q, bf_hi(qf[ks][e]) * r_q);
+    // q_hat rows leave through LDS (whole-row stores); the step buffers are
+    // not in use yet
+    const int slot = RS::BYTES * w;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      RS::put(smem, slot, c, 16 * ks + 8 * g, u32x2{qf[ks][0], qf[ks][1]});
+      RS::put(smem, slot, c, 16 * ks + 8 * g + 4, u32x2{qf[ks][2], qf[ks][3]});
+    }
+    RS::store_rows(smem, slot, make_rsrc(qhat + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
   }
-  const rsrc_t rstat_l = make_rsrc(lse2 + sb, 4LL * T);
-  const rsrc_t rstat_d = make_rsrc(delta + sb, 4LL * T);
-  const float lq = bload4f(rstat_l, qi * 4);
-  const float dlt = bload4f(rstat_d, qi * 4);
+  const float lq = bload4f(make_rsrc(lse + sb, 4LL * T), qi * 4) * kLog2e;
+  if (g == 0) {
+    bstore4f(dlt, make_rsrc(delta + sb, 4LL * T), qi * 4);
+    bstore4f(lq, make_rsrc(lse2 + sb, 4LL * T), qi * 4);
+  }
+  __syncthreads();   // every wave is done with its staging slot before the loads land there
 
   f32x16 acc[C::NB];
 #pragma unroll
@@ -717,10 +703,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   // T dropped).  The raw q rows come in and dq goes out through LDS (the step
   // buffers, free once every wave is past its last product), so global memory
   // sees whole rows.
-  using RS = RowStage32<D>;
-  static_assert(4 * RS::BYTES <= C::LDS_BYTES, "row staging fits in the step buffers");
-  const rsrc_t rstat_q = make_rsrc(rq + sb, 4LL * T);
-  const float r = bload4f(rstat_q, qi * 4);
+  const float r = r_q;
   __syncthreads();
   const int slot = RS::BYTES * w;
   RS::load_rows(smem, slot, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
@@ -757,13 +740,26 @@ template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const int nrows = a.B * a.T * a.H;
   const int nblk_p = (int)(((long long)nrows * (D / 8) + 255) / 256);
-  ProfToken t0 = prof_begin(K_BWD_PREP, stream);
-  hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(nblk_p), dim3(256), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.o,
-                     (const uint16_t*)a.dout, (uint16_t*)a.qhat, a.rq, a.kscale, a.delta, a.lse,
-                     a.lse2, nrows, a.T, a.H, a.eps);
+  ProfToken t0 = prof_begin(K_BWD_KSCALE, stream);
+  hipLaunchKernelGGL(bwd_kscale_kernel<D>, dim3(nblk_p), dim3(256), 0, stream,
+                     (const uint16_t*)a.k, a.kscale, nrows, a.T, a.H, a.eps);
   prof_end(t0);
   const int W = eff_window(a.T, a.window);
+  {
+    // dQ first: it also writes q_hat, Delta and lse log2(e) for dK/dV
+    using C = DqCfg<D>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(bwd_dq_kernel<D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    const int nqt = (a.T + C::BM - 1) / C::BM;
+    ProfToken t2 = prof_begin(K_BWD_DQ, stream);
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.o, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, (const float*)a.kscale,
+                       (uint16_t*)a.qhat, a.delta, a.lse2, (uint16_t*)a.dq, a.T, a.H, W, a.eps);
+    prof_end(t2);
+  }
   {
     using C = DkdvCfg<D>;
     // more than 64 KiB of dynamic LDS must be opted into, once per kernel
@@ -785,21 +781,6 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
                        (const float*)a.kscale, (uint16_t*)a.dk, (uint16_t*)a.dv, a.T, a.H, W, nkt,
                        ntiles);
     prof_end(t1);
-  }
-  {
-    using C = DqCfg<D>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_dq_kernel<D>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    const int nqt = (a.T + C::BM - 1) / C::BM;
-    ProfToken t2 = prof_begin(K_BWD_DQ, stream);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.qhat, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout, (const float*)a.lse2,
-                       (const float*)a.delta, (const float*)a.rq, (const float*)a.kscale,
-                       (uint16_t*)a.dq, a.T, a.H, W);
-    prof_end(t2);
   }
   return hipGetLastError();
 }

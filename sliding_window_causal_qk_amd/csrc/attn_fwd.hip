@@ -355,7 +355,7 @@ template <int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int nkb = a.LT / 64;
-  ProfToken t0 = prof_begin(K_SCALE, stream);
+  ProfToken t0 = prof_begin(K_FWD_PREP, stream);
   hipLaunchKernelGGL(fwd_prep_kernel<D>, dim3(nkb * a.B * a.H), dim3(256), 0, stream,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.kscale, (uint16_t*)a.vt, a.T,
                      a.H, a.LT, a.eps);

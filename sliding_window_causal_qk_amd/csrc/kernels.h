@@ -33,7 +33,6 @@ struct BwdArgs {
   void* dv;
   // workspace carve-up
   void* qhat;     // bf16 [B, T, H, D]: normalised queries
-  float* rq;      // [B, H, T]: 1 / rms(q)
   float* kscale;  // [B, H, T]: log2(e) / sqrt(D) / rms(k)
   float* delta;   // [B, H, T]: rowsum(dO * O)
   float* lse2;    // [B, H, T]: lse * log2(e)

@@ -5,7 +5,7 @@
 
 namespace swattn {
 
-enum KernelId { K_SCALE = 0, K_FWD = 1, K_BWD_PREP = 2, K_BWD_DKDV = 3, K_BWD_DQ = 4, kNumKernels = 5 };
+enum KernelId { K_FWD_PREP = 0, K_FWD = 1, K_BWD_KSCALE = 2, K_BWD_DKDV = 3, K_BWD_DQ = 4, kNumKernels = 5 };
 
 struct ProfToken {
   int kernel;  // -1: not recording

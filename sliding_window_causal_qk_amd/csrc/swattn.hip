@@ -118,7 +118,7 @@ size_t attn_fwd_workspace_bytes(int B, int T, int H, int D) {
 
 size_t attn_bwd_workspace_bytes(int B, int T, int H, int D) {
   if (B < 0 || T < 0 || H < 0 || D < 1) return 0;
-  return round_up((size_t)B * T * H * D * 2) + 4 * stats_bytes(B, T, H);
+  return round_up((size_t)B * T * H * D * 2) + 3 * stats_bytes(B, T, H);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
@@ -173,10 +173,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.qhat = ws;
-  a.rq = reinterpret_cast<float*>(ws + qh_bytes);
-  a.kscale = reinterpret_cast<float*>(ws + qh_bytes + sb);
-  a.delta = reinterpret_cast<float*>(ws + qh_bytes + 2 * sb);
-  a.lse2 = reinterpret_cast<float*>(ws + qh_bytes + 3 * sb);
+  a.kscale = reinterpret_cast<float*>(ws + qh_bytes);
+  a.delta = reinterpret_cast<float*>(ws + qh_bytes + sb);
+  a.lse2 = reinterpret_cast<float*>(ws + qh_bytes + 2 * sb);
   a.B = B; a.T = T; a.H = H; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_bwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

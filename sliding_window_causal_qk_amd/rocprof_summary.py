@@ -27,7 +27,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # kernel symbol fragment -> short name used by bench.py
-SHORT = (("k_scale_kernel", "k_scale"), ("attn_fwd_kernel", "attn_fwd"), ("bwd_prep_kernel", "bwd_prep"),
+SHORT = (("fwd_prep_kernel", "fwd_prep"), ("attn_fwd_kernel", "attn_fwd"), ("bwd_kscale_kernel", "bwd_kscale"),
          ("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"))
 
 

@@ -169,8 +169,8 @@ def test_unsupported(kw):
 def test_workspace_checks():
     need_f = sw.fwd_workspace_bytes(2, 64, 2, 64)
     need_b = sw.bwd_workspace_bytes(2, 64, 2, 64)
-    assert need_f >= 2 * 2 * 64 * 4
-    assert need_b >= 2 * 64 * 2 * 64 * 2 + 4 * 2 * 2 * 64 * 4
+    assert need_f >= 2 * 2 * 64 * 4 + 2 * 2 * 64 * 64 * 2
+    assert need_b >= 2 * 64 * 2 * 64 * 2 + 3 * 2 * 2 * 64 * 4
     assert _fwd(ws=None) == _lib.ATTN_ERR_WORKSPACE
     assert _fwd(wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE
     assert _fwd(ws=P + 16) == _lib.ATTN_ERR_WORKSPACE

@@ -33,29 +33,38 @@ namespace swattn {
 
 // ------------------------------------------------------------------ key scales
 // kscale[b, h, t] = log2(e) / sqrt(D) * r(k[b, t, h, :]) for the backward
-// kernels.  D / 8 lanes share one key row (16 bytes each).
+// kernels.  D / 8 lanes share one key row (16 bytes each); a thread handles
+// KR rows 256 / (D / 8) apart, so each has KR loads in flight.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_kscale_kernel(const uint16_t* __restrict__ k,
                                                          float* __restrict__ kscale, int nrows,
                                                          int T, int H, float eps) {
   constexpr int LPR = D / 8;
-  const int tid = blockIdx.x * 256 + threadIdx.x;
-  const int row = tid / LPR;
-  const int part = tid % LPR;
-  float ss = 0.f;
-  if (row < nrows) {
-    const u32x4 kv = ld16(k + (size_t)row * D + part * 8);
+  constexpr int RPB = 256 / LPR;     // rows per block pass
+  constexpr int KR = 4;
+  const int part = threadIdx.x % LPR;
+  const int rb = blockIdx.x * RPB * KR;   // first row of the block
+  const int row0 = rb + threadIdx.x / LPR;
+  // descriptor from the block's first row: rows past nrows read as zero
+  const rsrc_t rk = make_rsrc(k + (size_t)rb * D, (long long)(nrows - rb) * D * 2);
+  u32x4 kv[KR];
+#pragma unroll
+  for (int i = 0; i < KR; ++i) kv[i] = bload16(rk, ((threadIdx.x / LPR + RPB * i) * D + part * 8) * 2);
+#pragma unroll
+  for (int i = 0; i < KR; ++i) {
+    float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = bf_lo(kv[e]), b = bf_hi(kv[e]);
+      const float a = bf_lo(kv[i][e]), b = bf_hi(kv[i][e]);
       ss += a * a + b * b;
     }
-  }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
-  if (row < nrows && part == 0) {
-    const int h = row % H, bt = row / H, t = bt % T, b = bt / T;
-    kscale[((size_t)b * H + h) * T + t] = (1.0f / sqrtf(ss * (1.0f / D) + eps)) * (kLog2e / sqrtf((float)D));
+    for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
+    const int row = row0 + RPB * i;
+    if (row < nrows && part == 0) {
+      const int h = row % H, bt = row / H, t = bt % T, b = bt / T;
+      kscale[((size_t)b * H + h) * T + t] = (1.0f / sqrtf(ss * (1.0f / D) + eps)) * (kLog2e / sqrtf((float)D));
+    }
   }
 }
 
@@ -739,7 +748,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const int nrows = a.B * a.T * a.H;
-  const int nblk_p = (int)(((long long)nrows * (D / 8) + 255) / 256);
+  const int nblk_p = (int)(((long long)nrows * (D / 8) + 4 * 256 - 1) / (4 * 256));
   ProfToken t0 = prof_begin(K_BWD_KSCALE, stream);
   hipLaunchKernelGGL(bwd_kscale_kernel<D>, dim3(nblk_p), dim3(256), 0, stream,
                      (const uint16_t*)a.k, a.kscale, nrows, a.T, a.H, a.eps);

@@ -69,14 +69,19 @@ def _col(row: dict, *names):
 
 def trace(args):
     rows = _rows(_find(args.dir, "kernel_trace.csv"))
+    rows.sort(key=lambda r: int(_col(r, "Start_Timestamp", "Start-Timestamp")))
     per = {}
     for r in rows:
         name = _col(r, "Kernel_Name", "Kernel-Name", "Name")
         dur = (int(_col(r, "End_Timestamp", "End-Timestamp")) - int(_col(r, "Start_Timestamp", "Start-Timestamp"))) / 1e3
         per.setdefault(name, []).append(dur)
+    if args.skip_first:   # drop each kernel's first launches (the warm-up step)
+        per = {k: v[args.skip_first:] for k, v in per.items() if len(v) > args.skip_first}
     total = sum(sum(v) for v in per.values())
     lines = [f"# rocprofv3 kernel trace: {args.title}", "",
              "Command (from the repository root):", "", "    " + args.command, "",
+             f"Launches counted: all but the first {args.skip_first} of each kernel." if args.skip_first else
+             "Launches counted: all.", "",
              f"{'kernel':<12} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_ms':>9} {'pct':>6}  symbol"]
     for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{(short_name(name) or '-'):<12} {len(d):>6} {statistics.fmean(d):>9.2f} {min(d):>9.2f} "
@@ -140,6 +145,8 @@ def main():
     t.add_argument("--dir", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="")
+    t.add_argument("--skip-first", type=int, default=0,
+                   help="ignore the first N launches of every kernel (a warm-up step)")
     t.add_argument("--out")
     c = sub.add_parser("traffic")
     c.add_argument("--fetch", required=True)

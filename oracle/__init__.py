@@ -22,6 +22,7 @@ library routines, finite differences, values printed on the pages); none is
 """
 from .attention import (  # noqa: F401
     rms_norm,
+    kv_head,
     visible_mask,
     n_visible,
     scores,

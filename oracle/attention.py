@@ -25,6 +25,14 @@ What is computed (per batch b and head h; x[t] is the D-vector at position t):
       o_i  = sum_j P_ij v_j
       lse_i = m_i + ln sum_visible exp(s_ij - m_i)      (natural log, scaled logits)
 
+  Grouped key/value heads ("Autoresearch 深度教程" §7.3: the attention module
+  has n_kv_head key/value heads, allowed to be fewer than n_head; the K and V
+  projections are n_kv_head heads wide).  The pages do not spell out which
+  query heads share a key/value head; FlashAttention's grouping is taken:
+  with G = H / H_kv, query head h reads key/value head floor(h / G).  K and V
+  are then [B, T, H_kv, D]; a shared head's gradient is the sum over the G
+  query heads that read it.
+
   Backward, given dO (chain rule through the three steps above):
       dV = P^T dO
       dP = dO V^T
@@ -83,10 +91,22 @@ def _slice(x: np.ndarray, b: int, h: int) -> np.ndarray:
     return _f64(x[b, :, h, :])
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """Key/value head read by query head h (G = H / H_kv consecutive query
+    heads share one)."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError("the number of query heads must be a multiple of H_kv")
+    return h // (H // H_kv)
+
+
+def _kv(q, k, h: int) -> int:
+    return kv_head(h, np.shape(q)[2], np.shape(k)[2])
+
+
 def scores(q, k, b: int, h: int, window: int, causal: bool, eps: float,
            rows: Sequence[int] | None = None) -> np.ndarray:
     """Masked scaled scores s [len(rows), T] of slice (b, h); -inf where masked."""
-    qs, ks = _slice(q, b, h), _slice(k, b, h)
+    qs, ks = _slice(q, b, h), _slice(k, b, _kv(q, k, h))
     T, D = ks.shape
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
     qh, _ = rms_norm(qs[rows], eps)
@@ -111,7 +131,7 @@ def fwd_rows(q, k, v, b: int, h: int, rows: Sequence[int], window: int,
              causal: bool = True, eps: float = 1e-6) -> Tuple[np.ndarray, np.ndarray]:
     """Output rows o[rows] [n, D] and lse[rows] [n] of slice (b, h)."""
     rows = np.asarray(rows, dtype=np.int64)
-    vs = _slice(v, b, h)
+    vs = _slice(v, b, _kv(q, v, h))
     o = np.empty((len(rows), vs.shape[1]))
     lse = np.empty(len(rows))
     for s0 in range(0, len(rows), _ROW_BLOCK):
@@ -124,7 +144,8 @@ def fwd_rows(q, k, v, b: int, h: int, rows: Sequence[int], window: int,
 
 def attention_fwd(q, k, v, window: int, causal: bool = True,
                   eps: float = 1e-6) -> Tuple[np.ndarray, np.ndarray]:
-    """Full forward: o [B, T, H, D] and lse [B, H, T], both float64."""
+    """Full forward: o [B, T, H, D] and lse [B, H, T], both float64 (k, v may
+    have fewer heads than q: grouped key/value heads)."""
     B, T, H, D = np.shape(q)
     o = np.empty((B, T, H, np.shape(v)[3]))
     lse = np.empty((B, H, T))
@@ -142,8 +163,11 @@ def _rms_norm_bwd(x: np.ndarray, dx_hat: np.ndarray, eps: float) -> np.ndarray:
 
 
 def _bwd_slice(q, k, v, do, b, h, window, causal, eps):
-    """dq, dk, dv of one full slice [T, D] each."""
-    qs, ks, vs, dos = (_slice(t, b, h) for t in (q, k, v, do))
+    """Of query head h: dq [T, D], and its contributions dk_hat, dv [T, D] to
+    the gradients of the key/value head it reads."""
+    hk = _kv(q, k, h)
+    qs, dos = _slice(q, b, h), _slice(do, b, h)
+    ks, vs = _slice(k, b, hk), _slice(v, b, hk)
     T, D = qs.shape
     qh, _ = rms_norm(qs, eps)
     kh, _ = rms_norm(ks, eps)
@@ -160,19 +184,28 @@ def _bwd_slice(q, k, v, do, b, h, window, causal, eps):
         ds = p * (dp - delta[:, None])
         dq_hat[rows] = ds @ kh / np.sqrt(D)
         dk_hat += ds.T @ qh[rows] / np.sqrt(D)
-    return _rms_norm_bwd(qs, dq_hat, eps), _rms_norm_bwd(ks, dk_hat, eps), dv
+    return _rms_norm_bwd(qs, dq_hat, eps), dk_hat, dv
 
 
 def attention_bwd(q, k, v, do, window: int, causal: bool = True,
                   eps: float = 1e-6) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Full backward: dq, dk, dv [B, T, H, D] float64 (w.r.t. the pre-norm q, k)."""
+    """Full backward: dq [B, T, H, D], dk and dv [B, T, H_kv, D], float64
+    (w.r.t. the pre-norm q, k)."""
     B, T, H, D = np.shape(q)
+    H_kv = np.shape(k)[2]
     dq = np.empty((B, T, H, D))
-    dk = np.empty((B, T, H, D))
-    dv = np.empty((B, T, H, np.shape(v)[3]))
+    dk_hat = np.zeros((B, T, H_kv, D))
+    dv = np.zeros((B, T, H_kv, np.shape(v)[3]))
     for b in range(B):
         for h in range(H):
-            dq[b, :, h], dk[b, :, h], dv[b, :, h] = _bwd_slice(q, k, v, do, b, h, window, causal, eps)
+            hk = _kv(q, k, h)
+            dq[b, :, h], dkh, dvh = _bwd_slice(q, k, v, do, b, h, window, causal, eps)
+            dk_hat[b, :, hk] += dkh
+            dv[b, :, hk] += dvh
+    dk = np.empty((B, T, H_kv, D))
+    for b in range(B):
+        for hk in range(H_kv):
+            dk[b, :, hk] = _rms_norm_bwd(_slice(k, b, hk), dk_hat[b, :, hk], eps)
     return dq, dk, dv
 
 
@@ -190,11 +223,16 @@ def _rows_seeing(keys: Iterable[int], T: int, window: int, causal: bool) -> np.n
 
 def bwd_rows(q, k, v, do, b: int, h: int, q_rows: Sequence[int], k_rows: Sequence[int],
              window: int, causal: bool = True, eps: float = 1e-6):
-    """Sampled gradients of slice (b, h): dq[q_rows], dk[k_rows], dv[k_rows].
+    """Sampled gradients: dq[q_rows] of query head h; dk[k_rows], dv[k_rows] of
+    the key/value head that h reads, summed over every query head reading it.
 
     dq_i needs only row i of P and dP.  dk_j and dv_j need column j of P and dS,
-    hence every row that sees key j (each with its own lse and Delta)."""
-    qs, ks, vs, dos = (_slice(t, b, h) for t in (q, k, v, do))
+    hence every row that sees key j (each with its own lse and Delta), in every
+    query head of the group."""
+    H, H_kv = np.shape(q)[2], np.shape(k)[2]
+    hk = kv_head(h, H, H_kv)
+    qs, dos = _slice(q, b, h), _slice(do, b, h)
+    ks, vs = _slice(k, b, hk), _slice(v, b, hk)
     T, D = qs.shape
     q_rows = np.asarray(q_rows, dtype=np.int64)
     k_rows = np.asarray(k_rows, dtype=np.int64)
@@ -213,15 +251,18 @@ def bwd_rows(q, k, v, do, b: int, h: int, q_rows: Sequence[int], k_rows: Sequenc
     dk_hat = np.zeros((len(k_rows), D))
     dv = np.zeros((len(k_rows), vs.shape[1]))
     need = _rows_seeing(k_rows, T, window, causal)
-    for s0 in range(0, len(need), _ROW_BLOCK):
-        rows = need[s0:s0 + _ROW_BLOCK]
-        p, _ = probabilities(q, k, b, h, window, causal, eps, rows)
-        o = p @ vs
-        dp = dos[rows] @ vs.T
-        delta = np.sum(dos[rows] * o, axis=1)
-        ds = p * (dp - delta[:, None])
-        qh, _ = rms_norm(qs[rows], eps)
-        dv += p[:, k_rows].T @ dos[rows]
-        dk_hat += ds[:, k_rows].T @ qh / np.sqrt(D)
+    G = H // H_kv
+    for hq in range(hk * G, hk * G + G):
+        qs_g, dos_g = _slice(q, b, hq), _slice(do, b, hq)
+        for s0 in range(0, len(need), _ROW_BLOCK):
+            rows = need[s0:s0 + _ROW_BLOCK]
+            p, _ = probabilities(q, k, b, hq, window, causal, eps, rows)
+            o = p @ vs
+            dp = dos_g[rows] @ vs.T
+            delta = np.sum(dos_g[rows] * o, axis=1)
+            ds = p * (dp - delta[:, None])
+            qh, _ = rms_norm(qs_g[rows], eps)
+            dv += p[:, k_rows].T @ dos_g[rows]
+            dk_hat += ds[:, k_rows].T @ qh / np.sqrt(D)
     dk = _rms_norm_bwd(ks[k_rows], dk_hat, eps)
     return dq, dk, dv

@@ -46,6 +46,9 @@ MUTANTS = [
      "return r[..., None] * (dx_hat + x_hat * proj)"),
     ("norm_bwd_no_r", "return r[..., None] * (dx_hat - x_hat * proj)",
      "return (dx_hat - x_hat * proj)"),
+    ("gqa_heads_interleaved", "return h // (H // H_kv)", "return h % H_kv"),
+    ("gqa_dk_last_head_only", "dk_hat[b, :, hk] += dkh", "dk_hat[b, :, hk] = dkh"),
+    ("gqa_dv_last_head_only", "dv[b, :, hk] += dvh", "dv[b, :, hk] = dvh"),
 ]
 
 
@@ -72,6 +75,14 @@ def _pins_pass(A) -> bool:
             got = (A.attention_fwd(q, k, v, W, True, EPS)[0],) + tuple(A.attention_bwd(q, k, v, do, W, True, EPS))
             if not all(np.allclose(a, b, rtol=1e-9, atol=1e-11) for a, b in zip(got, ref)):
                 return False
+        # library: fp64 SDPA with grouped key/value heads
+        T, D, W = 20, 8, 6
+        q, do = (_rand((1, T, 4, D), s) for s in (21, 22))
+        k, v = (_rand((1, T, 2, D), s) for s in (23, 24))
+        ref = _torch_reference(q, k, v, do, W, True, EPS)
+        got = (A.attention_fwd(q, k, v, W, True, EPS)[0],) + tuple(A.attention_bwd(q, k, v, do, W, True, EPS))
+        if not all(a.shape == b.shape and np.allclose(a, b, rtol=1e-9, atol=1e-11) for a, b in zip(got, ref)):
+            return False
         # closed form: identical keys
         T, D = 16, 8
         q, v, do = (_rand((1, T, 1, D), s) for s in (13, 14, 15))

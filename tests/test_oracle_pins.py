@@ -120,7 +120,8 @@ def _torch_reference(q, k, v, do, window, causal, eps):
         mask = (j <= i) & ((i - j <= window) if window >= 0 else torch.ones(T, T, dtype=torch.bool))
     else:
         mask = (abs(i - j) <= window) if window >= 0 else torch.ones(T, T, dtype=torch.bool)
-    o = F.scaled_dot_product_attention(qn, kn, vt.transpose(1, 2), attn_mask=mask)
+    o = F.scaled_dot_product_attention(qn, kn, vt.transpose(1, 2), attn_mask=mask,
+                                       enable_gqa=k.shape[2] != H)
     o = o.transpose(1, 2)
     o.backward(torch.tensor(do))
     return o.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
@@ -139,6 +140,50 @@ def test_fwd_bwd_match_torch_sdpa(T, D, W, causal):
         np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
 
 
+# ------------------------------------------------- grouped key/value heads
+
+@pytest.mark.parametrize("H,H_kv,T,D,W", [
+    (4, 2, 40, 16, 7), (4, 1, 33, 8, -1), (6, 3, 24, 16, 0), (6, 2, 48, 8, 13),
+])
+def test_gqa_matches_torch_sdpa(H, H_kv, T, D, W):
+    """torch's SDPA with enable_gqa (query head h reads key/value head
+    h // (H / H_kv)), autograd for the gradients of the shared heads."""
+    q, do = (_rand((2, T, H, D), s) for s in (41, 42))
+    k, v = (_rand((2, T, H_kv, D), s) for s in (43, 44))
+    o_ref, dq_ref, dk_ref, dv_ref = _torch_reference(q, k, v, do, W, True, EPS)
+    o, _ = oracle.attention_fwd(q, k, v, W, True, EPS)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, W, True, EPS)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    for a, b in ((o, o_ref), (dq, dq_ref), (dk, dk_ref), (dv, dv_ref)):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_gqa_equals_repeated_heads():
+    """Grouped heads are the plain case with every key/value head repeated for
+    its G query heads; the shared head's gradient is the sum over the group."""
+    B, T, H, H_kv, D, W = 1, 30, 6, 2, 8, 5
+    G = H // H_kv
+    q, do = (_rand((B, T, H, D), s) for s in (45, 46))
+    k, v = (_rand((B, T, H_kv, D), s) for s in (47, 48))
+    kr, vr = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+    o, lse = oracle.attention_fwd(q, k, v, W, True, EPS)
+    o_r, lse_r = oracle.attention_fwd(q, kr, vr, W, True, EPS)
+    np.testing.assert_allclose(o, o_r, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_r, rtol=0, atol=1e-14)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, W, True, EPS)
+    dq_r, dk_r, dv_r = oracle.attention_bwd(q, kr, vr, do, W, True, EPS)
+    np.testing.assert_allclose(dq, dq_r, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, dk_r.reshape(B, T, H_kv, G, D).sum(axis=3), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_r.reshape(B, T, H_kv, G, D).sum(axis=3), rtol=0, atol=1e-13)
+
+
+def test_gqa_rejects_uneven_groups():
+    q = _rand((1, 4, 3, 4), 1)
+    k = _rand((1, 4, 2, 4), 2)
+    with pytest.raises(ValueError):
+        oracle.attention_fwd(q, k, k, 2, True, EPS)
+
+
 # -------------------------------------------------------- finite differences
 
 @pytest.mark.parametrize("W,causal", [(5, True), (-1, True), (3, False)])
@@ -150,6 +195,28 @@ def test_bwd_matches_finite_differences(W, causal):
     def loss(qq, kk, vv):
         o, _ = oracle.attention_fwd(qq, kk, vv, W, causal, EPS)
         return float(np.sum(o * do))
+
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.max(np.abs(num - grad)) / np.max(np.abs(grad))
+        assert err < 1e-7, (which, err)
+
+
+def test_gqa_bwd_matches_finite_differences():
+    T, D, W = 10, 4, 3
+    q, do = (_rand((1, T, 4, D), s) for s in (49, 50))
+    k, v = (_rand((1, T, 2, D), s) for s in (51, 52))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, W, True, EPS)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(oracle.attention_fwd(qq, kk, vv, W, True, EPS)[0] * do))
 
     h = 1e-6
     for which, grad in ((0, dq), (1, dk), (2, dv)):
@@ -273,6 +340,24 @@ def test_sampled_rows_match_full():
         np.testing.assert_allclose(sq, dq[b, rows, h], rtol=0, atol=1e-12)
         np.testing.assert_allclose(sk, dk[b, rows, h], rtol=0, atol=1e-12)
         np.testing.assert_allclose(sv, dv[b, rows, h], rtol=0, atol=1e-12)
+
+
+def test_sampled_rows_match_full_gqa():
+    T, D, W, H, H_kv = 50, 8, 11, 4, 2
+    q, do = (_rand((1, T, H, D), s) for s in (53, 54))
+    k, v = (_rand((1, T, H_kv, D), s) for s in (55, 56))
+    o, lse = oracle.attention_fwd(q, k, v, W, True, EPS)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, W, True, EPS)
+    rows = [0, 7, 11, 12, 30, T - 1]
+    for h in range(H):
+        orow, lrow = oracle.fwd_rows(q, k, v, 0, h, rows, W, True, EPS)
+        np.testing.assert_allclose(orow, o[0, rows, h], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lrow, lse[0, h, rows], rtol=0, atol=1e-14)
+        sq, sk, sv = oracle.bwd_rows(q, k, v, do, 0, h, rows, rows, W, True, EPS)
+        hk = oracle.kv_head(h, H, H_kv)
+        np.testing.assert_allclose(sq, dq[0, rows, h], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sk, dk[0, rows, hk], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sv, dv[0, rows, hk], rtol=0, atol=1e-12)
 
 
 def test_invalid_window_rejected():

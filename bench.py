@@ -55,16 +55,18 @@ def kernel_sources_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_units(kid, B, T, H, D, n_vis):
-    """(amount, unit) of algorithmic work of one launch of kernel `kid`."""
-    E = B * T * H * D
+def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None):
+    """(amount, unit) of algorithmic work of one launch of kernel `kid`
+    (H query heads, H_kv key/value heads)."""
+    H_kv = H if H_kv is None else H_kv
+    E_kv = B * T * H_kv * D
     if kid in FLOPS_PER_PAIR_D:
         return FLOPS_PER_PAIR_D[kid] * D * n_vis * B * H, "flop"
     if kid == 0:   # read K and V, write the key scales and V^T (rows padded to a multiple of 64)
         LT = (T + 63) // 64 * 64
-        return 2 * E + 2 * E + 4 * B * H * T + 2 * B * H * D * LT, "byte"
+        return 2 * E_kv + 2 * E_kv + 4 * B * H_kv * T + 2 * B * H_kv * D * LT, "byte"
     # bwd_kscale: read K, write the key scales
-    return 2 * E + 4 * B * H * T, "byte"
+    return 2 * E_kv + 4 * B * H_kv * T, "byte"
 
 
 def cpu_baseline(wl, windows, budget_s):
@@ -129,14 +131,15 @@ def main():
     from workloads import make_layer_inputs_device, workload
 
     wl = workload(args.workload)
-    B, T, H, D = wl.B, wl.T, wl.H, wl.D
+    B, T, H, D, H_kv = wl.B, wl.T, wl.H, wl.D, wl.kv_heads
     if wl.explicit_window is not None:
         windows = [wl.explicit_window] * wl.n_layer
     else:
         windows = sw.layer_windows(wl.pattern, wl.n_layer, T)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    print(f"[bench] workload {wl.name}: B={B} T={T} H={H} D={D} windows={windows}", file=sys.stderr, flush=True)
+    print(f"[bench] workload {wl.name}: B={B} T={T} H={H} H_kv={H_kv} D={D} windows={windows}",
+          file=sys.stderr, flush=True)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 18          # fp32 elements
@@ -151,13 +154,14 @@ def main():
 
     layers = []
     for l, W in enumerate(windows):
-        q, k, v, do = make_layer_inputs_device(B, T, H, D, wl.seed(l), wl.sigma_qkv, wl.sigma_do, dev)
+        q, k, v, do = make_layer_inputs_device(B, T, H, D, wl.seed(l), wl.sigma_qkv, wl.sigma_do, dev,
+                                               H_kv=H_kv)
         layers.append(dict(
             W=W, q=q, k=k, v=v, do=do,
             o=torch.empty_like(q), lse=torch.empty((B, H, T), dtype=torch.float32, device=dev),
             dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-            wsf=torch.empty(sw.fwd_workspace_bytes(B, T, H, D), dtype=torch.uint8, device=dev),
-            wsb=torch.empty(sw.bwd_workspace_bytes(B, T, H, D), dtype=torch.uint8, device=dev),
+            wsf=torch.empty(sw.fwd_workspace_bytes(B, T, H, D, H_kv), dtype=torch.uint8, device=dev),
+            wsb=torch.empty(sw.bwd_workspace_bytes(B, T, H, D, H_kv), dtype=torch.uint8, device=dev),
             n_vis=sw.visible_pairs(T, W),
         ))
     torch.cuda.synchronize()
@@ -199,7 +203,7 @@ def main():
         work = 0.0
         unit = None
         for L in layers:
-            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"])
+            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"], H_kv)
             work += amt * args.steps
         secs = tot.value * 1e-3
         if unit == "flop":
@@ -251,7 +255,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "D": D, "pattern": wl.pattern,
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "H_kv": H_kv, "D": D,
+                   "pattern": wl.pattern,
                    "n_layer": len(windows), "windows": windows, "eps": wl.eps,
                    "flop_convention": "F14 = 14*D*N_vis per (batch, head, layer)",
                    "flops_per_step": flops_step, "parallelism": "single GPU"},

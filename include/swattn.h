@@ -135,6 +135,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* stream);
 
 /*
+ * Grouped key/value heads ("Autoresearch 深度教程" §7.3: the attention module
+ * has n_kv_head key/value heads, which may be fewer than its n_head query
+ * heads; the K and V projections are n_kv_head heads wide).  The pages do not
+ * say which query heads share a key/value head; FlashAttention's grouping is
+ * used: with G = H / H_kv, query head h reads key/value head h / G.
+ *
+ * Same contract as attn_fwd / attn_bwd, except that k, v (inputs) and dk, dv
+ * (outputs) are bf16 [B, T, H_kv, D]; dk and dv of a shared head are the sums
+ * over its G query heads.  H_kv must be >= 1 and divide H (else
+ * ATTN_ERR_INVALID_ARG; H_kv < 0 is always invalid, and with H = 0 the call is
+ * an empty problem).  H_kv = H is exactly attn_fwd / attn_bwd.  The workspace
+ * sizes are those of the *_gqa_workspace_bytes functions.
+ */
+size_t attn_fwd_gqa_workspace_bytes(int B, int T, int H, int H_kv, int D);
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                 void* stream);
+size_t attn_bwd_gqa_workspace_bytes(int B, int T, int H, int H_kv, int D);
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                 void* stream);
+
+/*
  * Opt-in per-kernel timing, a measurement aid (not part of the operation).
  * While enabled, every kernel launch of attn_fwd / attn_bwd is bracketed by
  * two HIP events recorded on the launch stream.  Kernel ids: 0 fwd_prep

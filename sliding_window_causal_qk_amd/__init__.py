@@ -8,7 +8,9 @@ memory and the current stream.
     windows = layer_windows("SSSL", n_layer=8, seq_len=2048)   # [1024, ..., 2048]
     o = attention(q, k, v, window=windows[l])                    # autograd-aware
 
-q, k, v: bf16 CUDA tensors [B, T, H, D] (contiguous), D in {64, 128}.
+q: bf16 CUDA tensor [B, T, H, D] (contiguous), D in {64, 128}; k, v: bf16
+[B, T, H_kv, D] with H_kv dividing H (grouped key/value heads: query head h
+reads key/value head h // (H // H_kv); H_kv = H is plain multi-head attention).
 """
 from __future__ import annotations
 
@@ -47,12 +49,16 @@ def band_tiles(T: int, window: int, rows: int, cols: int, by_key: bool = False):
     return [tuple(a[i] for a in arrs) for i in range((T + rows - 1) // rows)]
 
 
-def fwd_workspace_bytes(B: int, T: int, H: int, D: int) -> int:
-    return int(lib().attn_fwd_workspace_bytes(B, T, H, D))
+def fwd_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int] = None) -> int:
+    if H_kv is None:
+        return int(lib().attn_fwd_workspace_bytes(B, T, H, D))
+    return int(lib().attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D))
 
 
-def bwd_workspace_bytes(B: int, T: int, H: int, D: int) -> int:
-    return int(lib().attn_bwd_workspace_bytes(B, T, H, D))
+def bwd_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int] = None) -> int:
+    if H_kv is None:
+        return int(lib().attn_bwd_workspace_bytes(B, T, H, D))
+    return int(lib().attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D))
 
 
 def _torch():
@@ -89,38 +95,56 @@ def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
     """Forward through the C ABI.  Returns (o bf16 [B,T,H,D], lse fp32 [B,H,T])."""
     torch = _torch()
     B, T, H, D = q.shape
-    for n, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(t, n, (B, T, H, D), torch.bfloat16)
+    H_kv = k.shape[2] if k.dim() == 4 else -1
+    _check_tensor(q, "q", (B, T, H, D), torch.bfloat16)
+    for n, t in (("k", k), ("v", v)):
+        _check_tensor(t, n, (B, T, H_kv, D), torch.bfloat16)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor(o, "out", (B, T, H, D), torch.bfloat16)
     _check_tensor(l, "lse", (B, H, T), torch.float32)
-    nbytes = fwd_workspace_bytes(B, T, H, D)
+    nbytes = fwd_workspace_bytes(B, T, H, D, H_kv)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(),
-                        B, T, H, D, int(window), int(bool(causal)), float(eps), _stream(stream))
+    if H_kv == H:
+        st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(),
+                            B, T, H, D, int(window), int(bool(causal)), float(eps), _stream(stream))
+    else:
+        st = lib().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), ws.data_ptr(),
+                                ws.numel(), B, T, H, H_kv, D, int(window), int(bool(causal)),
+                                float(eps), _stream(stream))
     check(st, "attn_fwd")
     return o, l
 
 
 def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float = 1e-6, *,
              dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward through the C ABI.  Returns (dq, dk, dv), bf16 [B,T,H,D]."""
+    """Backward through the C ABI.  Returns (dq, dk, dv): bf16, dq [B,T,H,D],
+    dk and dv shaped like k and v."""
     torch = _torch()
     B, T, H, D = q.shape
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    H_kv = k.shape[2] if k.dim() == 4 else -1
+    for n, t in (("q", q), ("o", o), ("dout", dout)):
         _check_tensor(t, n, (B, T, H, D), torch.bfloat16)
+    for n, t in (("k", k), ("v", v)):
+        _check_tensor(t, n, (B, T, H_kv, D), torch.bfloat16)
     _check_tensor(lse, "lse", (B, H, T), torch.float32)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_tensor(t, n, (B, T, H, D), torch.bfloat16)
-    nbytes = bwd_workspace_bytes(B, T, H, D)
+    _check_tensor(dq, "dq", (B, T, H, D), torch.bfloat16)
+    for n, t in (("dk", dk), ("dv", dv)):
+        _check_tensor(t, n, (B, T, H_kv, D), torch.bfloat16)
+    nbytes = bwd_workspace_bytes(B, T, H, D, H_kv)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                        _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(),
-                        B, T, H, D, int(window), int(bool(causal)), float(eps), _stream(stream))
+    if H_kv == H:
+        st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                            _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(),
+                            B, T, H, D, int(window), int(bool(causal)), float(eps), _stream(stream))
+    else:
+        st = lib().attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(),
+                                B, T, H, H_kv, D, int(window), int(bool(causal)), float(eps),
+                                _stream(stream))
     check(st, "attn_bwd")
     return dq, dk, dv
 

@@ -18,7 +18,8 @@ ATTN_ERR_HIP = 4
 EXPORTS = (
     "attn_status_string", "attn_version", "attn_layer_windows", "attn_visible_pairs",
     "attn_band_tiles", "attn_fwd_workspace_bytes", "attn_fwd", "attn_bwd_workspace_bytes",
-    "attn_bwd", "attn_profile_enable", "attn_profile_read", "attn_kernel_name",
+    "attn_bwd", "attn_fwd_gqa_workspace_bytes", "attn_fwd_gqa", "attn_bwd_gqa_workspace_bytes",
+    "attn_bwd_gqa", "attn_profile_enable", "attn_profile_read", "attn_kernel_name",
 )
 
 
@@ -62,6 +63,15 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size,
                            c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_vp]
     L.attn_bwd.restype = c_int
+    for f in (L.attn_fwd_gqa_workspace_bytes, L.attn_bwd_gqa_workspace_bytes):
+        f.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        f.restype = c_size
+    L.attn_fwd_gqa.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size,
+                               c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_vp]
+    L.attn_fwd_gqa.restype = c_int
+    L.attn_bwd_gqa.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size,
+                               c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_vp]
+    L.attn_bwd_gqa.restype = c_int
     L.attn_profile_enable.argtypes = [c_int]
     L.attn_profile_enable.restype = c_int
     L.attn_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_double),

@@ -11,6 +11,9 @@
 //   dx    = r (dx_hat - x_hat mean_d(dx_hat x_hat))   for x in {q, k}
 //       (gradient of the unit-gain RMSNorm that the okx.com review and
 //        "Autoresearch 深度教程" §7.3 place on q and k before the product)
+// With grouped key/value heads (G = H / H_kv query heads read one key/value
+// head, "Autoresearch 深度教程" §7.3), dk and dv of a shared head sum the
+// contributions of its G query heads.
 //
 // Kernels, in launch order:
 //   bwd_kscale: kscale = log2(e) / sqrt(D) / rms(k) for every key.
@@ -19,8 +22,9 @@
 //               lse log2(e) for bwd_dkdv, then walks the key tiles of its band,
 //               recomputing S and dP; the RMSNorm backward of Q runs in the
 //               epilogue.  No atomics: dQ is deterministic.
-//   bwd_dkdv:   persistent; a tile is 128 keys (32 per wave) walking the query
-//               blocks of its band; dV^T and dK_hat^T stay in registers; the
+//   bwd_dkdv:   persistent; a tile is 128 keys (32 per wave) of one key/value
+//               head, walking the query blocks of its band in each of the
+//               head's G query heads; dV^T and dK_hat^T stay in registers; the
 //               RMSNorm backward of K runs in the epilogue.
 #include <type_traits>
 
@@ -94,11 +98,14 @@ __device__ __forceinline__ int tr_off(int lane, int P) {
 // the next block runs on the VALU while the matrix cores still work through
 // C(i), and LDS reads for both products are in flight together.
 //
+// A tile of a key/value head shared by G query heads walks its band G times,
+// once per query head, and accumulates all of them before the epilogue.
+//
 // Tiles are split into 8 contiguous ranges, one per XCD (workgroup b runs on
 // XCD b % 8), so the tiles of one (batch, head) share that XCD's L2; inside a
 // range, round i gives workgroup s the tile i G8 + (s + 7 i) mod G8, which
 // rotates the light tiles of the causal tail through all workgroups.
-template <int D>
+template <int D, bool GROUPED>
 struct DkdvCfg {
   static constexpr int BNK = 128;       // keys per tile (32 per wave)
   static constexpr int BMQ = 32;        // queries per step
@@ -107,8 +114,8 @@ struct DkdvCfg {
   static constexpr int NB = D / 32;
   static constexpr int P = D + 24;      // q_hat / dO row pitch (bf16): odd multiple of 16 bytes
   static constexpr int PK = D + 8;      // K / V row pitch in the prefetch region
-  using Tile = DmaTileV<BMQ * P / 8>;
-  using KVTile = DmaTileV<BNK * PK / 8>;
+  using Tile = DmaTileV<BMQ * P / 8, 4, 1 + GROUPED>;
+  using KVTile = DmaTileV<BNK * PK / 8, 4, 1 + GROUPED>;
   static constexpr int DO_B = Tile::BYTES;          // dO tile after the q_hat tile
   static constexpr int ST_B = 2 * Tile::BYTES;      // 4 x 256 B: spare, spare, lse2, Delta
   static constexpr int STAGE = ST_B + 1024;
@@ -121,22 +128,29 @@ struct DkdvCfg {
   static_assert(2 * OUT_SLOT <= STAGE, "waves 0 and 1 stage their outputs in a freed step buffer");
 };
 
-template <int D>
+// GROUPED = false is the plain multi-head case, compiled with G = 1 so that the
+// walk over the query heads of a group folds away.
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qhat, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const float* __restrict__ kscale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    int T, int H, int W, int nkt, int ntiles) {
-  using C = DkdvCfg<D>;
+    int T, int H, int G_arg, int W, int nkt, int ntiles) {
+  using C = DkdvCfg<D, GROUPED>;
+  const int G = GROUPED ? G_arg : 1;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
   const int w = uniform(tid >> 6);
   const int lane = tid & 63, g = lane >> 5, c = lane & 31;
-  const int rs = H * D;
+  const int rs = H * D;                 // query-side row stride (q_hat, dO)
   const long long rsb = 2LL * rs;
   const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
+  const int Hkv = H / G;
+  const int rs_kv = Hkv * D;            // key-side row stride (K, V, dK, dV)
+  const long long rsb_kv = 2LL * rs_kv;
+  const long long kslice_bytes = (long long)(T - 1) * rsb_kv + 2 * D;
 
   // ---- tile list of this workgroup
   int xr = 0, ws = blockIdx.x, G8 = gridDim.x, N8 = ntiles;
@@ -151,11 +165,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     return (i * G8 < N8 && r < N8) ? xr * N8 + r : -1;
   };
   struct TileGeo {
-    int bh, j0, qb0, nsteps;
+    int bh, b, hk, j0, qb0, nsteps;   // bh = b Hkv + hk: the key/value slice
   };
   auto geo = [&](int t) {
     TileGeo tg;
     tg.bh = t / nkt;
+    tg.b = tg.bh / Hkv;
+    tg.hk = tg.bh - tg.b * Hkv;
     tg.j0 = (t % nkt) * C::BNK;
     int q_lo, q_hi;
     const bool any = q_range(tg.j0, tg.j0 + C::BNK - 1, T, W, &q_lo, &q_hi);
@@ -163,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     tg.nsteps = any ? q_hi / C::BMQ - tg.qb0 + 1 : 0;
     return tg;
   };
-  auto slice_base = [&](int bh) { return ((size_t)(bh / H) * T * H + (bh % H)) * D; };
+  auto kv_base = [&](const TileGeo& tg) { return ((size_t)tg.b * T * Hkv + tg.hk) * D; };
 
   // ---- direct-to-LDS staging
   typename C::Tile tile;
@@ -174,9 +190,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   typename C::KVTile kvtile;
   kvtile.init(w, lane, [&](int qc) {
     const int r = qc / (C::PK / 8), ch = qc % (C::PK / 8);
-    return (ch < D / 8) ? (r * rs + 8 * ch) * 2 : -1;
+    return (ch < D / 8) ? (r * rs_kv + 8 * ch) * 2 : -1;
   });
-  // The stream of query blocks runs across tiles.  A plan holds the source
+  // The stream of query blocks runs across tiles (and, in a tile, across the
+  // G query heads of its key/value head).  A plan holds the source
   // of the next block (computed with scalar control flow outside the
   // scheduled regions); issuing it is branch-free, so the loads interleave
   // with the MFMAs.  Past the end of the stream a plan has no bytes in range
@@ -190,28 +207,56 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     int nst;
     int r0;
   };
-  int dt = 0, ds = 0;                    // the next block: step ds of the dt-th tile
+  // The cursor: the next block is step ds of query head dgi of the dt-th tile.
+  // Its source pointers advance by one block per step and are recomputed only
+  // when the cursor moves to another query head or tile.
+  int dt = 0, ds = 0, dgi = 0;
   TileGeo dgeo;
+  const uint16_t* cq = qhat;
+  const uint16_t* cdo = dout;
+  const float* cst = w == 2 ? lse2 : delta;
+  long long cbytes = 0;
+  int cr0 = 0;
+  auto seek_head = [&]() {
+    const int hq = dgeo.hk * G + dgi;
+    const size_t sbase = ((size_t)dgeo.b * T * H + hq) * D;
+    cr0 = dgeo.qb0 * C::BMQ;
+    cq = qhat + sbase + (size_t)cr0 * rs;
+    cdo = dout + sbase + (size_t)cr0 * rs;
+    cbytes = slice_bytes - cr0 * rsb;
+    cst = (w == 2 ? lse2 : delta) + (size_t)(dgeo.b * H + hq) * T;
+  };
   int tcur = tile_at(0);
-  if (tcur >= 0) dgeo = geo(tcur);
+  if (tcur >= 0) {
+    dgeo = geo(tcur);
+    seek_head();
+  }
   auto plan_next = [&]() {
     while (tcur >= 0 && ds >= dgeo.nsteps) {
-      ++dt;
       ds = 0;
-      tcur = tile_at(dt);
-      if (tcur >= 0) dgeo = geo(tcur);
+      if (++dgi >= G) {
+        dgi = 0;
+        ++dt;
+        tcur = tile_at(dt);
+        if (tcur >= 0) dgeo = geo(tcur);
+      }
+      if (tcur >= 0) seek_head();
     }
     DmaPlan pl;
     const bool ok = tcur >= 0;
-    const int bh = ok ? dgeo.bh : 0;
-    const size_t sbase = slice_base(bh);
-    pl.r0 = ok ? (dgeo.qb0 + ds) * C::BMQ : 0;
-    pl.qh = qhat + sbase + (size_t)pl.r0 * rs;
-    pl.dO = dout + sbase + (size_t)pl.r0 * rs;
-    pl.nbytes = ok ? slice_bytes - pl.r0 * rsb : 0;
-    pl.st = (w == 2 ? lse2 : delta) + (size_t)bh * T;
+    pl.qh = cq;
+    pl.dO = cdo;
+    pl.st = cst;
+    pl.r0 = ok ? cr0 : 0;
+    pl.nbytes = ok ? cbytes : 0;
     pl.nst = (ok && w >= 2) ? 4 * T : 0;
-    if (ok) ++ds;
+    if (ok) {
+      ++ds;
+      cq += (size_t)C::BMQ * rs;
+      cdo += (size_t)C::BMQ * rs;
+      cbytes -= C::BMQ * rsb;
+      cr0 += C::BMQ;
+    }
     return pl;
   };
   auto issue_plan = [&](const DmaPlan& pl, int base) {
@@ -220,9 +265,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dma_row4(make_rsrc(pl.st, pl.nst), smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
   };
   auto issue_kv = [&](const TileGeo& tg) {
-    const size_t sbase = slice_base(tg.bh);
-    kvtile.issue(make_rsrc(k + sbase + (size_t)tg.j0 * rs, slice_bytes - tg.j0 * rsb), smem, C::KV_B, w);
-    kvtile.issue(make_rsrc(v + sbase + (size_t)tg.j0 * rs, slice_bytes - tg.j0 * rsb), smem,
+    const size_t sbase = kv_base(tg);
+    kvtile.issue(make_rsrc(k + sbase + (size_t)tg.j0 * rs_kv, kslice_bytes - tg.j0 * rsb_kv), smem,
+                 C::KV_B, w);
+    kvtile.issue(make_rsrc(v + sbase + (size_t)tg.j0 * rs_kv, kslice_bytes - tg.j0 * rsb_kv), smem,
                  C::KV_B + C::KVTile::BYTES, w);
   };
 
@@ -252,7 +298,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     if (t < 0) break;
     const TileGeo tg = geo(t);
     const int bh = tg.bh, j0 = tg.j0, qb0 = tg.qb0, nsteps = tg.nsteps;
-    const size_t sbase = slice_base(bh);
+    const size_t sbase = kv_base(tg);
     const int kw0 = j0 + 32 * w;
     const int kj = kw0 + c;
 
@@ -344,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // buffers.  The instruction order inside a step is fixed with schedule
     // groups: A(it+1)'s reads and MFMAs first, then C(it)'s MFMAs with their
     // transposed reads, with B(it+1)'s VALU work slotted between.
-    auto step_body = [&](int it, auto masked_c) {
+    auto step_body = [&](int s_next, auto masked_c) {   // B for step s_next of its query head
       issue_plan(pnext, b2);      // block it + 2 into the free buffer, spread over A
       stage_a(b1);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
@@ -357,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_barrier(0);   // A stays ahead of C and B
       stage_c(b0);
-      stage_b(b1, it + 1, masked_c);
+      stage_b(b1, s_next, masked_c);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
       for (int i = 0; i < 4 * C::NB - 4; ++i) {
@@ -395,18 +441,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       full_hi = qf1 >= 0 ? qf1 / C::BMQ - qb0 : -1;
       full_hi = imin(full_hi, nsteps - 1);
     }
-    // body of step `it` prepares B(it + 1): unmasked iff step it + 1 is full
-    const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // it in [u0, u1] -> unmasked
-    const int nloop = nsteps - 1;   // steps with a successor
+    // The tile runs G nsteps steps: step it + 1 = gi nsteps + s is step s of
+    // query head gi.  Body `it` prepares B(it + 1), unmasked iff step s is full.
+    const int nloop = G * nsteps - 1;   // steps with a successor
     int it = 0;
-    if (nloop > 0) step_body(it++, masked);
+    if (nloop > 0) {   // step 1 of head 0, or step 0 of head 1
+      step_body(nsteps > 1 ? 1 : 0, masked);
+      it = 1;
+    }
     if (kv_pending) {   // after a barrier that follows every wave's K / V reads
       if (nloop == 0) __syncthreads();
       issue_kv(geo(tile_at(ti + 1)));
     }
-    for (; it < imin(u0, nloop); ++it) step_body(it, masked);
-    for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
-    for (; it < nloop; ++it) step_body(it, masked);
+    for (int gi = 0; gi < G; ++gi) {
+      const int base = gi * nsteps;                         // it + 1 = base + s
+      const int it_end = imin(base + nsteps - 1, nloop);
+      for (; it < imin(base + full_lo - 1, it_end); ++it) step_body(it + 1 - base, masked);
+      for (; it < imin(base + full_hi, it_end); ++it) step_body(it + 1 - base, unmasked);
+      for (; it < it_end; ++it) step_body(it + 1 - base, masked);
+    }
     issue_plan(pnext, b2);          // the next tile's block 1 (or later) into the free buffer
     pnext = plan_next();
     stage_c(b0);
@@ -451,8 +504,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // the barrier), waves 2 and 3 their own slots.
     __syncthreads();
     const int slot = w < 2 ? b0 + C::OUT_SLOT * w : C::XO_B + C::OUT_SLOT * (w - 2);
-    const rsrc_t rdk = make_rsrc(dk + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
-    const rsrc_t rdv = make_rsrc(dv + sbase + (size_t)kw0 * rs, slice_bytes - kw0 * rsb);
+    const rsrc_t rdk = make_rsrc(dk + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+    const rsrc_t rdv = make_rsrc(dv + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -471,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int i = 0; i < 32 * D / 8 / 64; ++i) {
         const int idx = lane + 64 * i, r = idx / (D / 8), ch = idx % (D / 8);
         const u32x4 val = lds16(smem, slot + 2 * (r * C::OP + 8 * ch));
-        __builtin_amdgcn_raw_buffer_store_b128(val, ro, (r * rs + 8 * ch) * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro, (r * rs_kv + 8 * ch) * 2, 0, 0);
       }
     }
   }
@@ -509,7 +562,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ kscale, uint16_t* __restrict__ qhat, float* __restrict__ delta,
-    float* __restrict__ lse2, uint16_t* __restrict__ dq, int T, int H, int W, float eps) {
+    float* __restrict__ lse2, uint16_t* __restrict__ dq, int T, int H, int G, int W, float eps) {
   using C = DqCfg<D>;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -528,6 +581,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
   const size_t sbase = ((size_t)b * T * H + h) * D;
   const size_t sb = (size_t)bh * T;
+  const int Hkv = H / G;
+  const int rs_kv = Hkv * D;               // K / V row stride (elements)
+  const long long rsb_kv = 2LL * rs_kv;
+  const long long kslice_bytes = (long long)(T - 1) * rsb_kv + 2 * D;
+  const size_t kvbase = ((size_t)b * T * Hkv + h / G) * D;
 
   // ---- the backward's per-query preparation, for this kernel and the dK/dV
   // kernel that runs after it: r_q and q_hat = q r_q (bf16), Delta = dO . o,
@@ -591,14 +649,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
   // ---- direct-to-LDS staging of one key step
   typename C::Tile tile;
-  tile.init(w, lane, rs);
-  const rsrc_t rks = make_rsrc(kscale + sb, w == 0 ? 4LL * T : 0);   // wave 0 loads kscale
-  const uint16_t* k_s = k + sbase;
-  const uint16_t* v_s = v + sbase;
+  tile.init(w, lane, rs_kv);
+  const rsrc_t rks = make_rsrc(kscale + (size_t)(b * Hkv + h / G) * T, w == 0 ? 4LL * T : 0);   // wave 0 loads kscale
+  const uint16_t* k_s = k + kvbase;
+  const uint16_t* v_s = v + kvbase;
   auto issue_step = [&](int step, int base) {
     const int r0 = (jb0 + step) * C::BN;
-    tile.issue(make_rsrc(k_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base, w);
-    tile.issue(make_rsrc(v_s + (size_t)r0 * rs, slice_bytes - r0 * rsb), smem, base + C::V_B, w);
+    tile.issue(make_rsrc(k_s + (size_t)r0 * rs_kv, kslice_bytes - r0 * rsb_kv), smem, base, w);
+    tile.issue(make_rsrc(v_s + (size_t)r0 * rs_kv, kslice_bytes - r0 * rsb_kv), smem, base + C::V_B, w);
     dma_row4(rks, smem, base + C::ST_B + 256 * w, (r0 + lane) * 4);
   };
 
@@ -747,11 +805,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  const int nrows = a.B * a.T * a.H;
+  const int G = a.H / a.Hkv;
+  const int nrows = a.B * a.T * a.Hkv;
   const int nblk_p = (int)(((long long)nrows * (D / 8) + 4 * 256 - 1) / (4 * 256));
   ProfToken t0 = prof_begin(K_BWD_KSCALE, stream);
   hipLaunchKernelGGL(bwd_kscale_kernel<D>, dim3(nblk_p), dim3(256), 0, stream,
-                     (const uint16_t*)a.k, a.kscale, nrows, a.T, a.H, a.eps);
+                     (const uint16_t*)a.k, a.kscale, nrows, a.T, a.Hkv, a.eps);
   prof_end(t0);
   const int W = eff_window(a.T, a.window);
   {
@@ -766,29 +825,35 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.o, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, (const float*)a.kscale,
-                       (uint16_t*)a.qhat, a.delta, a.lse2, (uint16_t*)a.dq, a.T, a.H, W, a.eps);
+                       (uint16_t*)a.qhat, a.delta, a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps);
     prof_end(t2);
   }
   {
-    using C = DkdvCfg<D>;
+    using C = DkdvCfg<D, false>;
+    static_assert(C::LDS_BYTES == DkdvCfg<D, true>::LDS_BYTES, "one LDS size for both versions");
     // more than 64 KiB of dynamic LDS must be opted into, once per kernel
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_dkdv_kernel<D>),
+        reinterpret_cast<const void*>(bwd_dkdv_kernel<D, false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
+    static const hipError_t attr_g = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(bwd_dkdv_kernel<D, true>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (attr_g != hipSuccess) return attr_g;
     const int nkt = (a.T + C::BNK - 1) / C::BNK;
-    const int ntiles = nkt * a.B * a.H;
+    const int ntiles = nkt * a.B * a.Hkv;
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
       return hipErrorInvalidDevice;
     const int grid = imin(ncu, ntiles);   // persistent: one workgroup per CU
     ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid), dim3(256), C::LDS_BYTES, stream,
+    hipLaunchKernelGGL((G == 1 ? bwd_dkdv_kernel<D, false> : bwd_dkdv_kernel<D, true>), dim3(grid),
+                       dim3(256), C::LDS_BYTES, stream,
                        (const uint16_t*)a.qhat, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (const float*)a.kscale, (uint16_t*)a.dk, (uint16_t*)a.dv, a.T, a.H, W, nkt,
-                       ntiles);
+                       (const float*)a.kscale, (uint16_t*)a.dk, (uint16_t*)a.dv, a.T, a.H, G, W,
+                       nkt, ntiles);
     prof_end(t1);
   }
   return hipGetLastError();

@@ -9,6 +9,8 @@
 //   s_ij = q_hat_i . k_hat_j / sqrt(D) for the keys of the (W, 0) window
 //       ("Autoresearch 深度教程" §5.2.2; FlashAttention-3 call of §5.2.1)
 //   o_i = softmax_j(s_ij) v,   lse_i = ln sum_j exp(s_ij)
+//   With grouped key/value heads (n_kv_head < n_head, "Autoresearch 深度教程"
+//   §7.3), query head h reads key/value head h / G, G = H / H_kv.
 //
 // MI355X design:
 //  * QK-norm bounds every logit: |s_ij| <= |q_hat||k_hat|/sqrt(D) < sqrt(D).
@@ -43,7 +45,8 @@
 namespace swattn {
 
 // ------------------------------------------------------------ forward pre-pass
-// One workgroup per (batch, head, block of 64 keys):
+// One workgroup per (batch, key/value head, block of 64 keys); H is the number
+// of key/value heads here:
 //   kscale[b, h, t] = log2(e) / sqrt(D) * r(k[b, t, h, :])
 //   vt[b, h, d, tpos(t)] = v[b, t, h, d]   (V transposed; inside every group of
 //       16 keys the columns are permuted by tpos16, so that the 8 keys one lane
@@ -149,7 +152,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const float* __restrict__ kscale,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int LT, int W, float eps) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int G, int LT, int W,
+    float eps) {
   using C = FwdCfg<D>;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -158,6 +162,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int bh = lid / nqt;
   const int qt = nqt - 1 - (lid % nqt);  // heaviest query tiles of a head first
   const int b = bh / H, h = bh % H;
+  const int Hkv = H / G;
+  const int bhk = b * Hkv + h / G;        // key/value slice read by this head
   const int i0 = qt * C::BM;
 
   const int tid = threadIdx.x;
@@ -167,6 +173,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const long long rsb = 2LL * rs;
   const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
   const size_t sbase = ((size_t)b * T * H + h) * D;
+  const int rs_kv = Hkv * D;               // K row stride (elements)
+  const long long rsb_kv = 2LL * rs_kv;
+  const long long kslice_bytes = (long long)(T - 1) * rsb_kv + 2 * D;
 
   // ---- query fragment: normalised q row (i0 + 32 w + c), B operand of S^T = K Q^T
   const int qw0 = i0 + 32 * w;
@@ -207,20 +216,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   typename C::KTile ktile;
   ktile.init(w, lane, [&](int qc) {
     const int r = qc / (C::PK / 8), ch = qc % (C::PK / 8);
-    return (r < C::BN && ch < D / 8) ? (r * rs + 8 * ch) * 2 : -1;
+    return (r < C::BN && ch < D / 8) ? (r * rs_kv + 8 * ch) * 2 : -1;
   });
   typename C::VTile vtile;
   vtile.init(w, lane, [&](int qc) {
     const int r = qc >> 2, s = qc & 3;
     return (r * LT + 8 * vt_slot(r, s)) * 2;
   });
-  const rsrc_t rks = make_rsrc(kscale + (size_t)bh * T, 4LL * T);
-  const uint16_t* k_s = k + sbase;
-  const uint16_t* vt_s = vt + (size_t)bh * D * LT;
+  const rsrc_t rks = make_rsrc(kscale + (size_t)bhk * T, 4LL * T);
+  const uint16_t* k_s = k + ((size_t)b * T * Hkv + (h / G)) * D;
+  const uint16_t* vt_s = vt + (size_t)bhk * D * LT;
   const long long vt_bytes = 2LL * D * LT;
   auto issue_step = [&](int step, int base) {
     const int j0 = (jb0 + step) * C::BN;
-    ktile.issue(make_rsrc(k_s + (size_t)j0 * rs, slice_bytes - j0 * rsb), smem, base, w);
+    ktile.issue(make_rsrc(k_s + (size_t)j0 * rs_kv, kslice_bytes - j0 * rsb_kv), smem, base, w);
     vtile.issue(make_rsrc(vt_s + j0, vt_bytes - 2LL * j0), smem, base + C::V_B, w);
     if (w == 0) dma_row4(rks, smem, base + C::ST_B, (j0 + lane) * 4);   // wave 0 loads kscale
   };
@@ -356,9 +365,9 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D>;
   const int nkb = a.LT / 64;
   ProfToken t0 = prof_begin(K_FWD_PREP, stream);
-  hipLaunchKernelGGL(fwd_prep_kernel<D>, dim3(nkb * a.B * a.H), dim3(256), 0, stream,
+  hipLaunchKernelGGL(fwd_prep_kernel<D>, dim3(nkb * a.B * a.Hkv), dim3(256), 0, stream,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.kscale, (uint16_t*)a.vt, a.T,
-                     a.H, a.LT, a.eps);
+                     a.Hkv, a.LT, a.eps);
   prof_end(t0);
   const int nqt = (a.T + C::BM - 1) / C::BM;
   const int nblk = nqt * a.B * a.H;
@@ -371,7 +380,8 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   ProfToken t1 = prof_begin(K_FWD, stream);
   hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nblk), dim3(256), C::LDS_BYTES, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.vt,
-                     (const float*)a.kscale, (uint16_t*)a.o, a.lse, a.T, a.H, a.LT, W, a.eps);
+                     (const float*)a.kscale, (uint16_t*)a.o, a.lse, a.T, a.H, a.H / a.Hkv, a.LT, W,
+                     a.eps);
   prof_end(t1);
   return hipGetLastError();
 }

@@ -153,8 +153,9 @@ struct DmaTile {
 // w, w + NW, ...).  The LDS region written is NI KiB; lanes past the tile read
 // out of range and write zero there.  Chunk q of the tile
 // maps to the source byte offset returned by src(q) (a functor), or to an
-// out-of-range offset when src returns a negative value.
-template <int NCH_, int NW = 4>
+// out-of-range offset when src returns a negative value.  TAG keeps the
+// instantiations of different kernels apart (see DmaTile).
+template <int NCH_, int NW = 4, int TAG = 0>
 struct DmaTileV {
   static constexpr int NCH = NCH_;
   static constexpr int NI = (NCH + 63) / 64;

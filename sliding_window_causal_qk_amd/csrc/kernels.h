@@ -13,10 +13,11 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  float* kscale;  // workspace: [B, H, T]
-  void* vt;       // workspace: bf16 [B, H, D, LT], V transposed, keys permuted (tpos16)
+  float* kscale;  // workspace: [B, Hkv, T]
+  void* vt;       // workspace: bf16 [B, Hkv, D, LT], V transposed, keys permuted (tpos16)
   int LT;         // row length of vt: T rounded up to a multiple of 64
   int B, T, H, D;
+  int Hkv;        // key/value heads (H is a multiple); q, o: H heads, k, v: Hkv
   int window;
   float eps;
 };
@@ -33,10 +34,11 @@ struct BwdArgs {
   void* dv;
   // workspace carve-up
   void* qhat;     // bf16 [B, T, H, D]: normalised queries
-  float* kscale;  // [B, H, T]: log2(e) / sqrt(D) / rms(k)
+  float* kscale;  // [B, Hkv, T]: log2(e) / sqrt(D) / rms(k)
   float* delta;   // [B, H, T]: rowsum(dO * O)
   float* lse2;    // [B, H, T]: lse * log2(e)
   int B, T, H, D;
+  int Hkv;        // key/value heads (H is a multiple); k, v, dk, dv have Hkv heads
   int window;
   float eps;
 };

@@ -18,11 +18,13 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Shared checks of attn_fwd / attn_bwd.  Returns ATTN_OK to proceed, or a
-// status; *empty is set for problems with no rows.
-int check_common(int B, int T, int H, int D, int window, int causal, float eps, bool* empty) {
+// Shared checks of the forward / backward entry points.  Returns ATTN_OK to
+// proceed, or a status; *empty is set for problems with no rows.
+int check_common(int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                 bool* empty) {
   *empty = false;
-  if (B < 0 || T < 0 || H < 0 || D < 1) return ATTN_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return ATTN_ERR_INVALID_ARG;
+  if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(eps) || !(eps > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (window < -1) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
@@ -111,21 +113,29 @@ int attn_band_tiles(int T, int window, int rows, int cols, int by_key, int* firs
   return ATTN_OK;
 }
 
-size_t attn_fwd_workspace_bytes(int B, int T, int H, int D) {
-  if (B < 0 || T < 0 || H < 0 || D < 1) return 0;
-  return stats_bytes(B, T, H) + vt_bytes(B, T, H, D);
+size_t attn_fwd_gqa_workspace_bytes(int B, int T, int H, int H_kv, int D) {
+  if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
+  return stats_bytes(B, T, H_kv) + vt_bytes(B, T, H_kv, D);
 }
 
-size_t attn_bwd_workspace_bytes(int B, int T, int H, int D) {
-  if (B < 0 || T < 0 || H < 0 || D < 1) return 0;
+size_t attn_fwd_workspace_bytes(int B, int T, int H, int D) {
+  return attn_fwd_gqa_workspace_bytes(B, T, H, H, D);
+}
+
+size_t attn_bwd_gqa_workspace_bytes(int B, int T, int H, int H_kv, int D) {
+  if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
   return round_up((size_t)B * T * H * D * 2) + 3 * stats_bytes(B, T, H);
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-             size_t workspace_bytes, int B, int T, int H, int D, int window, int causal, float eps,
-             void* stream) {
+size_t attn_bwd_workspace_bytes(int B, int T, int H, int D) {
+  return attn_bwd_gqa_workspace_bytes(B, T, H, H, D);
+}
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, int B, int T, int H, int H_kv, int D,
+                 int window, int causal, float eps, void* stream) {
   bool empty;
-  int st = check_common(B, T, H, D, window, causal, eps, &empty);
+  int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
   const void* ins[3] = {q, k, v};
   for (const void* p : ins)
@@ -133,25 +143,33 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, v
   if (!o || !lse || !aligned(o, 16) || !aligned(lse, 16)) return ATTN_ERR_INVALID_ARG;
   for (const void* p : ins)
     if (p == o || p == (const void*)lse) return ATTN_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < attn_fwd_workspace_bytes(B, T, H, D)) return ATTN_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D))
+    return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
 
   swattn::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.kscale = static_cast<float*>(workspace);
-  a.vt = static_cast<char*>(workspace) + stats_bytes(B, T, H);
+  a.vt = static_cast<char*>(workspace) + stats_bytes(B, T, H_kv);
   a.LT = vt_cols(T);
-  a.B = B; a.T = T; a.H = H; a.D = D; a.window = window; a.eps = eps;
+  a.B = B; a.T = T; a.H = H; a.Hkv = H_kv; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_fwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             const void* dout, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, int B, int T, int H, int D, int window, int causal,
-             float eps, void* stream) {
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+             size_t workspace_bytes, int B, int T, int H, int D, int window, int causal, float eps,
+             void* stream) {
+  return attn_fwd_gqa(q, k, v, o, lse, workspace, workspace_bytes, B, T, H, H, D, window, causal,
+                      eps, stream);
+}
+
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window,
+                 int causal, float eps, void* stream) {
   bool empty;
-  int st = check_common(B, T, H, D, window, causal, eps, &empty);
+  int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
   const void* ins[6] = {q, k, v, o, lse, dout};
   void* outs[3] = {dq, dk, dv};
@@ -163,7 +181,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
       if (x == p) return ATTN_ERR_INVALID_ARG;
   }
   if (dq == dk || dq == dv || dk == dv) return ATTN_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, T, H, D)) return ATTN_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D))
+    return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
@@ -176,9 +195,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.kscale = reinterpret_cast<float*>(ws + qh_bytes);
   a.delta = reinterpret_cast<float*>(ws + qh_bytes + sb);
   a.lse2 = reinterpret_cast<float*>(ws + qh_bytes + 2 * sb);
-  a.B = B; a.T = T; a.H = H; a.D = D; a.window = window; a.eps = eps;
+  a.B = B; a.T = T; a.H = H; a.Hkv = H_kv; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_bwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int T, int H, int D, int window, int causal,
+             float eps, void* stream) {
+  return attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H, D,
+                      window, causal, eps, stream);
 }
 
 }  // extern "C"

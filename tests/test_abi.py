@@ -178,6 +178,51 @@ def test_workspace_checks():
     assert _bwd(wsb=need_b - 1) == _lib.ATTN_ERR_WORKSPACE
 
 
+def _fwd_gqa(H_kv, wsb=1 << 40, **kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3], lse=ALIGNED[4],
+             ws=ALIGNED[5], B=2, T=64, H=4, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], wsb,
+                                   a["B"], a["T"], a["H"], H_kv, a["D"], a["window"], a["causal"],
+                                   a["eps"], None)
+
+
+def _bwd_gqa(H_kv, wsb=1 << 40, **kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3], lse=ALIGNED[4],
+             do=ALIGNED[5], dq=ALIGNED[6], dk=ALIGNED[7], dv=ALIGNED[8], ws=ALIGNED[9],
+             B=2, T=64, H=4, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                   a["dk"], a["dv"], a["ws"], wsb, a["B"], a["T"], a["H"], H_kv,
+                                   a["D"], a["window"], a["causal"], a["eps"], None)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 0), (4, -1), (4, 3), (4, 8), (6, 4), (0, -1)])
+def test_gqa_invalid_head_counts(H, H_kv):
+    assert _fwd_gqa(H_kv, H=H) == _lib.ATTN_ERR_INVALID_ARG
+    assert _bwd_gqa(H_kv, H=H) == _lib.ATTN_ERR_INVALID_ARG
+
+
+def test_gqa_validation_and_workspace():
+    for H_kv in (1, 2, 4):
+        need_f = sw.fwd_workspace_bytes(2, 64, 4, 64, H_kv)
+        need_b = sw.bwd_workspace_bytes(2, 64, 4, 64, H_kv)
+        # key scales and V^T cover the H_kv key/value heads only
+        assert need_f >= 2 * H_kv * 64 * 4 + 2 * H_kv * 64 * 64 * 2
+        assert need_b >= 2 * 64 * 4 * 64 * 2 + 3 * 2 * 4 * 64 * 4
+        assert _fwd_gqa(H_kv, wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE
+        assert _bwd_gqa(H_kv, wsb=need_b - 1) == _lib.ATTN_ERR_WORKSPACE
+        assert _fwd_gqa(H_kv, q=None) == _lib.ATTN_ERR_INVALID_ARG
+        assert _bwd_gqa(H_kv, dk=P + 4) == _lib.ATTN_ERR_INVALID_ARG
+        assert _bwd_gqa(H_kv, dv=ALIGNED[6]) == _lib.ATTN_ERR_INVALID_ARG
+        assert _fwd_gqa(H_kv, D=96) == _lib.ATTN_ERR_UNSUPPORTED
+    assert sw.fwd_workspace_bytes(2, 64, 4, 64, 1) < sw.fwd_workspace_bytes(2, 64, 4, 64, 4)
+    assert sw.fwd_workspace_bytes(2, 64, 4, 64, 4) == sw.fwd_workspace_bytes(2, 64, 4, 64)
+    assert sw.bwd_workspace_bytes(2, 64, 4, 64, 4) == sw.bwd_workspace_bytes(2, 64, 4, 64)
+    nulls = dict(q=None, k=None, v=None, o=None, lse=None, ws=None)
+    assert _fwd_gqa(0, wsb=0, H=0, **nulls) == _lib.ATTN_OK
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(H=0)])
 def test_empty_problem_is_ok_and_touches_nothing(kw):
     nulls = dict(q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0)

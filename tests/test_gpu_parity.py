@@ -100,6 +100,81 @@ def test_small_full_parity(torch_dev, B, T, H, D, W, seed):
     _close("dv", _np(dv), rv)
 
 
+GQA_SMALL = [
+    # (B, T, H, H_kv, D, W, seed): grouped key/value heads
+    (1, 128, 4, 2, 64, 64, 40),
+    (1, 20, 4, 2, 128, 5, 41),     # one query block per key tile: every step changes query head
+    (2, 257, 4, 1, 128, 100, 42),
+    (1, 300, 6, 3, 128, -1, 43),
+    (2, 333, 4, 2, 64, 0, 44),
+    (1, 448, 8, 2, 128, 65, 45),
+    (1, 129, 2, 1, 64, 2000, 46),
+]
+
+
+@pytest.mark.parametrize("B,T,H,H_kv,D,W,seed", GQA_SMALL,
+                         ids=[f"B{c[0]}T{c[1]}H{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}" for c in GQA_SMALL])
+def test_gqa_small_full_parity(torch_dev, B, T, H, H_kv, D, W, seed):
+    _say(f"[parity] gqa B={B} T={T} H={H} H_kv={H_kv} D={D} W={W} seed={seed}")
+    inp = make_layer_inputs(B, T, H, D, seed, H_kv=H_kv)
+    qf, kf, vf, dof = inp.as_f32()
+    o, lse, dq, dk, dv = _run(torch_dev, inp, W)
+    assert tuple(dk.shape) == (B, T, H_kv, D) and tuple(dv.shape) == (B, T, H_kv, D)
+    ro, rl = oracle.attention_fwd(qf, kf, vf, W, True, EPS)
+    rq, rk, rv = oracle.attention_bwd(qf, kf, vf, dof, W, True, EPS)
+    _close("o", _np(o), ro)
+    _close("lse", _np(lse), rl)
+    _close("dq", _np(dq), rq)
+    _close("dk", _np(dk), rk)
+    _close("dv", _np(dv), rv)
+
+
+def test_gqa_entry_with_equal_heads_is_the_plain_entry(torch_dev):
+    """attn_fwd_gqa / attn_bwd_gqa with H_kv = H give bit-identical results to
+    attn_fwd / attn_bwd."""
+    import sliding_window_causal_qk_amd as sw
+    torch = torch_dev
+    B, T, H, D, W = 1, 200, 2, 128, 60
+    _say(f"[parity] gqa entry with H_kv = H, T={T}")
+    inp = make_layer_inputs(B, T, H, D, 47)
+    q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
+    L = sw.lib()
+    s = torch.cuda.current_stream().cuda_stream
+    outs = []
+    for gqa in (False, True):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        wf = torch.empty(sw.fwd_workspace_bytes(B, T, H, D, H), dtype=torch.uint8, device="cuda")
+        wb = torch.empty(sw.bwd_workspace_bytes(B, T, H, D, H), dtype=torch.uint8, device="cuda")
+        head = (H, H) if gqa else (H,)
+        f = L.attn_fwd_gqa if gqa else L.attn_fwd
+        bw = L.attn_bwd_gqa if gqa else L.attn_bwd
+        sw.check(f(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), wf.data_ptr(),
+                   wf.numel(), B, T, *head, D, W, 1, EPS, s), "fwd")
+        sw.check(bw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), wb.data_ptr(), wb.numel(), B, T, *head, D,
+                    W, 1, EPS, s), "bwd")
+        torch.cuda.synchronize()
+        outs.append((o, lse, dq, dk, dv))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+def test_gqa_autograd(torch_dev):
+    import sliding_window_causal_qk_amd as sw
+    torch = torch_dev
+    _say("[parity] gqa autograd wrapper")
+    inp = make_layer_inputs(1, 200, 4, 128, 48, H_kv=2)
+    q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
+    ref = _run(torch, inp, 50)
+    qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = sw.attention(qq, kk, vv, 50)
+    o.backward(do)
+    assert torch.equal(o.detach(), ref[0])
+    assert torch.equal(qq.grad, ref[2]) and torch.equal(kk.grad, ref[3]) and torch.equal(vv.grad, ref[4])
+
+
 def _sample_rows(T, W, rng, n=6):
     fixed = [0, 1, 63, 64, 127, 128, T // 2, T - 2, T - 1]
     if W >= 0:
@@ -109,7 +184,8 @@ def _sample_rows(T, W, rng, n=6):
 
 
 def _sampled_check(torch, wl, layer, window, slices):
-    inp = make_layer_inputs(wl.B, wl.T, wl.H, wl.D, wl.seed(layer), wl.sigma_qkv, wl.sigma_do)
+    inp = make_layer_inputs(wl.B, wl.T, wl.H, wl.D, wl.seed(layer), wl.sigma_qkv, wl.sigma_do,
+                            H_kv=wl.H_kv)
     qf, kf, vf, dof = inp.as_f32()
     o, lse, dq, dk, dv = _run(torch, inp, window, wl.eps)
     rng = np.random.default_rng(1234 + layer)
@@ -122,9 +198,10 @@ def _sampled_check(torch, wl, layer, window, slices):
         _close(f"lse[{b},{h}]", l_s, rl)
         keys = rows[:4] + rows[-3:]
         sq, sk, sv = oracle.bwd_rows(qf, kf, vf, dof, b, h, rows, keys, window, True, wl.eps)
+        hk = oracle.kv_head(h, wl.H, wl.kv_heads)   # dk, dv: the key/value head h reads
         _close(f"dq[{b},{h}]", _np(dq[b, rows, h]), sq)
-        _close(f"dk[{b},{h}]", _np(dk[b, keys, h]), sk)
-        _close(f"dv[{b},{h}]", _np(dv[b, keys, h]), sv)
+        _close(f"dk[{b},{hk}]", _np(dk[b, keys, hk]), sk)
+        _close(f"dv[{b},{hk}]", _np(dv[b, keys, hk]), sv)
     for name, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert bool(torch.isfinite(t).all()), f"{name} has non-finite values"
 
@@ -137,7 +214,8 @@ def test_single_layer_workloads_sampled(torch_dev, name):
     _sampled_check(torch_dev, wl, 0, wl.explicit_window, slices)
 
 
-@pytest.mark.parametrize("name,layer", [("sssl_stack", 0), ("sssl_stack", 3), ("long", 0), ("long", 3)])
+@pytest.mark.parametrize("name,layer", [("sssl_stack", 0), ("sssl_stack", 3), ("long", 0), ("long", 3),
+                                        ("gqa_sssl_stack", 0), ("gqa_sssl_stack", 3)])
 def test_stack_and_long_workloads_sampled(torch_dev, name, layer):
     import sliding_window_causal_qk_amd as sw
     wl = workload(name)

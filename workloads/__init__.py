@@ -56,13 +56,16 @@ class LayerInputs:
 
 
 def make_layer_inputs(B: int, T: int, H: int, D: int, seed: int,
-                      sigma_qkv: float = 1.0, sigma_do: float = 1.0) -> LayerInputs:
-    """Q, K, V then dO, drawn in that order from one default_rng(seed) stream."""
+                      sigma_qkv: float = 1.0, sigma_do: float = 1.0,
+                      H_kv: int | None = None) -> LayerInputs:
+    """Q, K, V then dO, drawn in that order from one default_rng(seed) stream.
+    Q and dO have H heads, K and V H_kv (default H)."""
     rng = np.random.default_rng(seed)
     shape = (B, T, H, D)
+    kv_shape = (B, T, H if H_kv is None else H_kv, D)
     q = gaussian_bf16(shape, rng, sigma_qkv)
-    k = gaussian_bf16(shape, rng, sigma_qkv)
-    v = gaussian_bf16(shape, rng, sigma_qkv)
+    k = gaussian_bf16(kv_shape, rng, sigma_qkv)
+    v = gaussian_bf16(kv_shape, rng, sigma_qkv)
     do = gaussian_bf16(shape, rng, sigma_do)
     return LayerInputs(q, k, v, do)
 
@@ -82,9 +85,14 @@ class Workload:
     explicit_window: int | None = None   # for the single-layer configs
     eps: float = EPS
     notes: str = ""
+    H_kv: int | None = None   # key/value heads (None: H, plain multi-head attention)
 
     def seed(self, layer: int) -> int:
         return self.seed0 + layer
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.H_kv is None else self.H_kv
 
 
 WORKLOADS: List[Workload] = [
@@ -100,6 +108,9 @@ WORKLOADS: List[Workload] = [
     Workload("long", B=4, T=8192, H=8, D=128, pattern="SSSL", n_layer=4, seed0=2000,
              sigma_qkv=2.0 ** 0.5,
              notes="one SSSL period at T=8192; Q/K/V variance 2, dO variance 1"),
+    Workload("gqa_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=3000,
+             H_kv=2,
+             notes="the SSSL stack with grouped key/value heads, n_kv_head = n_head / 2"),
 ]
 
 
@@ -111,7 +122,8 @@ def workload(name: str) -> Workload:
 
 
 def make_layer_inputs_device(B: int, T: int, H: int, D: int, seed: int,
-                             sigma_qkv: float = 1.0, sigma_do: float = 1.0, device="cuda"):
+                             sigma_qkv: float = 1.0, sigma_do: float = 1.0, device="cuda",
+                             H_kv: int | None = None):
     """Same recipe drawn on the GPU (torch's Philox stream, not numpy's): N(0, sigma^2)
     in fp32, rounded to bf16 (round to nearest even), Q, K, V then dO from one
     generator seeded with `seed`.  For timing runs, where only the distribution
@@ -120,9 +132,10 @@ def make_layer_inputs_device(B: int, T: int, H: int, D: int, seed: int,
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     shape = (B, T, H, D)
+    kv_shape = (B, T, H if H_kv is None else H_kv, D)
     out = []
-    for sigma in (sigma_qkv, sigma_qkv, sigma_qkv, sigma_do):
-        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    for sigma, shp in ((sigma_qkv, shape), (sigma_qkv, kv_shape), (sigma_qkv, kv_shape), (sigma_do, shape)):
+        x = torch.randn(shp, generator=g, device=device, dtype=torch.float32)
         if sigma != 1.0:
             x.mul_(sigma)
         out.append(x.to(torch.bfloat16))

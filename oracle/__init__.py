@@ -31,5 +31,9 @@ from .attention import (  # noqa: F401
     attention_bwd,
     fwd_rows,
     bwd_rows,
+    rope,
+    rope_bwd,
+    attention_fwd_rope,
+    attention_bwd_rope,
 )
 from .schedule import layer_windows, flops_per_token  # noqa: F401

@@ -33,6 +33,15 @@ What is computed (per batch b and head h; x[t] is the D-vector at position t):
   are then [B, T, H_kv, D]; a shared head's gradient is the sum over the G
   query heads that read it.
 
+  Rotary position embedding, optionally applied to q and k before the norm
+  ("Autoresearch 深度教程" §7.4: each head's D channels are split into the
+  halves x1 = x[:D/2], x2 = x[D/2:]; position t rotates every pair (x1_i, x2_i)
+  by the angle whose cosine and sine are cos[t, i], sin[t, i], tables held in
+  bf16; §7.3's attention module rotates q and k, then normalises them):
+      y1 = x1 * cos + x2 * sin,   y2 = x2 * cos - x1 * sin
+  The backward maps a gradient g of y back through the transpose:
+      dx1 = g1 * cos - g2 * sin,  dx2 = g1 * sin + g2 * cos
+
   Backward, given dO (chain rule through the three steps above):
       dV = P^T dO
       dP = dO V^T
@@ -89,6 +98,43 @@ def n_visible(T: int, window: int, causal: bool = True) -> int:
 
 def _slice(x: np.ndarray, b: int, h: int) -> np.ndarray:
     return _f64(x[b, :, h, :])
+
+
+def rope(x, cos, sin) -> np.ndarray:
+    """Rotary embedding of x [..., T, H, D] (or [T, D]) with tables cos, sin
+    [T, D/2]: position t rotates the pair (x[..., i], x[..., i + D/2]) by the
+    angle of (cos[t, i], sin[t, i])."""
+    x = _f64(x)
+    c, s = _f64(cos), _f64(sin)
+    if x.ndim == 4:
+        c, s = c[None, :, None, :], s[None, :, None, :]
+    h = x.shape[-1] // 2
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)
+
+
+def rope_bwd(g, cos, sin) -> np.ndarray:
+    """Gradient w.r.t. the input of rope, given the gradient g of its output."""
+    g = _f64(g)
+    c, s = _f64(cos), _f64(sin)
+    if g.ndim == 4:
+        c, s = c[None, :, None, :], s[None, :, None, :]
+    h = g.shape[-1] // 2
+    g1, g2 = g[..., :h], g[..., h:]
+    return np.concatenate([g1 * c - g2 * s, g1 * s + g2 * c], axis=-1)
+
+
+def attention_fwd_rope(q, k, v, cos, sin, window: int, causal: bool = True,
+                       eps: float = 1e-6) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward with rotary embedding of q and k before the norm."""
+    return attention_fwd(rope(q, cos, sin), rope(k, cos, sin), v, window, causal, eps)
+
+
+def attention_bwd_rope(q, k, v, do, cos, sin, window: int, causal: bool = True,
+                       eps: float = 1e-6):
+    """dq, dk (w.r.t. the q, k before rotation), dv of attention_fwd_rope."""
+    dq, dk, dv = attention_bwd(rope(q, cos, sin), rope(k, cos, sin), v, do, window, causal, eps)
+    return rope_bwd(dq, cos, sin), rope_bwd(dk, cos, sin), dv
 
 
 def kv_head(h: int, H: int, H_kv: int) -> int:

@@ -13,7 +13,8 @@ import types
 import numpy as np
 import pytest
 
-from tests.test_oracle_pins import _rand, _torch_reference, brute_force_fwd
+from tests.test_oracle_pins import (_rand, _torch_reference, _torch_rope_reference, bf16_round,
+                                    brute_force_fwd, rope_tables)
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "oracle", "attention.py")
@@ -49,6 +50,11 @@ MUTANTS = [
     ("gqa_heads_interleaved", "return h // (H // H_kv)", "return h % H_kv"),
     ("gqa_dk_last_head_only", "dk_hat[b, :, hk] += dkh", "dk_hat[b, :, hk] = dkh"),
     ("gqa_dv_last_head_only", "dv[b, :, hk] += dvh", "dv[b, :, hk] = dvh"),
+    ("rope_sign", "[x1 * c + x2 * s, x2 * c - x1 * s]", "[x1 * c - x2 * s, x2 * c + x1 * s]"),
+    ("rope_interleaved_pairs", "x1, x2 = x[..., :h], x[..., h:]", "x1, x2 = x[..., 0::2], x[..., 1::2]"),
+    ("rope_bwd_sign", "[g1 * c - g2 * s, g1 * s + g2 * c]", "[g1 * c + g2 * s, g2 * c - g1 * s]"),
+    ("rope_bwd_missing", "return rope_bwd(dq, cos, sin), rope_bwd(dk, cos, sin), dv",
+     "return dq, dk, dv"),
 ]
 
 
@@ -81,6 +87,15 @@ def _pins_pass(A) -> bool:
         k, v = (_rand((1, T, 2, D), s) for s in (23, 24))
         ref = _torch_reference(q, k, v, do, W, True, EPS)
         got = (A.attention_fwd(q, k, v, W, True, EPS)[0],) + tuple(A.attention_bwd(q, k, v, do, W, True, EPS))
+        if not all(a.shape == b.shape and np.allclose(a, b, rtol=1e-9, atol=1e-11) for a, b in zip(got, ref)):
+            return False
+        # library: complex-multiplication rotary embedding + fp64 SDPA, autograd
+        T, D, W = 14, 8, 5
+        q, k, v, do = (_rand((1, T, 2, D), s) for s in (25, 26, 27, 28))
+        c, s = (bf16_round(t) for t in rope_tables(T, D))
+        ref = _torch_rope_reference(q, k, v, do, c, s, W, EPS)
+        got = ((A.attention_fwd_rope(q, k, v, c, s, W, True, EPS)[0],)
+               + tuple(A.attention_bwd_rope(q, k, v, do, c, s, W, True, EPS)))
         if not all(a.shape == b.shape and np.allclose(a, b, rtol=1e-9, atol=1e-11) for a, b in zip(got, ref)):
             return False
         # closed form: identical keys

@@ -184,6 +184,121 @@ def test_gqa_rejects_uneven_groups():
         oracle.attention_fwd(q, k, k, 2, True, EPS)
 
 
+# ------------------------------------------------------- rotary embedding
+
+def rope_tables(T, D, base=10000.0, offset=0):
+    """Exact fp64 cos/sin tables: position t, pair i has angle t / base^(2i/D)."""
+    inv = 1.0 / base ** (np.arange(0, D, 2) / D)
+    ang = np.outer(np.arange(offset, offset + T), inv)
+    return np.cos(ang), np.sin(ang)
+
+
+def bf16_round(x):
+    """Round to bfloat16 (nearest even) and back to float64, via torch."""
+    torch = pytest.importorskip("torch")
+    return torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_rope_matches_complex_rotation():
+    """Each pair (x_i, x_{i+D/2}) as the complex number x_i + j x_{i+D/2},
+    multiplied by e^{-j theta}: the real part is the first half, the imaginary
+    part the second."""
+    T, H, D = 9, 2, 16
+    x = _rand((2, T, H, D), 60)
+    c, s = (bf16_round(t) for t in rope_tables(T, D))
+    z = (x[..., :D // 2] + 1j * x[..., D // 2:]) * (c - 1j * s)[None, :, None, :]
+    y = oracle.rope(x, c, s)
+    np.testing.assert_allclose(y[..., :D // 2], z.real, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(y[..., D // 2:], z.imag, rtol=0, atol=1e-14)
+    e = np.zeros((1, T, 1, D))
+    e[..., 3] = 1.0
+    y = oracle.rope(e, c, s)
+    np.testing.assert_array_equal(y[0, :, 0, 3], c[:, 3])
+    np.testing.assert_array_equal(y[0, :, 0, 3 + D // 2], -s[:, 3])
+
+
+def test_rope_exact_tables_are_rotations():
+    T, D = 12, 8
+    x = _rand((1, T, 3, D), 61)
+    c, s = rope_tables(T, D)
+    y = oracle.rope(x, c, s)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14)
+    np.testing.assert_allclose(oracle.rope_bwd(y, c, s), x, rtol=0, atol=1e-14)   # R^T R = I
+
+
+def test_rope_attention_depends_on_relative_position():
+    """With exact tables, shifting every position by the same amount leaves
+    the attention output unchanged: scores see only i - j."""
+    T, D, W = 24, 16, 7
+    q, k, v = (_rand((1, T, 2, D), s) for s in (62, 63, 64))
+    c0, s0 = rope_tables(T, D)
+    c1, s1 = rope_tables(T, D, offset=37)
+    o0, l0 = oracle.attention_fwd_rope(q, k, v, c0, s0, W, True, EPS)
+    o1, l1 = oracle.attention_fwd_rope(q, k, v, c1, s1, W, True, EPS)
+    np.testing.assert_allclose(o0, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l0, l1, rtol=0, atol=1e-12)
+    o2, _ = oracle.attention_fwd(q, k, v, W, True, EPS)
+    assert np.max(np.abs(o0 - o2)) > 1e-3      # the rotation does change the result
+
+
+def _torch_rope_reference(q, k, v, do, c, s, window, eps):
+    """torch autograd through a complex-multiplication rotary embedding,
+    rms_norm and SDPA with a band mask (fp64, CPU)."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    B, T, H, D = q.shape
+    h = D // 2
+    rot = torch.complex(torch.tensor(c), -torch.tensor(s))[None, :, None, :]
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+
+    def rotate(x):
+        z = torch.complex(x[..., :h], x[..., h:]) * rot
+        return torch.cat([z.real, z.imag], dim=-1)
+    qn = F.rms_norm(rotate(qt), (D,), eps=eps).transpose(1, 2)
+    kn = F.rms_norm(rotate(kt), (D,), eps=eps).transpose(1, 2)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    mask = (j <= i) & ((i - j <= window) if window >= 0 else torch.ones(T, T, dtype=torch.bool))
+    o = F.scaled_dot_product_attention(qn, kn, vt.transpose(1, 2), attn_mask=mask,
+                                       enable_gqa=k.shape[2] != H).transpose(1, 2)
+    o.backward(torch.tensor(do))
+    return o.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("H,H_kv,T,D,W", [(2, 2, 30, 16, 6), (4, 2, 33, 8, -1), (2, 1, 20, 16, 0)])
+def test_rope_fwd_bwd_match_torch(H, H_kv, T, D, W):
+    q, do = (_rand((2, T, H, D), s) for s in (65, 66))
+    k, v = (_rand((2, T, H_kv, D), s) for s in (67, 68))
+    c, s = (bf16_round(t) for t in rope_tables(T, D))
+    ref = _torch_rope_reference(q, k, v, do, c, s, W, EPS)
+    o, _ = oracle.attention_fwd_rope(q, k, v, c, s, W, True, EPS)
+    got = (o,) + tuple(oracle.attention_bwd_rope(q, k, v, do, c, s, W, True, EPS))
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_rope_bwd_matches_finite_differences():
+    T, D, W = 10, 8, 4
+    q, k, v, do = (_rand((1, T, 1, D), s) for s in (69, 70, 71, 72))
+    c, s = (bf16_round(t) for t in rope_tables(T, D))
+    dq, dk, dv = oracle.attention_bwd_rope(q, k, v, do, c, s, W, True, EPS)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(oracle.attention_fwd_rope(qq, kk, vv, c, s, W, True, EPS)[0] * do))
+
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.max(np.abs(num - grad)) / np.max(np.abs(grad))
+        assert err < 1e-7, (which, err)
+
+
 # -------------------------------------------------------- finite differences
 
 @pytest.mark.parametrize("W,causal", [(5, True), (-1, True), (3, False)])

@@ -55,18 +55,20 @@ def kernel_sources_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None):
+def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None, rope=False):
     """(amount, unit) of algorithmic work of one launch of kernel `kid`
-    (H query heads, H_kv key/value heads)."""
+    (H query heads, H_kv key/value heads; rope: the pre-passes also read the
+    two bf16 [T, D/2] tables and write the rotated keys)."""
     H_kv = H if H_kv is None else H_kv
     E_kv = B * T * H_kv * D
     if kid in FLOPS_PER_PAIR_D:
         return FLOPS_PER_PAIR_D[kid] * D * n_vis * B * H, "flop"
+    extra = (2 * E_kv + 2 * T * D) if rope else 0
     if kid == 0:   # read K and V, write the key scales and V^T (rows padded to a multiple of 64)
         LT = (T + 63) // 64 * 64
-        return 2 * E_kv + 2 * E_kv + 4 * B * H_kv * T + 2 * B * H_kv * D * LT, "byte"
+        return 2 * E_kv + 2 * E_kv + 4 * B * H_kv * T + 2 * B * H_kv * D * LT + extra, "byte"
     # bwd_kscale: read K, write the key scales
-    return 2 * E_kv + 4 * B * H_kv * T, "byte"
+    return 2 * E_kv + 4 * B * H_kv * T + extra, "byte"
 
 
 def cpu_baseline(wl, windows, budget_s):
@@ -128,7 +130,7 @@ def main():
 
     import torch
     import sliding_window_causal_qk_amd as sw
-    from workloads import make_layer_inputs_device, workload
+    from workloads import make_layer_inputs_device, rope_tables_bf16, workload
 
     wl = workload(args.workload)
     B, T, H, D, H_kv = wl.B, wl.T, wl.H, wl.D, wl.kv_heads
@@ -152,6 +154,12 @@ def main():
         print(f"[bench] copy calibration: 2 launches of {args.copy_calibration_mib} MiB read + "
               f"{args.copy_calibration_mib} MiB written", file=sys.stderr, flush=True)
 
+    rope = None
+    if wl.rope:
+        rope = tuple(torch.from_numpy(t.view("int16")).view(torch.bfloat16).to(dev)
+                     for t in rope_tables_bf16(T, D))
+    fws = sw.fwd_rope_workspace_bytes if wl.rope else sw.fwd_workspace_bytes
+    bws = sw.bwd_rope_workspace_bytes if wl.rope else sw.bwd_workspace_bytes
     layers = []
     for l, W in enumerate(windows):
         q, k, v, do = make_layer_inputs_device(B, T, H, D, wl.seed(l), wl.sigma_qkv, wl.sigma_do, dev,
@@ -160,8 +168,8 @@ def main():
             W=W, q=q, k=k, v=v, do=do,
             o=torch.empty_like(q), lse=torch.empty((B, H, T), dtype=torch.float32, device=dev),
             dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-            wsf=torch.empty(sw.fwd_workspace_bytes(B, T, H, D, H_kv), dtype=torch.uint8, device=dev),
-            wsb=torch.empty(sw.bwd_workspace_bytes(B, T, H, D, H_kv), dtype=torch.uint8, device=dev),
+            wsf=torch.empty(fws(B, T, H, D, H_kv), dtype=torch.uint8, device=dev),
+            wsb=torch.empty(bws(B, T, H, D, H_kv), dtype=torch.uint8, device=dev),
             n_vis=sw.visible_pairs(T, W),
         ))
     torch.cuda.synchronize()
@@ -171,10 +179,10 @@ def main():
     def step():
         for L in layers:
             sw.attn_fwd(L["q"], L["k"], L["v"], L["W"], True, wl.eps,
-                        out=L["o"], lse=L["lse"], workspace=L["wsf"], stream=stream)
+                        out=L["o"], lse=L["lse"], workspace=L["wsf"], stream=stream, rope=rope)
         for L in reversed(layers):
             sw.attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], L["W"], True, wl.eps,
-                        dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["wsb"], stream=stream)
+                        dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["wsb"], stream=stream, rope=rope)
 
     for _ in range(args.warmup):
         step()
@@ -203,7 +211,7 @@ def main():
         work = 0.0
         unit = None
         for L in layers:
-            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"], H_kv)
+            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"], H_kv, wl.rope)
             work += amt * args.steps
         secs = tot.value * 1e-3
         if unit == "flop":
@@ -255,7 +263,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "H_kv": H_kv, "D": D,
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "H_kv": H_kv, "D": D, "rope": wl.rope,
                    "pattern": wl.pattern,
                    "n_layer": len(windows), "windows": windows, "eps": wl.eps,
                    "flop_convention": "F14 = 14*D*N_vis per (batch, head, layer)",

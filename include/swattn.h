@@ -161,6 +161,36 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
                  void* stream);
 
 /*
+ * Rotary position embedding fused into the QK-norm prologue ("Autoresearch
+ * 深度教程" §7.4 defines the rotation and its bf16 cos/sin tables; §7.3's
+ * attention module rotates q and k and then normalises them).  q and k are the
+ * projections BEFORE the rotation.  The operation is attn_fwd_gqa applied to
+ * rope(q) and rope(k), where for position t and channel i < D/2
+ *   rope(x)[i]       = x[i] cos[t, i] + x[i + D/2] sin[t, i]
+ *   rope(x)[i + D/2] = x[i + D/2] cos[t, i] - x[i] sin[t, i]
+ * (the same tables for q and k), and attn_bwd_rope returns dq and dk with
+ * respect to the q and k before the rotation.
+ * rope_cos, rope_sin: bf16 [T, D/2] device tables, row t for position t (for
+ * example the first T rows of a model's precomputed [1, T', 1, D/2] buffers),
+ * 16-byte aligned, read only; they must not alias an output.  All other rules
+ * are those of the *_gqa entry points; the workspace adds a bf16 copy of the
+ * rotated keys: *_rope_workspace_bytes.
+ */
+size_t attn_fwd_rope_workspace_bytes(int B, int T, int H, int H_kv, int D);
+int attn_fwd_rope(const void* q, const void* k, const void* v,
+                  const void* rope_cos, const void* rope_sin, void* o, float* lse,
+                  void* workspace, size_t workspace_bytes,
+                  int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                  void* stream);
+size_t attn_bwd_rope_workspace_bytes(int B, int T, int H, int H_kv, int D);
+int attn_bwd_rope(const void* q, const void* k, const void* v,
+                  const void* rope_cos, const void* rope_sin,
+                  const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                  int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                  void* stream);
+
+/*
  * Opt-in per-kernel timing, a measurement aid (not part of the operation).
  * While enabled, every kernel launch of attn_fwd / attn_bwd is bracketed by
  * two HIP events recorded on the launch stream.  Kernel ids: 0 fwd_prep

@@ -11,6 +11,8 @@ memory and the current stream.
 q: bf16 CUDA tensor [B, T, H, D] (contiguous), D in {64, 128}; k, v: bf16
 [B, T, H_kv, D] with H_kv dividing H (grouped key/value heads: query head h
 reads key/value head h // (H // H_kv); H_kv = H is plain multi-head attention).
+rope=(cos, sin): bf16 [T, D/2] tables; q and k are then the projections before
+the rotary embedding, which the kernels apply ahead of the norm.
 """
 from __future__ import annotations
 
@@ -24,7 +26,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "attention", "attn_fwd", "attn_bwd", "layer_windows", "visible_pairs", "band_tiles",
-    "fwd_workspace_bytes", "bwd_workspace_bytes", "SwattnError",
+    "fwd_workspace_bytes", "bwd_workspace_bytes", "fwd_rope_workspace_bytes",
+    "bwd_rope_workspace_bytes", "SwattnError",
 ]
 
 
@@ -61,6 +64,23 @@ def bwd_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int] = No
     return int(lib().attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D))
 
 
+def fwd_rope_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int] = None) -> int:
+    return int(lib().attn_fwd_rope_workspace_bytes(B, T, H, H if H_kv is None else H_kv, D))
+
+
+def bwd_rope_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int] = None) -> int:
+    return int(lib().attn_bwd_rope_workspace_bytes(B, T, H, H if H_kv is None else H_kv, D))
+
+
+def _check_rope(rope, T, D):
+    torch = _torch()
+    if not (isinstance(rope, (tuple, list)) and len(rope) == 2):
+        raise ValueError("rope must be a (cos, sin) pair of tensors")
+    for n, t in zip(("rope cos", "rope sin"), rope):
+        _check_tensor(t, n, (T, D // 2), torch.bfloat16)
+    return rope
+
+
 def _torch():
     import torch
     return torch
@@ -91,7 +111,7 @@ def _stream(stream) -> Optional[int]:
 
 
 def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
-             out=None, lse=None, workspace=None, stream=None) -> Tuple["object", "object"]:
+             out=None, lse=None, workspace=None, stream=None, rope=None) -> Tuple["object", "object"]:
     """Forward through the C ABI.  Returns (o bf16 [B,T,H,D], lse fp32 [B,H,T])."""
     torch = _torch()
     B, T, H, D = q.shape
@@ -103,6 +123,15 @@ def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
     l = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor(o, "out", (B, T, H, D), torch.bfloat16)
     _check_tensor(l, "lse", (B, H, T), torch.float32)
+    if rope is not None:
+        rc, rs = _check_rope(rope, T, D)
+        nbytes = fwd_rope_workspace_bytes(B, T, H, D, H_kv)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+        st = lib().attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(rc), _ptr(rs), _ptr(o), _ptr(l),
+                                 ws.data_ptr(), ws.numel(), B, T, H, H_kv, D, int(window),
+                                 int(bool(causal)), float(eps), _stream(stream))
+        check(st, "attn_fwd_rope")
+        return o, l
     nbytes = fwd_workspace_bytes(B, T, H, D, H_kv)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
     if H_kv == H:
@@ -117,7 +146,7 @@ def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
 
 
 def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float = 1e-6, *,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
+             dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None):
     """Backward through the C ABI.  Returns (dq, dk, dv): bf16, dq [B,T,H,D],
     dk and dv shaped like k and v."""
     torch = _torch()
@@ -134,6 +163,16 @@ def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float
     _check_tensor(dq, "dq", (B, T, H, D), torch.bfloat16)
     for n, t in (("dk", dk), ("dv", dv)):
         _check_tensor(t, n, (B, T, H_kv, D), torch.bfloat16)
+    if rope is not None:
+        rc, rs = _check_rope(rope, T, D)
+        nbytes = bwd_rope_workspace_bytes(B, T, H, D, H_kv)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+        st = lib().attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(rc), _ptr(rs), _ptr(o), _ptr(lse),
+                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(),
+                                 B, T, H, H_kv, D, int(window), int(bool(causal)), float(eps),
+                                 _stream(stream))
+        check(st, "attn_bwd_rope")
+        return dq, dk, dv
     nbytes = bwd_workspace_bytes(B, T, H, D, H_kv)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
     if H_kv == H:
@@ -154,18 +193,19 @@ def _make_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, window, causal, eps):
-            o, lse = attn_fwd(q, k, v, window, causal, eps)
+        def forward(ctx, q, k, v, window, causal, eps, rope_cos, rope_sin):
+            rope = None if rope_cos is None else (rope_cos, rope_sin)
+            o, lse = attn_fwd(q, k, v, window, causal, eps, rope=rope)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.cfg = (window, causal, eps)
+            ctx.cfg = (window, causal, eps, rope)
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            window, causal, eps = ctx.cfg
-            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), window, causal, eps)
-            return dq, dk, dv, None, None, None
+            window, causal, eps, rope = ctx.cfg
+            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), window, causal, eps, rope=rope)
+            return dq, dk, dv, None, None, None, None, None
 
     return _Attention
 
@@ -173,9 +213,12 @@ def _make_function():
 _fn = None
 
 
-def attention(q, k, v, window: int, causal: bool = True, eps: float = 1e-6):
-    """Autograd-aware QK-RMSNorm causal sliding-window attention (HIP kernels)."""
+def attention(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, rope=None):
+    """Autograd-aware QK-RMSNorm causal sliding-window attention (HIP kernels).
+    rope=(cos, sin) applies the rotary embedding to q and k before the norm;
+    the tables get no gradient."""
     global _fn
     if _fn is None:
         _fn = _make_function()
-    return _fn.apply(q, k, v, window, causal, eps)
+    rc, rs = (None, None) if rope is None else rope
+    return _fn.apply(q, k, v, window, causal, eps, rc, rs)

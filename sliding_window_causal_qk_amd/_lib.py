@@ -19,7 +19,8 @@ EXPORTS = (
     "attn_status_string", "attn_version", "attn_layer_windows", "attn_visible_pairs",
     "attn_band_tiles", "attn_fwd_workspace_bytes", "attn_fwd", "attn_bwd_workspace_bytes",
     "attn_bwd", "attn_fwd_gqa_workspace_bytes", "attn_fwd_gqa", "attn_bwd_gqa_workspace_bytes",
-    "attn_bwd_gqa", "attn_profile_enable", "attn_profile_read", "attn_kernel_name",
+    "attn_bwd_gqa", "attn_fwd_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope_workspace_bytes",
+    "attn_bwd_rope", "attn_profile_enable", "attn_profile_read", "attn_kernel_name",
 )
 
 
@@ -72,6 +73,13 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_gqa.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size,
                                c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_vp]
     L.attn_bwd_gqa.restype = c_int
+    for f in (L.attn_fwd_rope_workspace_bytes, L.attn_bwd_rope_workspace_bytes):
+        f.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        f.restype = c_size
+    L.attn_fwd_rope.argtypes = [c_vp] * 7 + [c_vp, c_size] + [c_int] * 7 + [c_float, c_vp]
+    L.attn_fwd_rope.restype = c_int
+    L.attn_bwd_rope.argtypes = [c_vp] * 11 + [c_vp, c_size] + [c_int] * 7 + [c_float, c_vp]
+    L.attn_bwd_rope.restype = c_int
     L.attn_profile_enable.argtypes = [c_int]
     L.attn_profile_enable.restype = c_int
     L.attn_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_double),

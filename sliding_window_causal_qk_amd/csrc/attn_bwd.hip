@@ -13,7 +13,9 @@
 //        "Autoresearch 深度教程" §7.3 place on q and k before the product)
 // With grouped key/value heads (G = H / H_kv query heads read one key/value
 // head, "Autoresearch 深度教程" §7.3), dk and dv of a shared head sum the
-// contributions of its G query heads.
+// contributions of its G query heads.  With the rotary embedding (§7.4) the
+// norm's input is the rotated q or k, and dq, dk go back through the
+// transposed rotation.
 //
 // Kernels, in launch order:
 //   bwd_kscale: kscale = log2(e) / sqrt(D) / rms(k) for every key.
@@ -39,9 +41,14 @@ namespace swattn {
 // kscale[b, h, t] = log2(e) / sqrt(D) * r(k[b, t, h, :]) for the backward
 // kernels.  D / 8 lanes share one key row (16 bytes each); a thread handles
 // KR rows 256 / (D / 8) apart, so each has KR loads in flight.
-template <int D>
+// ROPE: the rows are rotated first (a lane's rotation partner is the lane
+// D / 16 away) and written to kr, the K of the backward kernels.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void bwd_kscale_kernel(const uint16_t* __restrict__ k,
-                                                         float* __restrict__ kscale, int nrows,
+                                                         const uint16_t* __restrict__ rcos,
+                                                         const uint16_t* __restrict__ rsin,
+                                                         float* __restrict__ kscale,
+                                                         uint16_t* __restrict__ kr, int nrows,
                                                          int T, int H, float eps) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;     // rows per block pass
@@ -54,6 +61,25 @@ __global__ __launch_bounds__(256) void bwd_kscale_kernel(const uint16_t* __restr
   u32x4 kv[KR];
 #pragma unroll
   for (int i = 0; i < KR; ++i) kv[i] = bload16(rk, ((threadIdx.x / LPR + RPB * i) * D + part * 8) * 2);
+  if constexpr (ROPE) {
+    const rsrc_t rc = make_rsrc(rcos, (long long)T * D), rn = make_rsrc(rsin, (long long)T * D);
+    const rsrc_t rkr = make_rsrc(kr + (size_t)rb * D, (long long)(nrows - rb) * D * 2);
+    const bool second = part >= LPR / 2;   // this lane holds second-half channels
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int t = ((row0 + RPB * i) / H) % T;
+      const int off = (t * (D / 2) + 8 * (part % (LPR / 2))) * 2;
+      u32x4 other;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) other[e] = __shfl_xor(kv[i][e], LPR / 2);
+      float y1[8], y2[8];
+      rope8(second ? other : kv[i], second ? kv[i] : other, bload16(rc, off), bload16(rn, off), y1, y2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        kv[i][e] = second ? pack_bf16(y2[2 * e], y2[2 * e + 1]) : pack_bf16(y1[2 * e], y1[2 * e + 1]);
+      bstore16(kv[i], rkr, ((threadIdx.x / LPR + RPB * i) * D + part * 8) * 2);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < KR; ++i) {
     float ss = 0.f;
@@ -105,7 +131,7 @@ __device__ __forceinline__ int tr_off(int lane, int P) {
 // XCD b % 8), so the tiles of one (batch, head) share that XCD's L2; inside a
 // range, round i gives workgroup s the tile i G8 + (s + 7 i) mod G8, which
 // rotates the light tiles of the causal tail through all workgroups.
-template <int D, bool GROUPED>
+template <int D, bool GROUPED, bool ROPE>
 struct DkdvCfg {
   static constexpr int BNK = 128;       // keys per tile (32 per wave)
   static constexpr int BMQ = 32;        // queries per step
@@ -114,8 +140,8 @@ struct DkdvCfg {
   static constexpr int NB = D / 32;
   static constexpr int P = D + 24;      // q_hat / dO row pitch (bf16): odd multiple of 16 bytes
   static constexpr int PK = D + 8;      // K / V row pitch in the prefetch region
-  using Tile = DmaTileV<BMQ * P / 8, 4, 1 + GROUPED>;
-  using KVTile = DmaTileV<BNK * PK / 8, 4, 1 + GROUPED>;
+  using Tile = DmaTileV<BMQ * P / 8, 4, 1 + GROUPED + 2 * ROPE>;
+  using KVTile = DmaTileV<BNK * PK / 8, 4, 1 + GROUPED + 2 * ROPE>;
   static constexpr int DO_B = Tile::BYTES;          // dO tile after the q_hat tile
   static constexpr int ST_B = 2 * Tile::BYTES;      // 4 x 256 B: spare, spare, lse2, Delta
   static constexpr int STAGE = ST_B + 1024;
@@ -129,15 +155,17 @@ struct DkdvCfg {
 };
 
 // GROUPED = false is the plain multi-head case, compiled with G = 1 so that the
-// walk over the query heads of a group folds away.
-template <int D, bool GROUPED>
+// walk over the query heads of a group folds away.  ROPE: k holds the rotated
+// keys, and dK goes back through the transposed rotation in the epilogue.
+template <int D, bool GROUPED, bool ROPE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qhat, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta,
-    const float* __restrict__ kscale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    const float* __restrict__ kscale, const uint16_t* __restrict__ rcos,
+    const uint16_t* __restrict__ rsin, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     int T, int H, int G_arg, int W, int nkt, int ntiles) {
-  using C = DkdvCfg<D, GROUPED>;
+  using C = DkdvCfg<D, GROUPED, ROPE>;
   const int G = GROUPED ? G_arg : 1;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -460,6 +488,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (; it < imin(base + full_hi, it_end); ++it) step_body(it + 1 - base, unmasked);
       for (; it < it_end; ++it) step_body(it + 1 - base, masked);
     }
+    // rotary tables of key kj for the epilogue: channels 32 n + 8 q4 + 4 g + e
+    // (n < NB / 2) pair with n + NB / 2; loaded during the last products
+    u32x2 tc[C::NB / 2][4], tsn[C::NB / 2][4];
+    if constexpr (ROPE) {
+      const long long tb = (long long)(T - kw0) * D;
+      const rsrc_t rc = make_rsrc(rcos + (size_t)kw0 * (D / 2), tb);
+      const rsrc_t rn = make_rsrc(rsin + (size_t)kw0 * (D / 2), tb);
+#pragma unroll
+      for (int n = 0; n < C::NB / 2; ++n)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int off = (c * (D / 2) + 32 * n + 8 * q4 + 4 * g) * 2;
+          tc[n][q4] = bload8(rc, off);
+          tsn[n][q4] = bload8(rn, off);
+        }
+    }
     issue_plan(pnext, b2);          // the next tile's block 1 (or later) into the free buffer
     pnext = plan_next();
     stage_c(b0);
@@ -497,6 +541,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     dot += __shfl_xor(dot, 32);
     const float mean = dot * (1.0f / D);
+    if constexpr (ROPE) {
+      // dk of the rotated key, then back through the rotation of key kj
+#pragma unroll
+      for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_dk[n][r] = rk * (acc_dk[n][r] - khat[n][r] * mean);
+#pragma unroll
+      for (int n = 0; n < C::NB / 2; ++n)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float g1[4], g2[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g1[e] = acc_dk[n][4 * q4 + e];
+            g2[e] = acc_dk[n + C::NB / 2][4 * q4 + e];
+          }
+          rope4_bwd(g1, g2, tc[n][q4], tsn[n][q4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc_dk[n][4 * q4 + e] = g1[e];
+            acc_dk[n + C::NB / 2][4 * q4 + e] = g2[e];
+          }
+        }
+    }
     // outputs leave through LDS so that every store writes whole rows: the
     // lane's values (key c, d = 32 n + 8 q4 + 4 g + e) go to a row-major
     // 32 x D block, then each lane stores 16-byte chunks of 4 rows per
@@ -515,7 +583,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            y[e] = pass == 0 ? rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean) : acc_dv[n][4 * q4 + e];
+            y[e] = pass == 1 ? acc_dv[n][4 * q4 + e]
+                   : ROPE ? acc_dk[n][4 * q4 + e]
+                          : rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean);
           st8(smem + slot + 2 * (c * C::OP + 32 * n + 8 * q4 + 4 * g),
               u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
         }
@@ -540,7 +610,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // As in the dK/dV kernel the loop issues A(i+1), C(i), then B(i+1).  The
 // kernel fits two waves per SIMD, so the hardware also overlaps two
 // workgroups' phases.
-template <int D>
+template <int D, bool ROPE>
 struct DqCfg {
   static constexpr int BM = 128;   // queries per workgroup (32 per wave)
   static constexpr int BN = 32;    // keys per step
@@ -548,7 +618,7 @@ struct DqCfg {
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
   static constexpr int P = D + 24;
-  using Tile = DmaTile<D, BN, P, 1>;
+  using Tile = DmaTile<D, BN, P, 1 + ROPE>;
   static constexpr int V_B = Tile::BYTES;          // V tile after the K tile
   static constexpr int ST_B = 2 * Tile::BYTES;     // kscale (256 B), 3 spare
   static constexpr int STAGE = ST_B + 1024;
@@ -556,14 +626,17 @@ struct DqCfg {
   static constexpr int NPS = 2 * Tile::NIW + 1;    // direct loads per wave per step
 };
 
-template <int D>
+// ROPE: k holds the rotated keys; the queries are rotated in the prologue and
+// dQ goes back through the transposed rotation in the epilogue.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ kscale, uint16_t* __restrict__ qhat, float* __restrict__ delta,
+    const float* __restrict__ kscale, const uint16_t* __restrict__ rcos,
+    const uint16_t* __restrict__ rsin, uint16_t* __restrict__ qhat, float* __restrict__ delta,
     float* __restrict__ lse2, uint16_t* __restrict__ dq, int T, int H, int G, int W, float eps) {
-  using C = DqCfg<D>;
+  using C = DqCfg<D, ROPE>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int nqt = (T + C::BM - 1) / C::BM;
@@ -600,27 +673,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const rsrc_t rqr = make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
     const rsrc_t rdo = make_rsrc(dout + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
     const rsrc_t ror = make_rsrc(o + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
-    float ss = 0.f, dd = 0.f;
+    float dd = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       qf[ks] = bload16(rqr, (c * rs + 16 * ks + 8 * g) * 2);
       df[ks] = bload16(rdo, (c * rs + 16 * ks + 8 * g) * 2);
       const u32x4 of = bload16(ror, (c * rs + 16 * ks + 8 * g) * 2);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = bf_lo(qf[ks][e]), bb = bf_hi(qf[ks][e]);
-        ss += a * a + bb * bb;
+      for (int e = 0; e < 4; ++e)
         dd += bf_lo(df[ks][e]) * bf_lo(of[e]) + bf_hi(df[ks][e]) * bf_hi(of[e]);
-      }
     }
-    ss += __shfl_xor(ss, 32);
     dd += __shfl_xor(dd, 32);
-    r_q = 1.0f / sqrtf(ss * (1.0f / D) + eps);
     dlt = dd;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qf[ks][e] = pack_bf16(bf_lo(qf[ks][e]) * r_q, bf_hi(qf[ks][e]) * r_q);
+    r_q = normalise_query<D, ROPE>(qf, rcos, rsin, qw0, c, g, T, eps);
     // q_hat rows leave through LDS (whole-row stores); the step buffers are
     // not in use yet
     const int slot = RS::BYTES * w;
@@ -771,11 +836,69 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   // buffers, free once every wave is past its last product), so global memory
   // sees whole rows.
   const float r = r_q;
+  // rotary tables of query qi (channels 32 n + 8 q4 + 4 g + e, n < NB / 2,
+  // pair with n + NB / 2), in flight with the reload of the q rows
+  u32x2 tc[C::NB / 2][4], tsn[C::NB / 2][4];
+  if constexpr (ROPE) {
+    const long long tb = (long long)(T - qw0) * D;
+    const rsrc_t rc = make_rsrc(rcos + (size_t)qw0 * (D / 2), tb);
+    const rsrc_t rn = make_rsrc(rsin + (size_t)qw0 * (D / 2), tb);
+#pragma unroll
+    for (int n = 0; n < C::NB / 2; ++n)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int off = (c * (D / 2) + 32 * n + 8 * q4 + 4 * g) * 2;
+        tc[n][q4] = bload8(rc, off);
+        tsn[n][q4] = bload8(rn, off);
+      }
+  }
   __syncthreads();
   const int slot = RS::BYTES * w;
   RS::load_rows(smem, slot, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
   float dot = 0.f;
   f32x16 xh[C::NB];
+  if constexpr (ROPE) {
+    // the norm's input is the rotated q; the table entries serve the way back too
+#pragma unroll
+    for (int n = 0; n < C::NB / 2; ++n)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x2 q1 = RS::get(smem, slot, c, 32 * n + 8 * q4 + 4 * g);
+        const u32x2 q2 = RS::get(smem, slot, c, 32 * (n + C::NB / 2) + 8 * q4 + 4 * g);
+        float x1[4] = {bf_lo(q1[0]), bf_hi(q1[0]), bf_lo(q1[1]), bf_hi(q1[1])};
+        float x2[4] = {bf_lo(q2[0]), bf_hi(q2[0]), bf_lo(q2[1]), bf_hi(q2[1])};
+        rope4(x1, x2, tc[n][q4], tsn[n][q4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xh[n][4 * q4 + e] = x1[e] * r;
+          xh[n + C::NB / 2][4 * q4 + e] = x2[e] * r;
+        }
+      }
+#pragma unroll
+    for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[n][i] *= (1.0f / kLog2e);
+        dot += acc[n][i] * xh[n][i];
+      }
+    dot += __shfl_xor(dot, 32);
+    const float mean = dot * (1.0f / D);
+#pragma unroll
+    for (int n = 0; n < C::NB / 2; ++n)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float y1[4], y2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y1[e] = r * (acc[n][4 * q4 + e] - xh[n][4 * q4 + e] * mean);
+          y2[e] = r * (acc[n + C::NB / 2][4 * q4 + e] - xh[n + C::NB / 2][4 * q4 + e] * mean);
+        }
+        rope4_bwd(y1, y2, tc[n][q4], tsn[n][q4]);
+        RS::put(smem, slot, c, 32 * n + 8 * q4 + 4 * g, u32x2{pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3])});
+        RS::put(smem, slot, c, 32 * (n + C::NB / 2) + 8 * q4 + 4 * g,
+                u32x2{pack_bf16(y2[0], y2[1]), pack_bf16(y2[2], y2[3])});
+      }
+  } else {
 #pragma unroll
   for (int n = 0; n < C::NB; ++n)
 #pragma unroll
@@ -800,46 +923,54 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       for (int e = 0; e < 4; ++e) y[e] = r * (acc[n][4 * q4 + e] - xh[n][4 * q4 + e] * mean);
       RS::put(smem, slot, c, 32 * n + 8 * q4 + 4 * g, u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
     }
+  }
   RS::store_rows(smem, slot, make_rsrc(dq + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
 }
 
-template <int D>
+template <int D, bool GROUPED, bool ROPE>
+static hipError_t set_dkdv_lds() {
+  using C = DkdvCfg<D, GROUPED, ROPE>;
+  // more than 64 KiB of dynamic LDS must be opted into, once per kernel
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(bwd_dkdv_kernel<D, GROUPED, ROPE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  return attr;
+}
+
+template <int D, bool ROPE>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const int G = a.H / a.Hkv;
   const int nrows = a.B * a.T * a.Hkv;
   const int nblk_p = (int)(((long long)nrows * (D / 8) + 4 * 256 - 1) / (4 * 256));
+  // with the rotary embedding, the backward kernels read the rotated keys
+  const uint16_t* kk = (const uint16_t*)(ROPE ? a.kr : a.k);
   ProfToken t0 = prof_begin(K_BWD_KSCALE, stream);
-  hipLaunchKernelGGL(bwd_kscale_kernel<D>, dim3(nblk_p), dim3(256), 0, stream,
-                     (const uint16_t*)a.k, a.kscale, nrows, a.T, a.Hkv, a.eps);
+  hipLaunchKernelGGL((bwd_kscale_kernel<D, ROPE>), dim3(nblk_p), dim3(256), 0, stream,
+                     (const uint16_t*)a.k, (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, a.kscale,
+                     (uint16_t*)a.kr, nrows, a.T, a.Hkv, a.eps);
   prof_end(t0);
   const int W = eff_window(a.T, a.window);
   {
     // dQ first: it also writes q_hat, Delta and lse log2(e) for dK/dV
-    using C = DqCfg<D>;
+    using C = DqCfg<D, ROPE>;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_dq_kernel<D>),
+        reinterpret_cast<const void*>(bwd_dq_kernel<D, ROPE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int nqt = (a.T + C::BM - 1) / C::BM;
     ProfToken t2 = prof_begin(K_BWD_DQ, stream);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.o, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, (const float*)a.kscale,
-                       (uint16_t*)a.qhat, a.delta, a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, ROPE>), dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.o, kk, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, (const float*)a.kscale,
+                       (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.qhat, a.delta,
+                       a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps);
     prof_end(t2);
   }
   {
-    using C = DkdvCfg<D, false>;
-    static_assert(C::LDS_BYTES == DkdvCfg<D, true>::LDS_BYTES, "one LDS size for both versions");
-    // more than 64 KiB of dynamic LDS must be opted into, once per kernel
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_dkdv_kernel<D, false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    using C = DkdvCfg<D, false, ROPE>;
+    static_assert(C::LDS_BYTES == DkdvCfg<D, true, ROPE>::LDS_BYTES, "one LDS size for both versions");
+    const hipError_t attr = G == 1 ? set_dkdv_lds<D, false, ROPE>() : set_dkdv_lds<D, true, ROPE>();
     if (attr != hipSuccess) return attr;
-    static const hipError_t attr_g = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_dkdv_kernel<D, true>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (attr_g != hipSuccess) return attr_g;
     const int nkt = (a.T + C::BNK - 1) / C::BNK;
     const int ntiles = nkt * a.B * a.Hkv;
     int dev = 0, ncu = 0;
@@ -848,20 +979,21 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
       return hipErrorInvalidDevice;
     const int grid = imin(ncu, ntiles);   // persistent: one workgroup per CU
     ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
-    hipLaunchKernelGGL((G == 1 ? bwd_dkdv_kernel<D, false> : bwd_dkdv_kernel<D, true>), dim3(grid),
-                       dim3(256), C::LDS_BYTES, stream,
-                       (const uint16_t*)a.qhat, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (const float*)a.kscale, (uint16_t*)a.dk, (uint16_t*)a.dv, a.T, a.H, G, W,
-                       nkt, ntiles);
+    hipLaunchKernelGGL((G == 1 ? bwd_dkdv_kernel<D, false, ROPE> : bwd_dkdv_kernel<D, true, ROPE>),
+                       dim3(grid), dim3(256), C::LDS_BYTES, stream,
+                       (const uint16_t*)a.qhat, kk, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                       (const float*)a.lse2, (const float*)a.delta, (const float*)a.kscale,
+                       (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.dk,
+                       (uint16_t*)a.dv, a.T, a.H, G, W, nkt, ntiles);
     prof_end(t1);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  if (a.D == 128) return launch_bwd_d<128>(a, stream);
-  return launch_bwd_d<64>(a, stream);
+  const bool rope = a.rcos != nullptr;
+  if (a.D == 128) return rope ? launch_bwd_d<128, true>(a, stream) : launch_bwd_d<128, false>(a, stream);
+  return rope ? launch_bwd_d<64, true>(a, stream) : launch_bwd_d<64, false>(a, stream);
 }
 
 }  // namespace swattn

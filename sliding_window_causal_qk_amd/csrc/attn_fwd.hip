@@ -11,6 +11,9 @@
 //   o_i = softmax_j(s_ij) v,   lse_i = ln sum_j exp(s_ij)
 //   With grouped key/value heads (n_kv_head < n_head, "Autoresearch 深度教程"
 //   §7.3), query head h reads key/value head h / G, G = H / H_kv.
+//   With the rotary embedding (§7.4), q and k are rotated before the norm:
+//   channel pair (i, i + D/2) at position t turns by the angle of the bf16
+//   tables cos[t, i], sin[t, i].
 //
 // MI355X design:
 //  * QK-norm bounds every logit: |s_ij| <= |q_hat||k_hat|/sqrt(D) < sqrt(D).
@@ -52,11 +55,16 @@ namespace swattn {
 //       16 keys the columns are permuted by tpos16, so that the 8 keys one lane
 //       feeds to an MFMA k-step are one contiguous 16-byte chunk)
 // Columns of vt past T are written as zero.
-template <int D>
+// ROPE: the key rows are rotated first; the rotated rows (bf16) go to kr, the
+// K the attention kernel reads, and kscale is taken from them.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
+                                                       const uint16_t* __restrict__ rcos,
+                                                       const uint16_t* __restrict__ rsin,
                                                        float* __restrict__ kscale,
-                                                       uint16_t* __restrict__ vt, int T, int H,
+                                                       uint16_t* __restrict__ vt,
+                                                       uint16_t* __restrict__ kr, int T, int H,
                                                        int LT, float eps) {
   constexpr int KB = 64;                 // keys per workgroup
   constexpr int CH = D / 8;              // 16-byte chunks per row
@@ -76,21 +84,50 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(const uint16_t* __restric
   const rsrc_t rk = make_rsrc(k + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
   const rsrc_t rv = make_rsrc(v + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
 
-  // rows: thread -> key t0 + tid / TPR, chunks (tid % TPR) * CPT ...
+  // rows: thread -> key t0 + tid / TPR, CPT chunks: the first half of them
+  // first-half channels, the rest their rotation partners (the same split
+  // with and without ROPE, so that kscale sums in the same order)
   const int r = tid / TPR, part = tid % TPR;
-  float ss = 0.f;
+  auto chunk = [&](int i) {
+    return i < CPT / 2 ? part * (CPT / 2) + i : CH / 2 + part * (CPT / 2) + i - CPT / 2;
+  };
+  u32x4 kk[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int ch = part * CPT + i;
-    const u32x4 kk = bload16(rk, (r * rs + 8 * ch) * 2);
+    const int ch = chunk(i);
+    kk[i] = bload16(rk, (r * rs + 8 * ch) * 2);
     const u32x4 vv = bload16(rv, (r * rs + 8 * ch) * 2);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = bf_lo(kk[e]), bb = bf_hi(kk[e]);
-      ss += a * a + bb * bb;
-      vs[(r * LP + 8 * ch) / 2 + e] = vv[e];
-    }
+    for (int e = 0; e < 4; ++e) vs[(r * LP + 8 * ch) / 2 + e] = vv[e];
   }
+  if constexpr (ROPE) {
+    const long long tb = (long long)(T - t0) * D;   // table rows t0 .. T-1 (D / 2 bf16 each)
+    const rsrc_t rc = make_rsrc(rcos + (size_t)t0 * (D / 2), tb);
+    const rsrc_t rn = make_rsrc(rsin + (size_t)t0 * (D / 2), tb);
+    const rsrc_t rkr = make_rsrc(kr + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
+#pragma unroll
+    for (int i = 0; i < CPT / 2; ++i) {
+      const int ch = chunk(i);
+      const u32x4 c = bload16(rc, (r * (D / 2) + 8 * ch) * 2), sn = bload16(rn, (r * (D / 2) + 8 * ch) * 2);
+      float y1[8], y2[8];
+      rope8(kk[i], kk[i + CPT / 2], c, sn, y1, y2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kk[i][e] = pack_bf16(y1[2 * e], y1[2 * e + 1]);
+        kk[i + CPT / 2][e] = pack_bf16(y2[2 * e], y2[2 * e + 1]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) bstore16(kk[i], rkr, (r * rs + 8 * chunk(i)) * 2);
+  }
+  float ss = 0.f;   // of the keys the attention kernel multiplies (rotated, bf16)
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf_lo(kk[i][e]), bb = bf_hi(kk[i][e]);
+      ss += a * a + bb * bb;
+    }
 #pragma unroll
   for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
   if (part == 0 && t0 + r < T) {
@@ -129,7 +166,7 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(const uint16_t* __restric
 //   C(i): O^T += V^T P^T                       (V^T from the transposed copy)
 // The loop issues A(i+1), then C(i) interleaved with B(i+1).  Every MFMA
 // operand read from LDS is one conflict-free 16-byte read.
-template <int D>
+template <int D, bool ROPE>
 struct FwdCfg {
   static constexpr int BM = 128;   // queries per workgroup (32 per wave)
   static constexpr int BN = 32;    // keys per step
@@ -137,8 +174,8 @@ struct FwdCfg {
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
   static constexpr int PK = D + 8;                     // K row pitch (bf16): 16-byte reads conflict-free
-  using KTile = DmaTileV<BN * PK / 8>;
-  using VTile = DmaTileV<D * BN / 8>;                  // D rows of 64 bytes, xor-swizzled chunks
+  using KTile = DmaTileV<BN * PK / 8, 4, 8 + ROPE>;
+  using VTile = DmaTileV<D * BN / 8, 4, 8 + ROPE>;     // D rows of 64 bytes, xor-swizzled chunks
   static constexpr int V_B = KTile::BYTES;
   static constexpr int ST_B = V_B + VTile::BYTES;      // kscale (128 bytes used of 256)
   static constexpr int STAGE = ST_B + 256;
@@ -148,13 +185,16 @@ struct FwdCfg {
 // Chunk slot of logical chunk ch (0..3) in row r of a transposed 32-column tile.
 __device__ __forceinline__ int vt_slot(int r, int ch) { return ch ^ ((r >> 2) & 3); }
 
-template <int D>
+// ROPE: k is the rotated copy written by the pre-pass, and the queries are
+// rotated in the prologue.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const float* __restrict__ kscale,
+    const uint16_t* __restrict__ rcos, const uint16_t* __restrict__ rsin,
     uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int G, int LT, int W,
     float eps) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, ROPE>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int nqt = (T + C::BM - 1) / C::BM;
@@ -183,22 +223,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   u32x4 qf[C::KS];
   {
     const rsrc_t rq = make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
-    float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      qf[ks] = bload16(rq, (c * rs + 16 * ks + 8 * g) * 2);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = bf_lo(qf[ks][e]), bb = bf_hi(qf[ks][e]);
-        ss += a * a + bb * bb;
-      }
-    }
-    ss += __shfl_xor(ss, 32);
-    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qf[ks][e] = pack_bf16(bf_lo(qf[ks][e]) * r, bf_hi(qf[ks][e]) * r);
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = bload16(rq, (c * rs + 16 * ks + 8 * g) * 2);
+    normalise_query<D, ROPE>(qf, rcos, rsin, qw0, c, g, T, eps);
   }
 
   f32x16 acc[C::NB];
@@ -360,13 +387,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   }
 }
 
-template <int D>
+template <int D, bool ROPE>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, ROPE>;
   const int nkb = a.LT / 64;
   ProfToken t0 = prof_begin(K_FWD_PREP, stream);
-  hipLaunchKernelGGL(fwd_prep_kernel<D>, dim3(nkb * a.B * a.Hkv), dim3(256), 0, stream,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.kscale, (uint16_t*)a.vt, a.T,
+  hipLaunchKernelGGL((fwd_prep_kernel<D, ROPE>), dim3(nkb * a.B * a.Hkv), dim3(256), 0, stream,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.rcos,
+                     (const uint16_t*)a.rsin, a.kscale, (uint16_t*)a.vt, (uint16_t*)a.kr, a.T,
                      a.Hkv, a.LT, a.eps);
   prof_end(t0);
   const int nqt = (a.T + C::BM - 1) / C::BM;
@@ -374,21 +402,22 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   const int W = eff_window(a.T, a.window);
   // more than 64 KiB of dynamic LDS must be opted into, once per kernel
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(attn_fwd_kernel<D>),
+      reinterpret_cast<const void*>(attn_fwd_kernel<D, ROPE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   ProfToken t1 = prof_begin(K_FWD, stream);
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(nblk), dim3(256), C::LDS_BYTES, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.vt,
-                     (const float*)a.kscale, (uint16_t*)a.o, a.lse, a.T, a.H, a.H / a.Hkv, a.LT, W,
-                     a.eps);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, ROPE>), dim3(nblk), dim3(256), C::LDS_BYTES, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)(ROPE ? a.kr : a.k), (const uint16_t*)a.vt,
+                     (const float*)a.kscale, (const uint16_t*)a.rcos, (const uint16_t*)a.rsin,
+                     (uint16_t*)a.o, a.lse, a.T, a.H, a.H / a.Hkv, a.LT, W, a.eps);
   prof_end(t1);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  if (a.D == 128) return launch_fwd_d<128>(a, stream);
-  return launch_fwd_d<64>(a, stream);
+  const bool rope = a.rcos != nullptr;
+  if (a.D == 128) return rope ? launch_fwd_d<128, true>(a, stream) : launch_fwd_d<128, false>(a, stream);
+  return rope ? launch_fwd_d<64, true>(a, stream) : launch_fwd_d<64, false>(a, stream);
 }
 
 }  // namespace swattn

@@ -77,6 +77,51 @@ __device__ __forceinline__ void bstore4f(float v, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, 0);
 }
 
+__device__ __forceinline__ void bstore16(u32x4 v, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
+
+// ---- rotary embedding.  A head's channels pair up as (i, i + D/2); position t
+// rotates pair i by the angle whose cosine and sine are the bf16 table entries
+// c = cos[t, i], s = sin[t, i]:  y1 = x1 c + x2 s,  y2 = x2 c - x1 s.  The
+// gradient goes back through the transpose:  g1' = g1 c - g2 s,
+// g2' = g1 s + g2 c.
+// rope8: x1, x2 are 8 channels (bf16 pairs) of the first and second half, c, s
+// the matching 8 table entries; the rotated channels come back in fp32.
+__device__ __forceinline__ void rope8(u32x4 x1, u32x4 x2, u32x4 c, u32x4 s, float* y1, float* y2) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a[2] = {bf_lo(x1[e]), bf_hi(x1[e])}, b[2] = {bf_lo(x2[e]), bf_hi(x2[e])};
+    const float cc[2] = {bf_lo(c[e]), bf_hi(c[e])}, ss[2] = {bf_lo(s[e]), bf_hi(s[e])};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      y1[2 * e + h] = a[h] * cc[h] + b[h] * ss[h];
+      y2[2 * e + h] = b[h] * cc[h] - a[h] * ss[h];
+    }
+  }
+}
+// rope4 / rope4_bwd: 4 fp32 channels of each half in place, tables as 4 bf16.
+__device__ __forceinline__ void rope4(float* x1, float* x2, u32x2 c, u32x2 s) {
+  const float cc[4] = {bf_lo(c[0]), bf_hi(c[0]), bf_lo(c[1]), bf_hi(c[1])};
+  const float ss[4] = {bf_lo(s[0]), bf_hi(s[0]), bf_lo(s[1]), bf_hi(s[1])};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = x1[e], b = x2[e];
+    x1[e] = a * cc[e] + b * ss[e];
+    x2[e] = b * cc[e] - a * ss[e];
+  }
+}
+__device__ __forceinline__ void rope4_bwd(float* g1, float* g2, u32x2 c, u32x2 s) {
+  const float cc[4] = {bf_lo(c[0]), bf_hi(c[0]), bf_lo(c[1]), bf_hi(c[1])};
+  const float ss[4] = {bf_lo(s[0]), bf_hi(s[0]), bf_lo(s[1]), bf_hi(s[1])};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = g1[e], b = g2[e];
+    g1[e] = a * cc[e] - b * ss[e];
+    g2[e] = a * ss[e] + b * cc[e];
+  }
+}
+
 // Wave-uniform value moved to a scalar register.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -241,5 +286,47 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // group, arranged so that the 8 values one lane feeds to an MFMA k-step are
 // contiguous: k-group 0 takes offsets {0..3, 8..11}, k-group 1 {4..7, 12..15}.
 __device__ __forceinline__ int tpos16(int x) { return ((x >> 2) & 1) * 8 + (x >> 3) * 4 + (x & 3); }
+
+// Query prologue shared by the forward and dQ kernels: lane (g, c) holds
+// channels 16 ks + 8 g + 0..7 (ks < D / 16) of query qw0 + c as bf16 pairs.
+// With ROPE they are rotated first (the partner of k-step ks is ks + D / 32,
+// channels + D / 2, in the same lane).  On return they hold q_hat = x r,
+// r = 1 / sqrt(mean x^2 + eps), as bf16; the function returns r.
+template <int D, bool ROPE>
+__device__ __forceinline__ float normalise_query(u32x4* qf, const uint16_t* rcos, const uint16_t* rsin,
+                                                 int qw0, int c, int g, int T, float eps) {
+  constexpr int KS = D / 16;
+  float x[KS][8];
+  if constexpr (ROPE) {
+    const long long tb = (long long)(T - qw0) * D;
+    const rsrc_t rc = make_rsrc(rcos + (size_t)qw0 * (D / 2), tb);
+    const rsrc_t rn = make_rsrc(rsin + (size_t)qw0 * (D / 2), tb);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      const int off = (c * (D / 2) + 16 * ks + 8 * g) * 2;
+      rope8(qf[ks], qf[ks + KS / 2], bload16(rc, off), bload16(rn, off), x[ks], x[ks + KS / 2]);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[ks][2 * e] = bf_lo(qf[ks][e]);
+        x[ks][2 * e + 1] = bf_hi(qf[ks][e]);
+      }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += x[ks][j] * x[ks][j];
+  ss += __shfl_xor(ss, 32);
+  const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qf[ks][e] = pack_bf16(x[ks][2 * e] * r, x[ks][2 * e + 1] * r);
+  return r;
+}
 
 }  // namespace swattn

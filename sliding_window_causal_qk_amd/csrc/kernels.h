@@ -16,6 +16,9 @@ struct FwdArgs {
   float* kscale;  // workspace: [B, Hkv, T]
   void* vt;       // workspace: bf16 [B, Hkv, D, LT], V transposed, keys permuted (tpos16)
   int LT;         // row length of vt: T rounded up to a multiple of 64
+  const void* rcos;  // bf16 [T, D/2] rotary tables, or null: no rotary embedding
+  const void* rsin;
+  void* kr;          // workspace (rotary only): bf16 [B, T, Hkv, D], the rotated keys
   int B, T, H, D;
   int Hkv;        // key/value heads (H is a multiple); q, o: H heads, k, v: Hkv
   int window;
@@ -37,6 +40,9 @@ struct BwdArgs {
   float* kscale;  // [B, Hkv, T]: log2(e) / sqrt(D) / rms(k)
   float* delta;   // [B, H, T]: rowsum(dO * O)
   float* lse2;    // [B, H, T]: lse * log2(e)
+  const void* rcos;  // bf16 [T, D/2] rotary tables, or null: no rotary embedding
+  const void* rsin;
+  void* kr;          // workspace (rotary only): bf16 [B, T, Hkv, D], the rotated keys
   int B, T, H, D;
   int Hkv;        // key/value heads (H is a multiple); k, v, dk, dv have Hkv heads
   int window;

@@ -122,6 +122,11 @@ size_t attn_fwd_workspace_bytes(int B, int T, int H, int D) {
   return attn_fwd_gqa_workspace_bytes(B, T, H, H, D);
 }
 
+size_t attn_fwd_rope_workspace_bytes(int B, int T, int H, int H_kv, int D) {
+  if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
+  return attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D) + round_up((size_t)B * T * H_kv * D * 2);
+}
+
 size_t attn_bwd_gqa_workspace_bytes(int B, int T, int H, int H_kv, int D) {
   if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
   return round_up((size_t)B * T * H * D * 2) + 3 * stats_bytes(B, T, H);
@@ -131,20 +136,32 @@ size_t attn_bwd_workspace_bytes(int B, int T, int H, int D) {
   return attn_bwd_gqa_workspace_bytes(B, T, H, H, D);
 }
 
-int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
-                 void* workspace, size_t workspace_bytes, int B, int T, int H, int H_kv, int D,
-                 int window, int causal, float eps, void* stream) {
+size_t attn_bwd_rope_workspace_bytes(int B, int T, int H, int H_kv, int D) {
+  if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
+  return attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D) + round_up((size_t)B * T * H_kv * D * 2);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Forward with or without the rotary embedding (rcos == nullptr: none).
+int fwd_impl(const void* q, const void* k, const void* v, const void* rcos, const void* rsin,
+             void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int T, int H,
+             int H_kv, int D, int window, int causal, float eps, void* stream, bool rope) {
   bool empty;
   int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
-  const void* ins[3] = {q, k, v};
-  for (const void* p : ins)
-    if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  const void* ins[5] = {q, k, v, rcos, rsin};
+  const int nin = rope ? 5 : 3;
+  for (int i = 0; i < nin; ++i)
+    if (!ins[i] || !aligned(ins[i], 16)) return ATTN_ERR_INVALID_ARG;
   if (!o || !lse || !aligned(o, 16) || !aligned(lse, 16)) return ATTN_ERR_INVALID_ARG;
-  for (const void* p : ins)
-    if (p == o || p == (const void*)lse) return ATTN_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D))
-    return ATTN_ERR_WORKSPACE;
+  for (int i = 0; i < nin; ++i)
+    if (ins[i] == o || ins[i] == (const void*)lse) return ATTN_ERR_INVALID_ARG;
+  const size_t need = rope ? attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D)
+                           : attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
 
   swattn::FwdArgs a;
@@ -152,37 +169,35 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
   a.kscale = static_cast<float*>(workspace);
   a.vt = static_cast<char*>(workspace) + stats_bytes(B, T, H_kv);
   a.LT = vt_cols(T);
+  a.rcos = rope ? rcos : nullptr;
+  a.rsin = rope ? rsin : nullptr;
+  a.kr = rope ? static_cast<char*>(workspace) + attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
   a.B = B; a.T = T; a.H = H; a.Hkv = H_kv; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_fwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-             size_t workspace_bytes, int B, int T, int H, int D, int window, int causal, float eps,
-             void* stream) {
-  return attn_fwd_gqa(q, k, v, o, lse, workspace, workspace_bytes, B, T, H, H, D, window, causal,
-                      eps, stream);
-}
-
-int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                 size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window,
-                 int causal, float eps, void* stream) {
+int bwd_impl(const void* q, const void* k, const void* v, const void* rcos, const void* rsin,
+             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, int B, int T, int H, int H_kv, int D,
+             int window, int causal, float eps, void* stream, bool rope) {
   bool empty;
   int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
-  const void* ins[6] = {q, k, v, o, lse, dout};
+  const void* ins[8] = {q, k, v, o, lse, dout, rcos, rsin};
+  const int nin = rope ? 8 : 6;
   void* outs[3] = {dq, dk, dv};
-  for (const void* p : ins)
-    if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < nin; ++i)
+    if (!ins[i] || !aligned(ins[i], 16)) return ATTN_ERR_INVALID_ARG;
   for (void* p : outs) {
     if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
-    for (const void* x : ins)
-      if (x == p) return ATTN_ERR_INVALID_ARG;
+    for (int i = 0; i < nin; ++i)
+      if (ins[i] == p) return ATTN_ERR_INVALID_ARG;
   }
   if (dq == dk || dq == dv || dk == dv) return ATTN_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D))
-    return ATTN_ERR_WORKSPACE;
+  const size_t need = rope ? attn_bwd_rope_workspace_bytes(B, T, H, H_kv, D)
+                           : attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
@@ -195,17 +210,63 @@ int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, con
   a.kscale = reinterpret_cast<float*>(ws + qh_bytes);
   a.delta = reinterpret_cast<float*>(ws + qh_bytes + sb);
   a.lse2 = reinterpret_cast<float*>(ws + qh_bytes + 2 * sb);
+  a.rcos = rope ? rcos : nullptr;
+  a.rsin = rope ? rsin : nullptr;
+  a.kr = rope ? ws + attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
   a.B = B; a.T = T; a.H = H; a.Hkv = H_kv; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_bwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes, int B, int T, int H, int H_kv, int D,
+                 int window, int causal, float eps, void* stream) {
+  return fwd_impl(q, k, v, nullptr, nullptr, o, lse, workspace, workspace_bytes, B, T, H, H_kv, D,
+                  window, causal, eps, stream, false);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+             size_t workspace_bytes, int B, int T, int H, int D, int window, int causal, float eps,
+             void* stream) {
+  return fwd_impl(q, k, v, nullptr, nullptr, o, lse, workspace, workspace_bytes, B, T, H, H, D,
+                  window, causal, eps, stream, false);
+}
+
+int attn_fwd_rope(const void* q, const void* k, const void* v, const void* rope_cos,
+                  const void* rope_sin, void* o, float* lse, void* workspace,
+                  size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window,
+                  int causal, float eps, void* stream) {
+  return fwd_impl(q, k, v, rope_cos, rope_sin, o, lse, workspace, workspace_bytes, B, T, H, H_kv,
+                  D, window, causal, eps, stream, true);
+}
+
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window,
+                 int causal, float eps, void* stream) {
+  return bwd_impl(q, k, v, nullptr, nullptr, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                  B, T, H, H_kv, D, window, causal, eps, stream, false);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, int B, int T, int H, int D, int window, int causal,
              float eps, void* stream) {
-  return attn_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H, D,
-                      window, causal, eps, stream);
+  return bwd_impl(q, k, v, nullptr, nullptr, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
+                  B, T, H, H, D, window, causal, eps, stream, false);
+}
+
+int attn_bwd_rope(const void* q, const void* k, const void* v, const void* rope_cos,
+                  const void* rope_sin, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                  int T, int H, int H_kv, int D, int window, int causal, float eps,
+                  void* stream) {
+  return bwd_impl(q, k, v, rope_cos, rope_sin, o, lse, dout, dq, dk, dv, workspace,
+                  workspace_bytes, B, T, H, H_kv, D, window, causal, eps, stream, true);
 }
 
 }  // extern "C"

@@ -223,6 +223,52 @@ def test_gqa_validation_and_workspace():
     assert _fwd_gqa(0, wsb=0, H=0, **nulls) == _lib.ATTN_OK
 
 
+def _fwd_rope(wsb=1 << 40, **kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], c=ALIGNED[10], s=ALIGNED[11], o=ALIGNED[3],
+             lse=ALIGNED[4], ws=ALIGNED[5], B=2, T=64, H=4, H_kv=2, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_fwd_rope(a["q"], a["k"], a["v"], a["c"], a["s"], a["o"], a["lse"], a["ws"],
+                                    wsb, a["B"], a["T"], a["H"], a["H_kv"], a["D"], a["window"],
+                                    a["causal"], a["eps"], None)
+
+
+def _bwd_rope(wsb=1 << 40, **kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], c=ALIGNED[10], s=ALIGNED[11], o=ALIGNED[3],
+             lse=ALIGNED[4], do=ALIGNED[5], dq=ALIGNED[6], dk=ALIGNED[7], dv=ALIGNED[8], ws=ALIGNED[9],
+             B=2, T=64, H=4, H_kv=2, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_bwd_rope(a["q"], a["k"], a["v"], a["c"], a["s"], a["o"], a["lse"], a["do"],
+                                    a["dq"], a["dk"], a["dv"], a["ws"], wsb, a["B"], a["T"], a["H"],
+                                    a["H_kv"], a["D"], a["window"], a["causal"], a["eps"], None)
+
+
+ROPE_INVALID = [dict(c=None), dict(s=None), dict(c=P + 8), dict(s=P + 2), dict(H_kv=3), dict(H_kv=0),
+                dict(window=-2), dict(eps=0.0), dict(q=None)]
+
+
+@pytest.mark.parametrize("kw", ROPE_INVALID, ids=[str(k) for k in ROPE_INVALID])
+def test_rope_invalid(kw):
+    assert _fwd_rope(**kw) == _lib.ATTN_ERR_INVALID_ARG
+    assert _bwd_rope(**kw) == _lib.ATTN_ERR_INVALID_ARG
+
+
+def test_rope_aliasing_workspace_unsupported():
+    assert _fwd_rope(o=ALIGNED[10]) == _lib.ATTN_ERR_INVALID_ARG       # output over the cos table
+    assert _bwd_rope(dk=ALIGNED[11]) == _lib.ATTN_ERR_INVALID_ARG      # output over the sin table
+    assert _fwd_rope(D=96) == _lib.ATTN_ERR_UNSUPPORTED
+    assert _bwd_rope(causal=0) == _lib.ATTN_ERR_UNSUPPORTED
+    need_f = sw.fwd_rope_workspace_bytes(2, 64, 4, 64, 2)
+    need_b = sw.bwd_rope_workspace_bytes(2, 64, 4, 64, 2)
+    # the rotated keys, bf16 [B, T, H_kv, D], come on top of the plain workspaces
+    assert need_f >= sw.fwd_workspace_bytes(2, 64, 4, 64, 2) + 2 * 64 * 2 * 64 * 2
+    assert need_b >= sw.bwd_workspace_bytes(2, 64, 4, 64, 2) + 2 * 64 * 2 * 64 * 2
+    assert _fwd_rope(wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE
+    assert _bwd_rope(wsb=need_b - 1) == _lib.ATTN_ERR_WORKSPACE
+    assert _fwd_rope(ws=P + 16) == _lib.ATTN_ERR_WORKSPACE
+    nulls = dict(q=None, k=None, v=None, c=None, s=None, o=None, lse=None, ws=None)
+    assert _fwd_rope(wsb=0, T=0, **nulls) == _lib.ATTN_OK
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(H=0)])
 def test_empty_problem_is_ok_and_touches_nothing(kw):
     nulls = dict(q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0)

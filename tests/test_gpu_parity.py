@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_layer_inputs, WORKLOADS, workload, bf16_bits_to_f32
+from workloads import make_layer_inputs, WORKLOADS, workload, bf16_bits_to_f32, rope_tables_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -175,6 +175,77 @@ def test_gqa_autograd(torch_dev):
     assert torch.equal(qq.grad, ref[2]) and torch.equal(kk.grad, ref[3]) and torch.equal(vv.grad, ref[4])
 
 
+ROPE_SMALL = [
+    # (B, T, H, H_kv, D, W, seed): rotary embedding ahead of the norm
+    (1, 128, 2, 2, 64, 64, 50),
+    (2, 257, 4, 2, 128, 100, 51),
+    (1, 300, 2, 1, 128, -1, 52),
+    (1, 20, 4, 2, 128, 5, 53),
+    (2, 333, 2, 2, 64, 0, 54),
+    (1, 448, 2, 2, 128, 65, 55),
+    (1, 1, 1, 1, 64, 0, 56),
+]
+
+
+def _run_rope(torch, inp, tables, window, eps=EPS):
+    import sliding_window_causal_qk_amd as sw
+    q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
+    rope = tuple(_to_dev(torch, t) for t in tables)
+    o, lse = sw.attn_fwd(q, k, v, window, True, eps, rope=rope)
+    dq, dk, dv = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps, rope=rope)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("B,T,H,H_kv,D,W,seed", ROPE_SMALL,
+                         ids=[f"B{c[0]}T{c[1]}H{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}" for c in ROPE_SMALL])
+def test_rope_small_full_parity(torch_dev, B, T, H, H_kv, D, W, seed):
+    _say(f"[parity] rope B={B} T={T} H={H} H_kv={H_kv} D={D} W={W} seed={seed}")
+    inp = make_layer_inputs(B, T, H, D, seed, H_kv=H_kv)
+    tables = rope_tables_bf16(T, D)
+    c, sn = (bf16_bits_to_f32(t) for t in tables)
+    qf, kf, vf, dof = inp.as_f32()
+    o, lse, dq, dk, dv = _run_rope(torch_dev, inp, tables, W)
+    ro, rl = oracle.attention_fwd_rope(qf, kf, vf, c, sn, W, True, EPS)
+    rq, rk, rv = oracle.attention_bwd_rope(qf, kf, vf, dof, c, sn, W, True, EPS)
+    _close("o", _np(o), ro)
+    _close("lse", _np(lse), rl)
+    _close("dq", _np(dq), rq)
+    _close("dk", _np(dk), rk)
+    _close("dv", _np(dv), rv)
+
+
+def test_rope_with_identity_tables_is_the_plain_path(torch_dev):
+    """cos = 1, sin = 0 rotates nothing: bit-identical to the plain entry points
+    (the rotated keys are the keys, the norm sees the same values)."""
+    torch = torch_dev
+    B, T, H, D, W = 1, 200, 2, 128, 60
+    _say("[parity] rope with identity tables")
+    inp = make_layer_inputs(B, T, H, D, 57)
+    ones = np.full((T, D // 2), 0x3F80, dtype=np.uint16)    # bf16 1.0
+    zeros = np.zeros((T, D // 2), dtype=np.uint16)
+    a = _run(torch, inp, W)
+    b = _run_rope(torch, inp, (ones, zeros), W)
+    for name, x, y in zip(("o", "lse", "dq", "dk", "dv"), a, b):
+        assert torch.equal(x, y), name
+
+
+def test_rope_autograd(torch_dev):
+    import sliding_window_causal_qk_amd as sw
+    torch = torch_dev
+    _say("[parity] rope autograd wrapper")
+    inp = make_layer_inputs(1, 200, 4, 128, 58, H_kv=2)
+    tables = rope_tables_bf16(200, 128)
+    q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
+    rope = tuple(_to_dev(torch, t) for t in tables)
+    ref = _run_rope(torch, inp, tables, 50)
+    qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = sw.attention(qq, kk, vv, 50, rope=rope)
+    o.backward(do)
+    assert torch.equal(o.detach(), ref[0])
+    assert torch.equal(qq.grad, ref[2]) and torch.equal(kk.grad, ref[3]) and torch.equal(vv.grad, ref[4])
+
+
 def _sample_rows(T, W, rng, n=6):
     fixed = [0, 1, 63, 64, 127, 128, T // 2, T - 2, T - 1]
     if W >= 0:
@@ -187,17 +258,29 @@ def _sampled_check(torch, wl, layer, window, slices):
     inp = make_layer_inputs(wl.B, wl.T, wl.H, wl.D, wl.seed(layer), wl.sigma_qkv, wl.sigma_do,
                             H_kv=wl.H_kv)
     qf, kf, vf, dof = inp.as_f32()
-    o, lse, dq, dk, dv = _run(torch, inp, window, wl.eps)
+    if wl.rope:
+        tables = rope_tables_bf16(wl.T, wl.D)
+        c, sn = (bf16_bits_to_f32(t) for t in tables)
+        o, lse, dq, dk, dv = _run_rope(torch, inp, tables, window, wl.eps)
+    else:
+        o, lse, dq, dk, dv = _run(torch, inp, window, wl.eps)
     rng = np.random.default_rng(1234 + layer)
     for (b, h) in slices:
         rows = _sample_rows(wl.T, window, rng)
-        o_s = _np(o[b, rows, h])
-        l_s = _np(lse[b, h, rows])
-        ro, rl = oracle.fwd_rows(qf, kf, vf, b, h, rows, window, True, wl.eps)
-        _close(f"o[{b},{h}]", o_s, ro)
-        _close(f"lse[{b},{h}]", l_s, rl)
         keys = rows[:4] + rows[-3:]
-        sq, sk, sv = oracle.bwd_rows(qf, kf, vf, dof, b, h, rows, keys, window, True, wl.eps)
+        if wl.rope:
+            # the oracle on batch b's rotated q and k; gradients rotated back per row
+            qb, kb = oracle.rope(qf[b:b + 1], c, sn), oracle.rope(kf[b:b + 1], c, sn)
+            ro, rl = oracle.fwd_rows(qb, kb, vf[b:b + 1], 0, h, rows, window, True, wl.eps)
+            sq, sk, sv = oracle.bwd_rows(qb, kb, vf[b:b + 1], dof[b:b + 1], 0, h, rows, keys, window,
+                                         True, wl.eps)
+            sq = oracle.rope_bwd(sq, c[rows], sn[rows])
+            sk = oracle.rope_bwd(sk, c[keys], sn[keys])
+        else:
+            ro, rl = oracle.fwd_rows(qf, kf, vf, b, h, rows, window, True, wl.eps)
+            sq, sk, sv = oracle.bwd_rows(qf, kf, vf, dof, b, h, rows, keys, window, True, wl.eps)
+        _close(f"o[{b},{h}]", _np(o[b, rows, h]), ro)
+        _close(f"lse[{b},{h}]", _np(lse[b, h, rows]), rl)
         hk = oracle.kv_head(h, wl.H, wl.kv_heads)   # dk, dv: the key/value head h reads
         _close(f"dq[{b},{h}]", _np(dq[b, rows, h]), sq)
         _close(f"dk[{b},{hk}]", _np(dk[b, keys, hk]), sk)
@@ -215,7 +298,8 @@ def test_single_layer_workloads_sampled(torch_dev, name):
 
 
 @pytest.mark.parametrize("name,layer", [("sssl_stack", 0), ("sssl_stack", 3), ("long", 0), ("long", 3),
-                                        ("gqa_sssl_stack", 0), ("gqa_sssl_stack", 3)])
+                                        ("gqa_sssl_stack", 0), ("gqa_sssl_stack", 3),
+                                        ("rope_sssl_stack", 0), ("rope_sssl_stack", 3)])
 def test_stack_and_long_workloads_sampled(torch_dev, name, layer):
     import sliding_window_causal_qk_amd as sw
     wl = workload(name)

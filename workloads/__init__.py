@@ -43,6 +43,17 @@ def gaussian_bf16(shape: Tuple[int, ...], rng: np.random.Generator, sigma: float
     return round_to_bf16_bits(x)
 
 
+def rope_tables_bf16(T: int, D: int, base: float = 10000.0) -> Tuple[np.ndarray, np.ndarray]:
+    """Rotary tables as the tutorial's model precomputes them ("Autoresearch
+    深度教程" §7.4): inverse frequencies base^(-c / D) for c = 0, 2, .., D - 2,
+    angles t * inv_freq for positions t < T, cos and sin in fp32, rounded to
+    bf16.  Returns the (cos, sin) bit patterns, [T, D/2] uint16."""
+    channel = np.arange(0, D, 2, dtype=np.float32)
+    inv_freq = (1.0 / (np.float32(base) ** (channel / np.float32(D)))).astype(np.float32)
+    ang = np.outer(np.arange(T, dtype=np.float32), inv_freq).astype(np.float32)
+    return round_to_bf16_bits(np.cos(ang)), round_to_bf16_bits(np.sin(ang))
+
+
 @dataclass
 class LayerInputs:
     """bf16 bit patterns (uint16) in the [B, T, H, D] layout."""
@@ -86,6 +97,7 @@ class Workload:
     eps: float = EPS
     notes: str = ""
     H_kv: int | None = None   # key/value heads (None: H, plain multi-head attention)
+    rope: bool = False        # q, k are given before the rotary embedding (base 10000)
 
     def seed(self, layer: int) -> int:
         return self.seed0 + layer
@@ -111,6 +123,9 @@ WORKLOADS: List[Workload] = [
     Workload("gqa_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=3000,
              H_kv=2,
              notes="the SSSL stack with grouped key/value heads, n_kv_head = n_head / 2"),
+    Workload("rope_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=4000,
+             rope=True,
+             notes="the SSSL stack with the rotary embedding fused ahead of the QK norm"),
 ]
 
 

@@ -35,5 +35,8 @@ from .attention import (  # noqa: F401
     rope_bwd,
     attention_fwd_rope,
     attention_bwd_rope,
+    ve_gate,
+    attention_fwd_ve,
+    attention_bwd_ve,
 )
 from .schedule import layer_windows, flops_per_token  # noqa: F401

@@ -42,6 +42,17 @@ What is computed (per batch b and head h; x[t] is the D-vector at position t):
   The backward maps a gradient g of y back through the transpose:
       dx1 = g1 * cos - g2 * sin,  dx2 = g1 * sin + g2 * cos
 
+  Value-embedding gate, optionally applied to v ("Autoresearch 深度教程"
+  §5.2.3: a layer with a value embedding ve [B, T, H_kv, D] mixes it into v
+  through a per-token, per-head gate computed from the first 32 channels of
+  the block input x by a bias-free linear map W_g [H_kv, 32]):
+      z[b, t, h] = sum_c W_g[h, c] x[b, t, c],   gate = 2 sigmoid(z)
+      v' = v + gate * ve          (attention then uses v')
+  The backward, given dv' (the gradient attention hands to v'):
+      dv = dv',  dve = gate * dv',  dgate = sum_d dv' * ve,
+      dz = dgate * gate * (1 - gate / 2),
+      dW_g[h, c] = sum_{b,t} dz[b, t, h] x[b, t, c],  dx[b, t, c] = sum_h dz[b, t, h] W_g[h, c]
+
   Backward, given dO (chain rule through the three steps above):
       dV = P^T dO
       dP = dO V^T
@@ -122,6 +133,40 @@ def rope_bwd(g, cos, sin) -> np.ndarray:
     h = g.shape[-1] // 2
     g1, g2 = g[..., :h], g[..., h:]
     return np.concatenate([g1 * c - g2 * s, g1 * s + g2 * c], axis=-1)
+
+
+def ve_gate(xg, gate_w) -> np.ndarray:
+    """gate [B, T, H_kv] = 2 sigmoid(x[..., :32] W_g^T), xg [B, T, >= 32],
+    gate_w [H_kv, 32]."""
+    z = _f64(xg)[..., :32] @ _f64(gate_w).T
+    return 2.0 / (1.0 + np.exp(-z))
+
+
+def attention_fwd_ve(q, k, v, ve, xg, gate_w, window: int, causal: bool = True,
+                     eps: float = 1e-6, cos=None, sin=None):
+    """Forward with the value-embedding gate on v (and, given tables, the
+    rotary embedding of q and k)."""
+    vg = _f64(v) + ve_gate(xg, gate_w)[..., None] * _f64(ve)
+    if cos is not None:
+        return attention_fwd_rope(q, k, vg, cos, sin, window, causal, eps)
+    return attention_fwd(q, k, vg, window, causal, eps)
+
+
+def attention_bwd_ve(q, k, v, do, ve, xg, gate_w, window: int, causal: bool = True,
+                     eps: float = 1e-6, cos=None, sin=None):
+    """dq, dk, dv, dve, dxg [B, T, 32], dgate_w [H_kv, 32] of attention_fwd_ve."""
+    gate = ve_gate(xg, gate_w)
+    vg = _f64(v) + gate[..., None] * _f64(ve)
+    if cos is not None:
+        dq, dk, dvg = attention_bwd_rope(q, k, vg, do, cos, sin, window, causal, eps)
+    else:
+        dq, dk, dvg = attention_bwd(q, k, vg, do, window, causal, eps)
+    dve = gate[..., None] * dvg
+    dz = np.sum(dvg * _f64(ve), axis=-1) * gate * (1.0 - gate / 2.0)
+    x32 = _f64(xg)[..., :32]
+    dW = np.einsum("bth,btc->hc", dz, x32)
+    dx = dz @ _f64(gate_w)
+    return dq, dk, dvg, dve, dx, dW
 
 
 def attention_fwd_rope(q, k, v, cos, sin, window: int, causal: bool = True,

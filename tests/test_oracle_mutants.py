@@ -13,8 +13,8 @@ import types
 import numpy as np
 import pytest
 
-from tests.test_oracle_pins import (_rand, _torch_reference, _torch_rope_reference, bf16_round,
-                                    brute_force_fwd, rope_tables)
+from tests.test_oracle_pins import (_rand, _torch_reference, _torch_rope_reference, _torch_ve_reference,
+                                    bf16_round, brute_force_fwd, rope_tables)
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "oracle", "attention.py")
@@ -55,6 +55,10 @@ MUTANTS = [
     ("rope_bwd_sign", "[g1 * c - g2 * s, g1 * s + g2 * c]", "[g1 * c + g2 * s, g2 * c - g1 * s]"),
     ("rope_bwd_missing", "return rope_bwd(dq, cos, sin), rope_bwd(dk, cos, sin), dv",
      "return dq, dk, dv"),
+    ("ve_gate_no_factor_2", "return 2.0 / (1.0 + np.exp(-z))", "return 1.0 / (1.0 + np.exp(-z))"),
+    ("ve_sigmoid_derivative", "gate * (1.0 - gate / 2.0)", "gate * (1.0 - gate)"),
+    ("ve_dve_without_gate", "dve = gate[..., None] * dvg", "dve = dvg"),
+    ("ve_dx_transposed_map", "dx = dz @ _f64(gate_w)", "dx = np.sum(dz, axis=-1, keepdims=True) * np.sum(_f64(gate_w), axis=0)"),
 ]
 
 
@@ -97,6 +101,17 @@ def _pins_pass(A) -> bool:
         got = ((A.attention_fwd_rope(q, k, v, c, s, W, True, EPS)[0],)
                + tuple(A.attention_bwd_rope(q, k, v, do, c, s, W, True, EPS)))
         if not all(a.shape == b.shape and np.allclose(a, b, rtol=1e-9, atol=1e-11) for a, b in zip(got, ref)):
+            return False
+        # library: F.linear + sigmoid gate, autograd
+        T, D, W = 12, 8, 4
+        q, k, v, ve, do = (_rand((1, T, 2, D), s) for s in (29, 30, 31, 32, 33))
+        xg = _rand((1, T, 32), 34)
+        gw = _rand((2, 32), 35, 0.3)
+        ref = _torch_ve_reference(q, k, v, do, ve, xg, gw, W, EPS)
+        got = ((A.attention_fwd_ve(q, k, v, ve, xg, gw, W, True, EPS)[0],)
+               + tuple(A.attention_bwd_ve(q, k, v, do, ve, xg, gw, W, True, EPS)))
+        want = ref[:5] + (ref[5][..., :32], ref[6])
+        if not all(a.shape == b.shape and np.allclose(a, b, rtol=1e-9, atol=1e-11) for a, b in zip(got, want)):
             return False
         # closed form: identical keys
         T, D = 16, 8

@@ -299,6 +299,104 @@ def test_rope_bwd_matches_finite_differences():
         assert err < 1e-7, (which, err)
 
 
+# ------------------------------------------------- value-embedding gate
+
+def _torch_ve_reference(q, k, v, do, ve, xg, gw, window, eps, c=None, s=None):
+    """torch autograd through F.linear + sigmoid (the gate), the mix into v,
+    optionally a complex-multiplication rotation, rms_norm and SDPA (fp64)."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    B, T, H, D = q.shape
+    ts = [torch.tensor(x, requires_grad=True) for x in (q, k, v, ve, xg, gw)]
+    qt, kt, vt, vet, xt, wt = ts
+    gate = 2.0 * torch.sigmoid(F.linear(xt[..., :32], wt))
+    vg = vt + gate[..., None] * vet
+    if c is not None:
+        rot = torch.complex(torch.tensor(c), -torch.tensor(s))[None, :, None, :]
+
+        def rotate(x):
+            z = torch.complex(x[..., :D // 2], x[..., D // 2:]) * rot
+            return torch.cat([z.real, z.imag], dim=-1)
+        qr, kr = rotate(qt), rotate(kt)
+    else:
+        qr, kr = qt, kt
+    qn = F.rms_norm(qr, (D,), eps=eps).transpose(1, 2)
+    kn = F.rms_norm(kr, (D,), eps=eps).transpose(1, 2)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    mask = (j <= i) & ((i - j <= window) if window >= 0 else torch.ones(T, T, dtype=torch.bool))
+    o = F.scaled_dot_product_attention(qn, kn, vg.transpose(1, 2), attn_mask=mask,
+                                       enable_gqa=k.shape[2] != H).transpose(1, 2)
+    o.backward(torch.tensor(do))
+    return (o.detach().numpy(),) + tuple(t.grad.numpy() for t in ts)
+
+
+@pytest.mark.parametrize("H,H_kv,T,D,W,rope", [(2, 2, 24, 16, 5, False), (4, 2, 30, 8, -1, False),
+                                               (2, 1, 20, 16, 3, True)])
+def test_ve_fwd_bwd_match_torch(H, H_kv, T, D, W, rope):
+    q, do = (_rand((2, T, H, D), s) for s in (73, 74))
+    k, v, ve = (_rand((2, T, H_kv, D), s) for s in (75, 76, 77))
+    xg = _rand((2, T, 40), 78)          # a wider block input: only channels 0..31 feed the gate
+    gw = _rand((H_kv, 32), 79, 0.2)
+    c, sn = (bf16_round(t) for t in rope_tables(T, D)) if rope else (None, None)
+    ref = _torch_ve_reference(q, k, v, do, ve, xg, gw, W, EPS, c, sn)
+    o, _ = oracle.attention_fwd_ve(q, k, v, ve, xg, gw, W, True, EPS, c, sn)
+    dq, dk, dv, dve, dx, dW = oracle.attention_bwd_ve(q, k, v, do, ve, xg, gw, W, True, EPS, c, sn)
+    np.testing.assert_allclose(o, ref[0], rtol=1e-10, atol=1e-12)
+    for a, b in ((dq, ref[1]), (dk, ref[2]), (dv, ref[3]), (dve, ref[4]), (dW, ref[6])):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dx, ref[5][..., :32], rtol=1e-10, atol=1e-11)
+    assert np.all(ref[5][..., 32:] == 0)
+
+
+def test_ve_gate_closed_forms():
+    """W_g = 0 gives gate = 1 exactly (v' = v + ve); ve = 0 leaves attention
+    unchanged and gives no gate gradient."""
+    T, D, W = 20, 8, 6
+    q, k, v, ve, do = (_rand((1, T, 2, D), s) for s in (80, 81, 82, 83, 84))
+    xg = _rand((1, T, 32), 85)
+    zero_w = np.zeros((2, 32))
+    assert np.all(oracle.ve_gate(xg, zero_w) == 1.0)
+    o, lse = oracle.attention_fwd_ve(q, k, v, ve, xg, zero_w, W, True, EPS)
+    o2, lse2 = oracle.attention_fwd(q, k, v + ve, W, True, EPS)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-14)
+    gw = _rand((2, 32), 86, 0.3)
+    dq, dk, dv, dve, dx, dW = oracle.attention_bwd_ve(q, k, v, do, np.zeros_like(ve), xg, gw, W, True, EPS)
+    assert np.all(dx == 0) and np.all(dW == 0)
+    np.testing.assert_allclose(dve, oracle.ve_gate(xg, gw)[..., None] * dv, rtol=0, atol=0)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, W, True, EPS)
+    for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+def test_ve_bwd_matches_finite_differences():
+    T, D, W = 8, 4, 3
+    q, do = (_rand((1, T, 2, D), s) for s in (87, 88))
+    k, v, ve = (_rand((1, T, 1, D), s) for s in (89, 90, 91))
+    xg = _rand((1, T, 32), 92, 0.5)
+    gw = _rand((1, 32), 93, 0.3)
+    grads = oracle.attention_bwd_ve(q, k, v, do, ve, xg, gw, W, True, EPS)
+    args = [q, k, v, ve, xg, gw]
+    which_of = {0: 0, 1: 1, 2: 2, 3: 3, 4: 4, 5: 5}   # grads: dq, dk, dv, dve, dx, dW
+
+    def loss(a):
+        return float(np.sum(oracle.attention_fwd_ve(*a[:6], W, True, EPS)[0] * do))
+
+    h = 1e-6
+    for gi, ai in which_of.items():
+        grad = grads[gi]
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[ai][idx] += h
+            am[ai][idx] -= h
+            num[idx] = (loss(ap) - loss(am)) / (2 * h)
+        err = np.max(np.abs(num - grad)) / np.max(np.abs(grad))
+        assert err < 1e-7, (gi, err)
+
+
 # -------------------------------------------------------- finite differences
 
 @pytest.mark.parametrize("W,causal", [(5, True), (-1, True), (3, False)])

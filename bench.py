@@ -42,6 +42,7 @@ KERNELS = {
     2: ("bwd_kscale", "hbm"),
     3: ("bwd_dkdv", "mfma"),
     4: ("bwd_dq", "mfma"),
+    5: ("bwd_gate", "hbm"),
 }
 FLOPS_PER_PAIR_D = {1: 4, 3: 8, 4: 2}
 
@@ -55,10 +56,12 @@ def kernel_sources_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None, rope=False):
+def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None, rope=False, gate=False):
     """(amount, unit) of algorithmic work of one launch of kernel `kid`
     (H query heads, H_kv key/value heads; rope: the pre-passes also read the
-    two bf16 [T, D/2] tables and write the rotated keys)."""
+    two bf16 [T, D/2] tables and write the rotated keys; gate: they read ve and
+    the 32 gate channels of x, and the backward one also reads v and writes the
+    gated values and the gate)."""
     H_kv = H if H_kv is None else H_kv
     E_kv = B * T * H_kv * D
     if kid in FLOPS_PER_PAIR_D:
@@ -66,8 +69,14 @@ def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None, rope=False):
     extra = (2 * E_kv + 2 * T * D) if rope else 0
     if kid == 0:   # read K and V, write the key scales and V^T (rows padded to a multiple of 64)
         LT = (T + 63) // 64 * 64
+        if gate:
+            extra += 2 * E_kv + 64 * B * T
         return 2 * E_kv + 2 * E_kv + 4 * B * H_kv * T + 2 * B * H_kv * D * LT + extra, "byte"
+    if kid == 5:   # read dz and x's 32 gate channels, write dx (bf16) and the partial sums
+        return 4 * B * T * H_kv + 64 * B * T + 64 * B * T, "byte"
     # bwd_kscale: read K, write the key scales
+    if gate:
+        extra += 6 * E_kv + 64 * B * T + 4 * B * H_kv * T
     return 2 * E_kv + 4 * B * H_kv * T + extra, "byte"
 
 
@@ -158,8 +167,10 @@ def main():
     if wl.rope:
         rope = tuple(torch.from_numpy(t.view("int16")).view(torch.bfloat16).to(dev)
                      for t in rope_tables_bf16(T, D))
-    fws = sw.fwd_rope_workspace_bytes if wl.rope else sw.fwd_workspace_bytes
-    bws = sw.bwd_rope_workspace_bytes if wl.rope else sw.bwd_workspace_bytes
+    fws = (sw.fwd_ve_workspace_bytes if wl.ve_gate else
+           sw.fwd_rope_workspace_bytes if wl.rope else sw.fwd_workspace_bytes)
+    bws = (sw.bwd_ve_workspace_bytes if wl.ve_gate else
+           sw.bwd_rope_workspace_bytes if wl.rope else sw.bwd_workspace_bytes)
     layers = []
     for l, W in enumerate(windows):
         q, k, v, do = make_layer_inputs_device(B, T, H, D, wl.seed(l), wl.sigma_qkv, wl.sigma_do, dev,
@@ -172,6 +183,13 @@ def main():
             wsb=torch.empty(bws(B, T, H, D, H_kv), dtype=torch.uint8, device=dev),
             n_vis=sw.visible_pairs(T, W),
         ))
+        if wl.ve_gate:   # value embedding, block input (n_embd = H D channels) and gate map
+            g = torch.Generator(device=dev)
+            g.manual_seed(wl.seed(l) + 100)
+            layers[-1]["gate"] = (
+                torch.randn((B, T, H_kv, D), generator=g, device=dev).to(torch.bfloat16),
+                torch.randn((B, T, H * D), generator=g, device=dev).to(torch.bfloat16),
+                torch.randn((H_kv, 32), generator=g, device=dev) * 0.2)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -179,10 +197,12 @@ def main():
     def step():
         for L in layers:
             sw.attn_fwd(L["q"], L["k"], L["v"], L["W"], True, wl.eps,
-                        out=L["o"], lse=L["lse"], workspace=L["wsf"], stream=stream, rope=rope)
+                        out=L["o"], lse=L["lse"], workspace=L["wsf"], stream=stream, rope=rope,
+                        gate=L.get("gate"))
         for L in reversed(layers):
             sw.attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], L["W"], True, wl.eps,
-                        dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["wsb"], stream=stream, rope=rope)
+                        dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["wsb"], stream=stream, rope=rope,
+                        gate=L.get("gate"))
 
     for _ in range(args.warmup):
         step()
@@ -211,7 +231,7 @@ def main():
         work = 0.0
         unit = None
         for L in layers:
-            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"], H_kv, wl.rope)
+            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"], H_kv, wl.rope, wl.ve_gate)
             work += amt * args.steps
         secs = tot.value * 1e-3
         if unit == "flop":
@@ -264,6 +284,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "H_kv": H_kv, "D": D, "rope": wl.rope,
+                   "ve_gate": wl.ve_gate,
                    "pattern": wl.pattern,
                    "n_layer": len(windows), "windows": windows, "eps": wl.eps,
                    "flop_convention": "F14 = 14*D*N_vis per (batch, head, layer)",

@@ -191,13 +191,50 @@ int attn_bwd_rope(const void* q, const void* k, const void* v,
                   void* stream);
 
 /*
+ * Value-embedding gate fused into the V load ("Autoresearch 深度教程" §5.2.3:
+ * a layer with a value embedding ve mixes it into v through a gate computed
+ * per token and key/value head from the first 32 channels of the block input
+ * x by a bias-free linear map W_g):
+ *   gate[b, t, h] = 2 sigmoid(sum_{c < 32} gate_w[h, c] x[b, t, c]),
+ *   attention uses v + gate * ve in place of v.
+ * ve: bf16 [B, T, H_kv, D].  xg: bf16 gate input, token (b, t) at
+ * xg + (b T + t) xg_stride elements, channels 0..31 read (a [B, T, C] block
+ * input with xg_stride = C works as is); xg_stride >= 32 and a multiple of 8.
+ * gate_w: fp32 [H_kv, 32].  rope_cos / rope_sin: as in attn_fwd_rope, or both
+ * NULL for no rotation.  H_kv above 16 returns ATTN_ERR_UNSUPPORTED.
+ * attn_bwd_ve also writes dve (bf16 [B, T, H_kv, D]), dxg (bf16 [B, T, 32]:
+ * the gradient of x's first 32 channels; the other channels get none) and
+ * dgate_w (fp32 [H_kv, 32], summed over all tokens in a fixed order, so
+ * deterministic); dv is the gradient of v.  Every output must be 16-byte
+ * aligned and alias no input or other output.  Other rules as for the
+ * *_gqa entry points; workspace sizes: *_ve_workspace_bytes.
+ */
+size_t attn_fwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D);
+int attn_fwd_ve(const void* q, const void* k, const void* v, const void* ve,
+                const void* xg, int xg_stride, const float* gate_w,
+                const void* rope_cos, const void* rope_sin, void* o, float* lse,
+                void* workspace, size_t workspace_bytes,
+                int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                void* stream);
+size_t attn_bwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D);
+int attn_bwd_ve(const void* q, const void* k, const void* v, const void* ve,
+                const void* xg, int xg_stride, const float* gate_w,
+                const void* rope_cos, const void* rope_sin,
+                const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, void* dve, void* dxg, float* dgate_w,
+                void* workspace, size_t workspace_bytes,
+                int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                void* stream);
+
+/*
  * Opt-in per-kernel timing, a measurement aid (not part of the operation).
  * While enabled, every kernel launch of attn_fwd / attn_bwd is bracketed by
  * two HIP events recorded on the launch stream.  Kernel ids: 0 fwd_prep
  * (key scales and transposed V, the pre-pass of the forward), 1 attn_fwd
  * (forward attention),
  * 2 bwd_kscale (key scales of the backward), 3 bwd_dkdv (dK and dV),
- * 4 bwd_dq (dQ, with q_hat, Delta and lse log2(e) for bwd_dkdv).
+ * 4 bwd_dq (dQ, with q_hat, Delta and lse log2(e) for bwd_dkdv),
+ * 5 bwd_gate (the value-embedding gate's dx and dW_g, attn_bwd_ve only).
  *   attn_profile_enable(on): clears the totals and starts (on != 0) or stops
  *     recording; returns ATTN_ERR_HIP if waiting on earlier events failed.
  *   attn_profile_read(kernel, total_ms, launches): waits for the recorded

@@ -13,6 +13,9 @@ q: bf16 CUDA tensor [B, T, H, D] (contiguous), D in {64, 128}; k, v: bf16
 reads key/value head h // (H // H_kv); H_kv = H is plain multi-head attention).
 rope=(cos, sin): bf16 [T, D/2] tables; q and k are then the projections before
 the rotary embedding, which the kernels apply ahead of the norm.
+gate=(ve, x, gate_w): the value-embedding gate, attention on
+v + 2 sigmoid(x[..., :32] gate_w^T) ve; ve bf16 [B, T, H_kv, D], x bf16
+[B, T, C >= 32] (the block input), gate_w fp32 [H_kv, 32].
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "attention", "attn_fwd", "attn_bwd", "layer_windows", "visible_pairs", "band_tiles",
     "fwd_workspace_bytes", "bwd_workspace_bytes", "fwd_rope_workspace_bytes",
-    "bwd_rope_workspace_bytes", "SwattnError",
+    "bwd_rope_workspace_bytes", "fwd_ve_workspace_bytes", "bwd_ve_workspace_bytes", "SwattnError",
 ]
 
 
@@ -72,6 +75,27 @@ def bwd_rope_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int]
     return int(lib().attn_bwd_rope_workspace_bytes(B, T, H, H if H_kv is None else H_kv, D))
 
 
+def fwd_ve_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int] = None) -> int:
+    return int(lib().attn_fwd_ve_workspace_bytes(B, T, H, H if H_kv is None else H_kv, D))
+
+
+def bwd_ve_workspace_bytes(B: int, T: int, H: int, D: int, H_kv: Optional[int] = None) -> int:
+    return int(lib().attn_bwd_ve_workspace_bytes(B, T, H, H if H_kv is None else H_kv, D))
+
+
+def _check_gate(gate, B, T, H_kv, D):
+    torch = _torch()
+    if not (isinstance(gate, (tuple, list)) and len(gate) == 3):
+        raise ValueError("gate must be a (ve, x, gate_w) triple of tensors")
+    ve, x, gw = gate
+    _check_tensor(ve, "ve", (B, T, H_kv, D), torch.bfloat16)
+    _check_tensor(x, "x", None, torch.bfloat16)
+    if x.dim() != 3 or tuple(x.shape[:2]) != (B, T) or x.shape[2] < 32 or x.shape[2] % 8:
+        raise ValueError(f"x must be [B, T, C] with C >= 32 a multiple of 8, got {tuple(x.shape)}")
+    _check_tensor(gw, "gate_w", (H_kv, 32), torch.float32)
+    return ve, x, gw
+
+
 def _check_rope(rope, T, D):
     torch = _torch()
     if not (isinstance(rope, (tuple, list)) and len(rope) == 2):
@@ -111,7 +135,8 @@ def _stream(stream) -> Optional[int]:
 
 
 def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
-             out=None, lse=None, workspace=None, stream=None, rope=None) -> Tuple["object", "object"]:
+             out=None, lse=None, workspace=None, stream=None, rope=None,
+             gate=None) -> Tuple["object", "object"]:
     """Forward through the C ABI.  Returns (o bf16 [B,T,H,D], lse fp32 [B,H,T])."""
     torch = _torch()
     B, T, H, D = q.shape
@@ -123,6 +148,17 @@ def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
     l = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor(o, "out", (B, T, H, D), torch.bfloat16)
     _check_tensor(l, "lse", (B, H, T), torch.float32)
+    if gate is not None:
+        ve, x, gw = _check_gate(gate, B, T, H_kv, D)
+        rc, rs = _check_rope(rope, T, D) if rope is not None else (None, None)
+        nbytes = fwd_ve_workspace_bytes(B, T, H, D, H_kv)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+        st = lib().attn_fwd_ve(_ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(x), x.shape[2], _ptr(gw),
+                               _ptr(rc), _ptr(rs), _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(),
+                               B, T, H, H_kv, D, int(window), int(bool(causal)), float(eps),
+                               _stream(stream))
+        check(st, "attn_fwd_ve")
+        return o, l
     if rope is not None:
         rc, rs = _check_rope(rope, T, D)
         nbytes = fwd_rope_workspace_bytes(B, T, H, D, H_kv)
@@ -146,9 +182,11 @@ def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
 
 
 def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float = 1e-6, *,
-             dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None):
+             dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None, gate=None):
     """Backward through the C ABI.  Returns (dq, dk, dv): bf16, dq [B,T,H,D],
-    dk and dv shaped like k and v."""
+    dk and dv shaped like k and v; with gate=(ve, x, gate_w) also dve (bf16,
+    like ve), dx32 (bf16 [B, T, 32], the gradient of x's first 32 channels)
+    and dgate_w (fp32 [H_kv, 32])."""
     torch = _torch()
     B, T, H, D = q.shape
     H_kv = k.shape[2] if k.dim() == 4 else -1
@@ -163,6 +201,21 @@ def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float
     _check_tensor(dq, "dq", (B, T, H, D), torch.bfloat16)
     for n, t in (("dk", dk), ("dv", dv)):
         _check_tensor(t, n, (B, T, H_kv, D), torch.bfloat16)
+    if gate is not None:
+        ve, x, gw = _check_gate(gate, B, T, H_kv, D)
+        rc, rs = _check_rope(rope, T, D) if rope is not None else (None, None)
+        dve = torch.empty_like(ve)
+        dx32 = torch.empty((B, T, 32), dtype=torch.bfloat16, device=q.device)
+        dgw = torch.empty((H_kv, 32), dtype=torch.float32, device=q.device)
+        nbytes = bwd_ve_workspace_bytes(B, T, H, D, H_kv)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+        st = lib().attn_bwd_ve(_ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(x), x.shape[2], _ptr(gw),
+                               _ptr(rc), _ptr(rs), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dx32), _ptr(dgw),
+                               ws.data_ptr(), ws.numel(), B, T, H, H_kv, D, int(window),
+                               int(bool(causal)), float(eps), _stream(stream))
+        check(st, "attn_bwd_ve")
+        return dq, dk, dv, dve, dx32, dgw
     if rope is not None:
         rc, rs = _check_rope(rope, T, D)
         nbytes = bwd_rope_workspace_bytes(B, T, H, D, H_kv)
@@ -193,19 +246,26 @@ def _make_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, window, causal, eps, rope_cos, rope_sin):
+        def forward(ctx, q, k, v, window, causal, eps, rope_cos, rope_sin, ve, x, gate_w):
             rope = None if rope_cos is None else (rope_cos, rope_sin)
-            o, lse = attn_fwd(q, k, v, window, causal, eps, rope=rope)
+            gate = None if ve is None else (ve, x, gate_w)
+            o, lse = attn_fwd(q, k, v, window, causal, eps, rope=rope, gate=gate)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.cfg = (window, causal, eps, rope)
+            ctx.cfg = (window, causal, eps, rope, gate)
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            window, causal, eps, rope = ctx.cfg
-            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), window, causal, eps, rope=rope)
-            return dq, dk, dv, None, None, None, None, None
+            window, causal, eps, rope, gate = ctx.cfg
+            g = attn_bwd(q, k, v, o, lse, do.contiguous(), window, causal, eps, rope=rope, gate=gate)
+            if gate is None:
+                return g[0], g[1], g[2], None, None, None, None, None, None, None, None
+            dq, dk, dv, dve, dx32, dgw = g
+            x = gate[1]
+            dx = torch.zeros_like(x)
+            dx[..., :32] = dx32
+            return dq, dk, dv, None, None, None, None, None, dve, dx, dgw
 
     return _Attention
 
@@ -213,12 +273,14 @@ def _make_function():
 _fn = None
 
 
-def attention(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, rope=None):
+def attention(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, rope=None, gate=None):
     """Autograd-aware QK-RMSNorm causal sliding-window attention (HIP kernels).
     rope=(cos, sin) applies the rotary embedding to q and k before the norm;
-    the tables get no gradient."""
+    the tables get no gradient.  gate=(ve, x, gate_w) mixes the value
+    embedding into v; ve, x (its first 32 channels) and gate_w get gradients."""
     global _fn
     if _fn is None:
         _fn = _make_function()
     rc, rs = (None, None) if rope is None else rope
-    return _fn.apply(q, k, v, window, causal, eps, rc, rs)
+    ve, x, gw = (None, None, None) if gate is None else gate
+    return _fn.apply(q, k, v, window, causal, eps, rc, rs, ve, x, gw)

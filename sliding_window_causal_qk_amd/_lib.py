@@ -20,7 +20,8 @@ EXPORTS = (
     "attn_band_tiles", "attn_fwd_workspace_bytes", "attn_fwd", "attn_bwd_workspace_bytes",
     "attn_bwd", "attn_fwd_gqa_workspace_bytes", "attn_fwd_gqa", "attn_bwd_gqa_workspace_bytes",
     "attn_bwd_gqa", "attn_fwd_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope_workspace_bytes",
-    "attn_bwd_rope", "attn_profile_enable", "attn_profile_read", "attn_kernel_name",
+    "attn_bwd_rope", "attn_fwd_ve_workspace_bytes", "attn_fwd_ve", "attn_bwd_ve_workspace_bytes",
+    "attn_bwd_ve", "attn_profile_enable", "attn_profile_read", "attn_kernel_name",
 )
 
 
@@ -80,6 +81,15 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_rope.restype = c_int
     L.attn_bwd_rope.argtypes = [c_vp] * 11 + [c_vp, c_size] + [c_int] * 7 + [c_float, c_vp]
     L.attn_bwd_rope.restype = c_int
+    for f in (L.attn_fwd_ve_workspace_bytes, L.attn_bwd_ve_workspace_bytes):
+        f.argtypes = [c_int, c_int, c_int, c_int, c_int]
+        f.restype = c_size
+    L.attn_fwd_ve.argtypes = ([c_vp] * 5 + [c_int] + [c_vp] * 5 + [c_vp, c_size] + [c_int] * 7
+                              + [c_float, c_vp])
+    L.attn_fwd_ve.restype = c_int
+    L.attn_bwd_ve.argtypes = ([c_vp] * 5 + [c_int] + [c_vp] * 12 + [c_vp, c_size] + [c_int] * 7
+                              + [c_float, c_vp])
+    L.attn_bwd_ve.restype = c_int
     L.attn_profile_enable.argtypes = [c_int]
     L.attn_profile_enable.restype = c_int
     L.attn_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_double),

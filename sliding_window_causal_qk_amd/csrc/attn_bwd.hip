@@ -43,12 +43,20 @@ namespace swattn {
 // KR rows 256 / (D / 8) apart, so each has KR loads in flight.
 // ROPE: the rows are rotated first (a lane's rotation partner is the lane
 // D / 16 away) and written to kr, the K of the backward kernels.
-template <int D, bool ROPE>
+// VE: the same pass writes vr = v + gate ve (the V of the backward kernels)
+// and the gate of every key, gate = 2 sigmoid(W_g x[:32]).
+template <int D, bool ROPE, bool VE>
 __global__ __launch_bounds__(256) void bwd_kscale_kernel(const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ rcos,
                                                          const uint16_t* __restrict__ rsin,
+                                                         const uint16_t* __restrict__ v,
+                                                         const uint16_t* __restrict__ ve,
+                                                         const uint16_t* __restrict__ xg, int xs,
+                                                         const float* __restrict__ gate_w,
                                                          float* __restrict__ kscale,
-                                                         uint16_t* __restrict__ kr, int nrows,
+                                                         uint16_t* __restrict__ kr,
+                                                         uint16_t* __restrict__ vr,
+                                                         float* __restrict__ gate_out, int nrows,
                                                          int T, int H, float eps) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;     // rows per block pass
@@ -61,6 +69,29 @@ __global__ __launch_bounds__(256) void bwd_kscale_kernel(const uint16_t* __restr
   u32x4 kv[KR];
 #pragma unroll
   for (int i = 0; i < KR; ++i) kv[i] = bload16(rk, ((threadIdx.x / LPR + RPB * i) * D + part * 8) * 2);
+  if constexpr (VE) {
+    const rsrc_t rv = make_rsrc(v + (size_t)rb * D, (long long)(nrows - rb) * D * 2);
+    const rsrc_t rve = make_rsrc(ve + (size_t)rb * D, (long long)(nrows - rb) * D * 2);
+    const rsrc_t rvr = make_rsrc(vr + (size_t)rb * D, (long long)(nrows - rb) * D * 2);
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int row = row0 + RPB * i;   // (b T + t) H + h
+      const bool ok = row < nrows;
+      const int hk = row % H, bt = row / H;
+      const float gate = ve_gate_sum<LPR>(xg + (size_t)(ok ? bt : 0) * xs, gate_w + hk * 32, part, ok);
+      const int off = ((threadIdx.x / LPR + RPB * i) * D + part * 8) * 2;
+      u32x4 vv = bload16(rv, off);
+      const u32x4 ee = bload16(rve, off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vv[e] = pack_bf16(bf_lo(vv[e]) + gate * bf_lo(ee[e]), bf_hi(vv[e]) + gate * bf_hi(ee[e]));
+      bstore16(vv, rvr, off);
+      if (ok && part == 0) {
+        const int t = bt % T, b = bt / T;
+        gate_out[((size_t)b * H + hk) * T + t] = gate;
+      }
+    }
+  }
   if constexpr (ROPE) {
     const rsrc_t rc = make_rsrc(rcos, (long long)T * D), rn = make_rsrc(rsin, (long long)T * D);
     const rsrc_t rkr = make_rsrc(kr + (size_t)rb * D, (long long)(nrows - rb) * D * 2);
@@ -157,14 +188,19 @@ struct DkdvCfg {
 // GROUPED = false is the plain multi-head case, compiled with G = 1 so that the
 // walk over the query heads of a group folds away.  ROPE: k holds the rotated
 // keys, and dK goes back through the transposed rotation in the epilogue.
+// With the value-embedding gate (ve not null), v holds v + gate ve and the
+// epilogue also writes dve = gate dV and dz = (dV . ve) gate (1 - gate / 2),
+// the gradient of the gate's pre-sigmoid input ([B, T, Hkv]).
 template <int D, bool GROUPED, bool ROPE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qhat, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta,
     const float* __restrict__ kscale, const uint16_t* __restrict__ rcos,
-    const uint16_t* __restrict__ rsin, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    int T, int H, int G_arg, int W, int nkt, int ntiles) {
+    const uint16_t* __restrict__ rsin, const uint16_t* __restrict__ ve,
+    const float* __restrict__ gate, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    uint16_t* __restrict__ dve, float* __restrict__ dz, int T, int H, int G_arg, int W, int nkt,
+    int ntiles) {
   using C = DkdvCfg<D, GROUPED, ROPE>;
   const int G = GROUPED ? G_arg : 1;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -504,6 +540,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           tsn[n][q4] = bload8(rn, off);
         }
     }
+    // value embedding and gate of key kj (channels as above, all n)
+    const bool has_ve = ve != nullptr;
+    u32x2 vef[C::NB][4];
+    float gk = 0.f;
+    if (has_ve) {
+      const rsrc_t rve = make_rsrc(ve + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+#pragma unroll
+      for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) vef[n][q4] = bload8(rve, (c * rs_kv + 32 * n + 8 * q4 + 4 * g) * 2);
+      gk = bload4f(make_rsrc(gate + (size_t)bh * T, 4LL * T), kj * 4);
+    }
     issue_plan(pnext, b2);          // the next tile's block 1 (or later) into the free buffer
     pnext = plan_next();
     stage_c(b0);
@@ -565,6 +613,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           }
         }
     }
+    if (has_ve) {
+      float dg = 0.f;   // dV . ve of key kj, this lane's half of the channels
+#pragma unroll
+      for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float x[4] = {bf_lo(vef[n][q4][0]), bf_hi(vef[n][q4][0]), bf_lo(vef[n][q4][1]),
+                              bf_hi(vef[n][q4][1])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dg += acc_dv[n][4 * q4 + e] * x[e];
+        }
+      dg += __shfl_xor(dg, 32);
+      if (g == 0)
+        bstore4f(dg * gk * (1.0f - 0.5f * gk),
+                 make_rsrc(dz + (size_t)tg.b * T * Hkv, 4LL * T * Hkv), (kj * Hkv + tg.hk) * 4);
+    }
     // outputs leave through LDS so that every store writes whole rows: the
     // lane's values (key c, d = 32 n + 8 q4 + 4 g + e) go to a row-major
     // 32 x D block, then each lane stores 16-byte chunks of 4 rows per
@@ -574,8 +638,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int slot = w < 2 ? b0 + C::OUT_SLOT * w : C::XO_B + C::OUT_SLOT * (w - 2);
     const rsrc_t rdk = make_rsrc(dk + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
     const rsrc_t rdv = make_rsrc(dv + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+    const rsrc_t rdve = make_rsrc(dve + sbase + (size_t)kw0 * rs_kv, has_ve ? kslice_bytes - kw0 * rsb_kv : 0);
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < 3; ++pass) {
+      if (pass == 2 && !has_ve) break;
 #pragma unroll
       for (int n = 0; n < C::NB; ++n)
 #pragma unroll
@@ -583,13 +649,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            y[e] = pass == 1 ? acc_dv[n][4 * q4 + e]
-                   : ROPE ? acc_dk[n][4 * q4 + e]
-                          : rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean);
+            y[e] = pass == 2   ? gk * acc_dv[n][4 * q4 + e]
+                   : pass == 1 ? acc_dv[n][4 * q4 + e]
+                   : ROPE      ? acc_dk[n][4 * q4 + e]
+                               : rk * (acc_dk[n][4 * q4 + e] - khat[n][4 * q4 + e] * mean);
           st8(smem + slot + 2 * (c * C::OP + 32 * n + 8 * q4 + 4 * g),
               u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
         }
-      const rsrc_t ro = pass == 0 ? rdk : rdv;
+      const rsrc_t ro = pass == 0 ? rdk : pass == 1 ? rdv : rdve;
 #pragma unroll
       for (int i = 0; i < 32 * D / 8 / 64; ++i) {
         const int idx = lane + 64 * i, r = idx / (D / 8), ch = idx % (D / 8);
@@ -927,6 +994,79 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   RS::store_rows(smem, slot, make_rsrc(dq + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
 }
 
+// ------------------------------------------------------------ gate gradients
+// The last step of the value-embedding gate's backward, from dz [B T, Hkv]:
+//   dx[bt, c]   = sum_h dz[bt, h] W_g[h, c]            (c < 32, bf16 out)
+//   dW_g[h, c]  = sum_bt dz[bt, h] x[bt, c]
+// ve_gate_bwd_kernel: block i takes tokens 64 i .. 64 i + 63 as 8 groups of
+// 32 lanes; lane c of group j handles channel c of tokens j, j + 8, .., with
+// all 8 tokens' loads in flight.  The groups' sums of dW_g meet in LDS and the
+// block writes one partial [Hkv, 32].  ve_gate_dw_kernel (one block per head)
+// adds the partials in a fixed order, so dW_g is deterministic.
+constexpr int kGateMaxH = 16;   // key/value heads the gate kernels support
+
+__global__ __launch_bounds__(256) void ve_gate_bwd_kernel(const float* __restrict__ dz,
+                                                          const uint16_t* __restrict__ xg, int xs,
+                                                          const float* __restrict__ gate_w,
+                                                          uint16_t* __restrict__ dxg,
+                                                          float* __restrict__ part, int nbt, int Hkv) {
+  __shared__ float red[8][kGateMaxH * 32];
+  const int c = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int t0 = blockIdx.x * kGateTokens + grp;
+  float xv[8], dx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int bt = t0 + 8 * i;
+    xv[i] = bt < nbt ? __uint_as_float((uint32_t)xg[(size_t)bt * xs + c] << 16) : 0.f;
+    dx[i] = 0.f;
+  }
+  for (int h = 0; h < Hkv; ++h) {
+    const float w = gate_w[h * 32 + c];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int bt = t0 + 8 * i;
+      const float d = bt < nbt ? dz[(size_t)bt * Hkv + h] : 0.f;
+      dx[i] += d * w;
+      acc += d * xv[i];
+    }
+    red[grp][h * 32 + c] = acc;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int bt = t0 + 8 * i;
+    if (bt < nbt) dxg[(size_t)bt * 32 + c] = (uint16_t)(pack_bf16(dx[i], 0.f) & 0xffff);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < Hkv * 32; i += 256) {
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += red[j][i];
+    part[(size_t)blockIdx.x * Hkv * 32 + i] = sum;
+  }
+}
+
+// block h: lane c of group j adds the partials j, j + 8, .. of channel c
+__global__ __launch_bounds__(256) void ve_gate_dw_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ dw, int nblk, int Hkv) {
+  __shared__ float red[8][32];
+  const int c = threadIdx.x & 31, grp = threadIdx.x >> 5, h = blockIdx.x;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  int b = grp;
+  for (; b + 24 < nblk; b += 32)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sum[u] += part[((size_t)(b + 8 * u) * Hkv + h) * 32 + c];
+  for (; b < nblk; b += 8) sum[0] += part[((size_t)b * Hkv + h) * 32 + c];
+  red[grp][c] = (sum[0] + sum[1]) + (sum[2] + sum[3]);
+  __syncthreads();
+  if (grp == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += red[j][c];
+    dw[h * 32 + c] = t;
+  }
+}
+
 template <int D, bool GROUPED, bool ROPE>
 static hipError_t set_dkdv_lds() {
   using C = DkdvCfg<D, GROUPED, ROPE>;
@@ -942,12 +1082,17 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const int G = a.H / a.Hkv;
   const int nrows = a.B * a.T * a.Hkv;
   const int nblk_p = (int)(((long long)nrows * (D / 8) + 4 * 256 - 1) / (4 * 256));
-  // with the rotary embedding, the backward kernels read the rotated keys
+  // with the rotary embedding, the backward kernels read the rotated keys;
+  // with the value-embedding gate, the gated values
   const uint16_t* kk = (const uint16_t*)(ROPE ? a.kr : a.k);
+  const uint16_t* vv = (const uint16_t*)(a.ve ? a.vr : a.v);
   ProfToken t0 = prof_begin(K_BWD_KSCALE, stream);
-  hipLaunchKernelGGL((bwd_kscale_kernel<D, ROPE>), dim3(nblk_p), dim3(256), 0, stream,
-                     (const uint16_t*)a.k, (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, a.kscale,
-                     (uint16_t*)a.kr, nrows, a.T, a.Hkv, a.eps);
+  hipLaunchKernelGGL((a.ve ? bwd_kscale_kernel<D, ROPE, true> : bwd_kscale_kernel<D, ROPE, false>),
+                     dim3(nblk_p), dim3(256), 0, stream,
+                     (const uint16_t*)a.k, (const uint16_t*)a.rcos, (const uint16_t*)a.rsin,
+                     (const uint16_t*)a.v, (const uint16_t*)a.ve, (const uint16_t*)a.xg, a.xs,
+                     a.gate_w, a.kscale, (uint16_t*)a.kr, (uint16_t*)a.vr, a.gate, nrows, a.T,
+                     a.Hkv, a.eps);
   prof_end(t0);
   const int W = eff_window(a.T, a.window);
   {
@@ -960,7 +1105,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     const int nqt = (a.T + C::BM - 1) / C::BM;
     ProfToken t2 = prof_begin(K_BWD_DQ, stream);
     hipLaunchKernelGGL((bwd_dq_kernel<D, ROPE>), dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.o, kk, (const uint16_t*)a.v,
+                       (const uint16_t*)a.q, (const uint16_t*)a.o, kk, vv,
                        (const uint16_t*)a.dout, a.lse, (const float*)a.kscale,
                        (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.qhat, a.delta,
                        a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps);
@@ -981,11 +1126,22 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
     hipLaunchKernelGGL((G == 1 ? bwd_dkdv_kernel<D, false, ROPE> : bwd_dkdv_kernel<D, true, ROPE>),
                        dim3(grid), dim3(256), C::LDS_BYTES, stream,
-                       (const uint16_t*)a.qhat, kk, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                       (const uint16_t*)a.qhat, kk, vv, (const uint16_t*)a.dout,
                        (const float*)a.lse2, (const float*)a.delta, (const float*)a.kscale,
-                       (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.dk,
-                       (uint16_t*)a.dv, a.T, a.H, G, W, nkt, ntiles);
+                       (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (const uint16_t*)a.ve,
+                       (const float*)a.gate, (uint16_t*)a.dk, (uint16_t*)a.dv, (uint16_t*)a.dve, a.dz,
+                       a.T, a.H, G, W, nkt, ntiles);
     prof_end(t1);
+  }
+  if (a.ve) {
+    const int nbt = a.B * a.T;
+    const int nblk = (nbt + kGateTokens - 1) / kGateTokens;
+    ProfToken t3 = prof_begin(K_BWD_GATE, stream);
+    hipLaunchKernelGGL(ve_gate_bwd_kernel, dim3(nblk), dim3(256), 0, stream, (const float*)a.dz,
+                       (const uint16_t*)a.xg, a.xs, a.gate_w, (uint16_t*)a.dxg, a.dw_part, nbt, a.Hkv);
+    hipLaunchKernelGGL(ve_gate_dw_kernel, dim3(a.Hkv), dim3(256), 0, stream, (const float*)a.dw_part,
+                       a.dgate_w, nblk, a.Hkv);
+    prof_end(t3);
   }
   return hipGetLastError();
 }

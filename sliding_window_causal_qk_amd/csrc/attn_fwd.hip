@@ -14,6 +14,8 @@
 //   With the rotary embedding (§7.4), q and k are rotated before the norm:
 //   channel pair (i, i + D/2) at position t turns by the angle of the bf16
 //   tables cos[t, i], sin[t, i].
+//   With the value-embedding gate (§5.2.3), attention uses
+//   v + 2 sigmoid(W_g x[:32]) ve in place of v.
 //
 // MI355X design:
 //  * QK-norm bounds every logit: |s_ij| <= |q_hat||k_hat|/sqrt(D) < sqrt(D).
@@ -57,11 +59,16 @@ namespace swattn {
 // Columns of vt past T are written as zero.
 // ROPE: the key rows are rotated first; the rotated rows (bf16) go to kr, the
 // K the attention kernel reads, and kscale is taken from them.
-template <int D, bool ROPE>
+// VE: the rows transposed into vt are v + gate ve, gate = 2 sigmoid(W_g x[:32])
+// of the token and key/value head (x row t of batch b at xg + (b T + t) xs).
+template <int D, bool ROPE, bool VE>
 __global__ __launch_bounds__(256) void fwd_prep_kernel(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
                                                        const uint16_t* __restrict__ rcos,
                                                        const uint16_t* __restrict__ rsin,
+                                                       const uint16_t* __restrict__ ve,
+                                                       const uint16_t* __restrict__ xg, int xs,
+                                                       const float* __restrict__ gate_w,
                                                        float* __restrict__ kscale,
                                                        uint16_t* __restrict__ vt,
                                                        uint16_t* __restrict__ kr, int T, int H,
@@ -92,11 +99,21 @@ __global__ __launch_bounds__(256) void fwd_prep_kernel(const uint16_t* __restric
     return i < CPT / 2 ? part * (CPT / 2) + i : CH / 2 + part * (CPT / 2) + i - CPT / 2;
   };
   u32x4 kk[CPT];
+  float gate = 0.f;
+  if constexpr (VE)
+    gate = ve_gate_sum<TPR>(xg + ((size_t)b * T + t0 + r) * xs, gate_w + h * 32, part, t0 + r < T);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int ch = chunk(i);
     kk[i] = bload16(rk, (r * rs + 8 * ch) * 2);
-    const u32x4 vv = bload16(rv, (r * rs + 8 * ch) * 2);
+    u32x4 vv = bload16(rv, (r * rs + 8 * ch) * 2);
+    if constexpr (VE) {
+      const rsrc_t rve = make_rsrc(ve + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
+      const u32x4 ee = bload16(rve, (r * rs + 8 * ch) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vv[e] = pack_bf16(bf_lo(vv[e]) + gate * bf_lo(ee[e]), bf_hi(vv[e]) + gate * bf_hi(ee[e]));
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) vs[(r * LP + 8 * ch) / 2 + e] = vv[e];
   }
@@ -392,10 +409,11 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, ROPE>;
   const int nkb = a.LT / 64;
   ProfToken t0 = prof_begin(K_FWD_PREP, stream);
-  hipLaunchKernelGGL((fwd_prep_kernel<D, ROPE>), dim3(nkb * a.B * a.Hkv), dim3(256), 0, stream,
+  hipLaunchKernelGGL((a.ve ? fwd_prep_kernel<D, ROPE, true> : fwd_prep_kernel<D, ROPE, false>),
+                     dim3(nkb * a.B * a.Hkv), dim3(256), 0, stream,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.rcos,
-                     (const uint16_t*)a.rsin, a.kscale, (uint16_t*)a.vt, (uint16_t*)a.kr, a.T,
-                     a.Hkv, a.LT, a.eps);
+                     (const uint16_t*)a.rsin, (const uint16_t*)a.ve, (const uint16_t*)a.xg, a.xs,
+                     a.gate_w, a.kscale, (uint16_t*)a.vt, (uint16_t*)a.kr, a.T, a.Hkv, a.LT, a.eps);
   prof_end(t0);
   const int nqt = (a.T + C::BM - 1) / C::BM;
   const int nblk = nqt * a.B * a.H;

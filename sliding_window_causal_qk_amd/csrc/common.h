@@ -122,6 +122,26 @@ __device__ __forceinline__ void rope4_bwd(float* g1, float* g2, u32x2 c, u32x2 s
   }
 }
 
+// ---- value-embedding gate: gate = 2 sigmoid(sum_c w[c] x[c]) over the 32
+// gate channels of a token (x bf16, w fp32).  NL consecutive lanes share a
+// token, each summing 32 / NL channels starting at 32 / NL * part; every lane
+// of the group returns the gate.
+template <int NL>
+__device__ __forceinline__ float ve_gate_sum(const uint16_t* xrow, const float* w, int part, bool valid) {
+  constexpr int NC = 32 / NL;
+  float z = 0.f;
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < NC; j += 2) {
+      const uint32_t xx = *reinterpret_cast<const uint32_t*>(xrow + NC * part + j);
+      z += bf_lo(xx) * w[NC * part + j] + bf_hi(xx) * w[NC * part + j + 1];
+    }
+  }
+#pragma unroll
+  for (int m = NL / 2; m >= 1; m >>= 1) z += __shfl_xor(z, m, NL);
+  return 2.0f / (1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
 // Wave-uniform value moved to a scalar register.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

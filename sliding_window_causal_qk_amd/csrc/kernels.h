@@ -19,6 +19,10 @@ struct FwdArgs {
   const void* rcos;  // bf16 [T, D/2] rotary tables, or null: no rotary embedding
   const void* rsin;
   void* kr;          // workspace (rotary only): bf16 [B, T, Hkv, D], the rotated keys
+  const void* ve;    // bf16 [B, T, Hkv, D] value embedding, or null: no gate
+  const void* xg;    // bf16 gate input: token (b, t) at xg + (b T + t) xs, channels 0..31
+  int xs;
+  const float* gate_w;  // fp32 [Hkv, 32]
   int B, T, H, D;
   int Hkv;        // key/value heads (H is a multiple); q, o: H heads, k, v: Hkv
   int window;
@@ -43,11 +47,26 @@ struct BwdArgs {
   const void* rcos;  // bf16 [T, D/2] rotary tables, or null: no rotary embedding
   const void* rsin;
   void* kr;          // workspace (rotary only): bf16 [B, T, Hkv, D], the rotated keys
+  // value-embedding gate (ve null: none)
+  const void* ve;    // bf16 [B, T, Hkv, D]
+  const void* xg;    // bf16 gate input: token (b, t) at xg + (b T + t) xs, channels 0..31
+  int xs;
+  const float* gate_w;  // fp32 [Hkv, 32]
+  void* dve;         // bf16 [B, T, Hkv, D]
+  void* dxg;         // bf16 [B, T, 32]
+  float* dgate_w;    // fp32 [Hkv, 32]
+  void* vr;          // workspace: bf16 [B, T, Hkv, D], v + gate ve
+  float* gate;       // workspace: [B, Hkv, T]
+  float* dz;         // workspace: [B, T, Hkv], gradient of the gate's pre-sigmoid input
+  float* dw_part;    // workspace: [ceil(B T / kGateTokens), Hkv, 32], per-block partial sums of dgate_w
   int B, T, H, D;
   int Hkv;        // key/value heads (H is a multiple); k, v, dk, dv have Hkv heads
   int window;
   float eps;
 };
+
+// tokens per block of the first pass of the gate's weight-gradient reduction
+constexpr int kGateTokens = 64;
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);

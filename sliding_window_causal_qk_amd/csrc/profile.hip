@@ -25,7 +25,7 @@ std::vector<Rec> g_recs;
 double g_total_ms[kNumKernels];
 long long g_count[kNumKernels];
 
-const char* kNames[kNumKernels] = {"fwd_prep", "attn_fwd", "bwd_kscale", "bwd_dkdv", "bwd_dq"};
+const char* kNames[kNumKernels] = {"fwd_prep", "attn_fwd", "bwd_kscale", "bwd_dkdv", "bwd_dq", "bwd_gate"};
 
 // fold finished records into the totals; returns false on a HIP error
 bool drain() {

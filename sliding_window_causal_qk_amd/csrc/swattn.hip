@@ -141,26 +141,76 @@ size_t attn_bwd_rope_workspace_bytes(int B, int T, int H, int H_kv, int D) {
   return attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D) + round_up((size_t)B * T * H_kv * D * 2);
 }
 
+size_t attn_fwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D) {
+  return attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D);
+}
+
+size_t attn_bwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D) {
+  if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
+  return attn_bwd_rope_workspace_bytes(B, T, H, H_kv, D) + round_up((size_t)B * T * H_kv * D * 2) +
+         2 * stats_bytes(B, T, H_kv) +
+         round_up(((size_t)B * T + swattn::kGateTokens - 1) / swattn::kGateTokens * H_kv * 32 * 4);
+}
+
 }  // extern "C"
 
 namespace {
 
-// Forward with or without the rotary embedding (rcos == nullptr: none).
-int fwd_impl(const void* q, const void* k, const void* v, const void* rcos, const void* rsin,
-             void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int T, int H,
-             int H_kv, int D, int window, int causal, float eps, void* stream, bool rope) {
+// Optional parts of a call: rotary tables, and the value-embedding gate's
+// inputs and (backward) gradient outputs.
+struct Extras {
+  bool rope = false;
+  const void* rcos = nullptr;
+  const void* rsin = nullptr;
+  bool gate = false;
+  const void* ve = nullptr;
+  const void* xg = nullptr;
+  int xs = 0;
+  const float* gate_w = nullptr;
+  void* dve = nullptr;
+  void* dxg = nullptr;
+  float* dgate_w = nullptr;
+};
+
+constexpr int kGateMaxKvHeads = 16;
+
+// Checks of the optional inputs; appends them to `ins` for the aliasing test.
+int check_extras(const Extras& x, int H_kv, const void** ins, int* nin) {
+  if (x.rope) {
+    if (!x.rcos || !x.rsin || !aligned(x.rcos, 16) || !aligned(x.rsin, 16)) return ATTN_ERR_INVALID_ARG;
+    ins[(*nin)++] = x.rcos;
+    ins[(*nin)++] = x.rsin;
+  }
+  if (x.gate) {
+    if (!x.ve || !x.xg || !x.gate_w || !aligned(x.ve, 16) || !aligned(x.xg, 16) || !aligned(x.gate_w, 16))
+      return ATTN_ERR_INVALID_ARG;
+    if (x.xs < 32 || x.xs % 8 != 0) return ATTN_ERR_INVALID_ARG;
+    if (H_kv > kGateMaxKvHeads) return ATTN_ERR_UNSUPPORTED;
+    ins[(*nin)++] = x.ve;
+    ins[(*nin)++] = x.xg;
+    ins[(*nin)++] = x.gate_w;
+  }
+  return ATTN_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+             size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window, int causal,
+             float eps, void* stream, const Extras& x) {
   bool empty;
   int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
-  const void* ins[5] = {q, k, v, rcos, rsin};
-  const int nin = rope ? 5 : 3;
-  for (int i = 0; i < nin; ++i)
+  const void* ins[8] = {q, k, v};
+  int nin = 3;
+  st = check_extras(x, H_kv, ins, &nin);
+  if (st != ATTN_OK) return st;
+  for (int i = 0; i < 3; ++i)
     if (!ins[i] || !aligned(ins[i], 16)) return ATTN_ERR_INVALID_ARG;
   if (!o || !lse || !aligned(o, 16) || !aligned(lse, 16)) return ATTN_ERR_INVALID_ARG;
   for (int i = 0; i < nin; ++i)
     if (ins[i] == o || ins[i] == (const void*)lse) return ATTN_ERR_INVALID_ARG;
-  const size_t need = rope ? attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D)
-                           : attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D);
+  const size_t need = x.gate   ? attn_fwd_ve_workspace_bytes(B, T, H, H_kv, D)
+                      : x.rope ? attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D)
+                               : attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
 
@@ -169,34 +219,43 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* rcos, cons
   a.kscale = static_cast<float*>(workspace);
   a.vt = static_cast<char*>(workspace) + stats_bytes(B, T, H_kv);
   a.LT = vt_cols(T);
-  a.rcos = rope ? rcos : nullptr;
-  a.rsin = rope ? rsin : nullptr;
-  a.kr = rope ? static_cast<char*>(workspace) + attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
+  a.rcos = x.rope ? x.rcos : nullptr;
+  a.rsin = x.rope ? x.rsin : nullptr;
+  a.kr = x.rope ? static_cast<char*>(workspace) + attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
+  a.ve = x.gate ? x.ve : nullptr;
+  a.xg = x.xg;
+  a.xs = x.xs;
+  a.gate_w = x.gate_w;
   a.B = B; a.T = T; a.H = H; a.Hkv = H_kv; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_fwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int bwd_impl(const void* q, const void* k, const void* v, const void* rcos, const void* rsin,
-             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-             void* workspace, size_t workspace_bytes, int B, int T, int H, int H_kv, int D,
-             int window, int causal, float eps, void* stream, bool rope) {
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window, int causal,
+             float eps, void* stream, const Extras& x) {
   bool empty;
   int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
-  const void* ins[8] = {q, k, v, o, lse, dout, rcos, rsin};
-  const int nin = rope ? 8 : 6;
-  void* outs[3] = {dq, dk, dv};
-  for (int i = 0; i < nin; ++i)
+  const void* ins[12] = {q, k, v, o, lse, dout};
+  int nin = 6;
+  st = check_extras(x, H_kv, ins, &nin);
+  if (st != ATTN_OK) return st;
+  for (int i = 0; i < 6; ++i)
     if (!ins[i] || !aligned(ins[i], 16)) return ATTN_ERR_INVALID_ARG;
-  for (void* p : outs) {
-    if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  void* outs[6] = {dq, dk, dv, x.dve, x.dxg, x.dgate_w};
+  const int nout = x.gate ? 6 : 3;
+  for (int j = 0; j < nout; ++j) {
+    if (!outs[j] || !aligned(outs[j], 16)) return ATTN_ERR_INVALID_ARG;
     for (int i = 0; i < nin; ++i)
-      if (ins[i] == p) return ATTN_ERR_INVALID_ARG;
+      if (ins[i] == outs[j]) return ATTN_ERR_INVALID_ARG;
+    for (int i = 0; i < j; ++i)
+      if (outs[i] == outs[j]) return ATTN_ERR_INVALID_ARG;
   }
-  if (dq == dk || dq == dv || dk == dv) return ATTN_ERR_INVALID_ARG;
-  const size_t need = rope ? attn_bwd_rope_workspace_bytes(B, T, H, H_kv, D)
-                           : attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D);
+  const size_t need = x.gate   ? attn_bwd_ve_workspace_bytes(B, T, H, H_kv, D)
+                      : x.rope ? attn_bwd_rope_workspace_bytes(B, T, H, H_kv, D)
+                               : attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
 
@@ -210,12 +269,52 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* rcos, cons
   a.kscale = reinterpret_cast<float*>(ws + qh_bytes);
   a.delta = reinterpret_cast<float*>(ws + qh_bytes + sb);
   a.lse2 = reinterpret_cast<float*>(ws + qh_bytes + 2 * sb);
-  a.rcos = rope ? rcos : nullptr;
-  a.rsin = rope ? rsin : nullptr;
-  a.kr = rope ? ws + attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
+  a.rcos = x.rope ? x.rcos : nullptr;
+  a.rsin = x.rope ? x.rsin : nullptr;
+  a.kr = x.rope ? ws + attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
+  a.ve = x.gate ? x.ve : nullptr;
+  a.xg = x.xg;
+  a.xs = x.xs;
+  a.gate_w = x.gate_w;
+  a.dve = x.dve;
+  a.dxg = x.dxg;
+  a.dgate_w = x.dgate_w;
+  a.vr = a.gate = a.dz = a.dw_part = nullptr;
+  if (x.gate) {
+    char* g = ws + attn_bwd_rope_workspace_bytes(B, T, H, H_kv, D);
+    a.vr = g;
+    g += round_up((size_t)B * T * H_kv * D * 2);
+    a.gate = reinterpret_cast<float*>(g);
+    g += stats_bytes(B, T, H_kv);
+    a.dz = reinterpret_cast<float*>(g);
+    g += stats_bytes(B, T, H_kv);
+    a.dw_part = reinterpret_cast<float*>(g);
+  }
   a.B = B; a.T = T; a.H = H; a.Hkv = H_kv; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_bwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+Extras rope_extras(const void* rcos, const void* rsin) {
+  Extras x;
+  x.rope = true;
+  x.rcos = rcos;
+  x.rsin = rsin;
+  return x;
+}
+
+Extras gate_extras(const void* ve, const void* xg, int xs, const float* gate_w, const void* rcos,
+                   const void* rsin) {
+  Extras x;
+  x.rope = rcos != nullptr || rsin != nullptr;   // tables optional: both or neither
+  x.rcos = rcos;
+  x.rsin = rsin;
+  x.gate = true;
+  x.ve = ve;
+  x.xg = xg;
+  x.xs = xs;
+  x.gate_w = gate_w;
+  return x;
 }
 
 }  // namespace
@@ -225,39 +324,47 @@ extern "C" {
 int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                  void* workspace, size_t workspace_bytes, int B, int T, int H, int H_kv, int D,
                  int window, int causal, float eps, void* stream) {
-  return fwd_impl(q, k, v, nullptr, nullptr, o, lse, workspace, workspace_bytes, B, T, H, H_kv, D,
-                  window, causal, eps, stream, false);
+  return fwd_impl(q, k, v, o, lse, workspace, workspace_bytes, B, T, H, H_kv, D, window, causal, eps,
+                  stream, Extras());
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
              size_t workspace_bytes, int B, int T, int H, int D, int window, int causal, float eps,
              void* stream) {
-  return fwd_impl(q, k, v, nullptr, nullptr, o, lse, workspace, workspace_bytes, B, T, H, H, D,
-                  window, causal, eps, stream, false);
+  return fwd_impl(q, k, v, o, lse, workspace, workspace_bytes, B, T, H, H, D, window, causal, eps,
+                  stream, Extras());
 }
 
 int attn_fwd_rope(const void* q, const void* k, const void* v, const void* rope_cos,
                   const void* rope_sin, void* o, float* lse, void* workspace,
                   size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window,
                   int causal, float eps, void* stream) {
-  return fwd_impl(q, k, v, rope_cos, rope_sin, o, lse, workspace, workspace_bytes, B, T, H, H_kv,
-                  D, window, causal, eps, stream, true);
+  return fwd_impl(q, k, v, o, lse, workspace, workspace_bytes, B, T, H, H_kv, D, window, causal, eps,
+                  stream, rope_extras(rope_cos, rope_sin));
+}
+
+int attn_fwd_ve(const void* q, const void* k, const void* v, const void* ve, const void* xg,
+                int xg_stride, const float* gate_w, const void* rope_cos, const void* rope_sin,
+                void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int T, int H,
+                int H_kv, int D, int window, int causal, float eps, void* stream) {
+  return fwd_impl(q, k, v, o, lse, workspace, workspace_bytes, B, T, H, H_kv, D, window, causal, eps,
+                  stream, gate_extras(ve, xg, xg_stride, gate_w, rope_cos, rope_sin));
 }
 
 int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window,
                  int causal, float eps, void* stream) {
-  return bwd_impl(q, k, v, nullptr, nullptr, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-                  B, T, H, H_kv, D, window, causal, eps, stream, false);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H_kv, D,
+                  window, causal, eps, stream, Extras());
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, int B, int T, int H, int D, int window, int causal,
              float eps, void* stream) {
-  return bwd_impl(q, k, v, nullptr, nullptr, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,
-                  B, T, H, H, D, window, causal, eps, stream, false);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H, D,
+                  window, causal, eps, stream, Extras());
 }
 
 int attn_bwd_rope(const void* q, const void* k, const void* v, const void* rope_cos,
@@ -265,8 +372,22 @@ int attn_bwd_rope(const void* q, const void* k, const void* v, const void* rope_
                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
                   int T, int H, int H_kv, int D, int window, int causal, float eps,
                   void* stream) {
-  return bwd_impl(q, k, v, rope_cos, rope_sin, o, lse, dout, dq, dk, dv, workspace,
-                  workspace_bytes, B, T, H, H_kv, D, window, causal, eps, stream, true);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H_kv, D,
+                  window, causal, eps, stream, rope_extras(rope_cos, rope_sin));
+}
+
+int attn_bwd_ve(const void* q, const void* k, const void* v, const void* ve, const void* xg,
+                int xg_stride, const float* gate_w, const void* rope_cos, const void* rope_sin,
+                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                void* dve, void* dxg, float* dgate_w, void* workspace, size_t workspace_bytes,
+                int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                void* stream) {
+  Extras x = gate_extras(ve, xg, xg_stride, gate_w, rope_cos, rope_sin);
+  x.dve = dve;
+  x.dxg = dxg;
+  x.dgate_w = dgate_w;
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H_kv, D,
+                  window, causal, eps, stream, x);
 }
 
 }  // extern "C"

@@ -269,6 +269,55 @@ def test_rope_aliasing_workspace_unsupported():
     assert _fwd_rope(wsb=0, T=0, **nulls) == _lib.ATTN_OK
 
 
+def _fwd_ve(wsb=1 << 40, **kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], ve=ALIGNED[3], x=ALIGNED[4], xs=512, gw=ALIGNED[5],
+             c=None, s=None, o=ALIGNED[6], lse=ALIGNED[7], ws=ALIGNED[8], B=2, T=64, H=4, H_kv=2, D=64,
+             window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_fwd_ve(a["q"], a["k"], a["v"], a["ve"], a["x"], a["xs"], a["gw"], a["c"], a["s"],
+                                  a["o"], a["lse"], a["ws"], wsb, a["B"], a["T"], a["H"], a["H_kv"], a["D"],
+                                  a["window"], a["causal"], a["eps"], None)
+
+
+def _bwd_ve(wsb=1 << 40, **kw):
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], ve=ALIGNED[3], x=ALIGNED[4], xs=512, gw=ALIGNED[5],
+             c=None, s=None, o=ALIGNED[6], lse=ALIGNED[7], do=ALIGNED[8], dq=ALIGNED[9], dk=ALIGNED[10],
+             dv=ALIGNED[11], dve=P + 12 * 0x1000000, dx=P + 13 * 0x1000000, dgw=P + 14 * 0x1000000,
+             ws=P + 15 * 0x1000000, B=2, T=64, H=4, H_kv=2, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return _lib.lib().attn_bwd_ve(a["q"], a["k"], a["v"], a["ve"], a["x"], a["xs"], a["gw"], a["c"], a["s"],
+                                  a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["dve"], a["dx"],
+                                  a["dgw"], a["ws"], wsb, a["B"], a["T"], a["H"], a["H_kv"], a["D"],
+                                  a["window"], a["causal"], a["eps"], None)
+
+
+VE_INVALID = [dict(ve=None), dict(x=None), dict(gw=None), dict(ve=P + 8), dict(x=P + 4), dict(xs=16),
+              dict(xs=36), dict(c=ALIGNED[10]), dict(s=ALIGNED[11]), dict(H_kv=3), dict(eps=-1.0)]
+
+
+@pytest.mark.parametrize("kw", VE_INVALID, ids=[str(k) for k in VE_INVALID])
+def test_ve_invalid(kw):
+    assert _fwd_ve(**kw) == _lib.ATTN_ERR_INVALID_ARG
+    assert _bwd_ve(**kw) == _lib.ATTN_ERR_INVALID_ARG
+
+
+def test_ve_outputs_workspace_unsupported():
+    for kw in (dict(dve=None), dict(dx=None), dict(dgw=P + 4), dict(dve=ALIGNED[3]), dict(dx=ALIGNED[4]),
+               dict(dgw=ALIGNED[9]), dict(dve=ALIGNED[10])):
+        assert _bwd_ve(**kw) == _lib.ATTN_ERR_INVALID_ARG, kw
+    assert _fwd_ve(o=ALIGNED[3]) == _lib.ATTN_ERR_INVALID_ARG      # output over ve
+    assert _fwd_ve(H=32, H_kv=32) == _lib.ATTN_ERR_UNSUPPORTED      # more key/value heads than the gate kernels take
+    need_f = sw.fwd_ve_workspace_bytes(2, 64, 4, 64, 2)
+    need_b = sw.bwd_ve_workspace_bytes(2, 64, 4, 64, 2)
+    assert need_f == sw.fwd_rope_workspace_bytes(2, 64, 4, 64, 2)
+    # gated values, the gate, dz and the partial sums of dgate_w on top of the rope workspace
+    assert need_b >= sw.bwd_rope_workspace_bytes(2, 64, 4, 64, 2) + 2 * 64 * 2 * 64 * 2 + 2 * 2 * 2 * 64 * 4
+    assert _fwd_ve(wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE
+    assert _bwd_ve(wsb=need_b - 1) == _lib.ATTN_ERR_WORKSPACE
+    nulls = dict(q=None, k=None, v=None, ve=None, x=None, gw=None, o=None, lse=None, ws=None)
+    assert _fwd_ve(wsb=0, B=0, **nulls) == _lib.ATTN_OK
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(H=0)])
 def test_empty_problem_is_ok_and_touches_nothing(kw):
     nulls = dict(q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0)

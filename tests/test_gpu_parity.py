@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import make_layer_inputs, WORKLOADS, workload, bf16_bits_to_f32, rope_tables_bf16
+from workloads import (make_layer_inputs, make_gate_inputs, WORKLOADS, workload, bf16_bits_to_f32,
+                       rope_tables_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,6 +56,16 @@ def _close(name, got, want):
                              f"first at {tuple(idx)}: got {got[tuple(idx)]}, want {want[tuple(idx)]}; "
                              f"max abs err {err.max():.3g}")
     return float(err.max())
+
+
+def _close_sum(name, got, want, scale):
+    """Check of a sum over many terms: |got - want| <= ATOL + RTOL * scale,
+    scale the sum of the terms' magnitudes."""
+    err = np.abs(np.asarray(got, dtype=np.float64) - want)
+    bad = err > ATOL + RTOL * scale
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert not bad.any(), (f"{name}: {bad.sum()} / {bad.size} out of tolerance; max err {err.max():.3g}, "
+                           f"max allowed {(ATOL + RTOL * scale).max():.3g}")
 
 
 def _run(torch, inp, window, eps=EPS):
@@ -246,6 +257,77 @@ def test_rope_autograd(torch_dev):
     assert torch.equal(qq.grad, ref[2]) and torch.equal(kk.grad, ref[3]) and torch.equal(vv.grad, ref[4])
 
 
+VE_SMALL = [
+    # (B, T, H, H_kv, D, W, C, rope, seed): value-embedding gate (C: block input width)
+    (1, 128, 2, 2, 64, 64, 64, False, 60),
+    (2, 257, 4, 2, 128, 100, 512, False, 61),
+    (1, 300, 2, 1, 128, -1, 40, True, 62),
+    (1, 20, 4, 2, 128, 5, 64, True, 63),
+    (2, 333, 2, 2, 64, 0, 32, False, 64),
+    (1, 1, 1, 1, 64, 0, 32, False, 65),
+]
+
+
+def _gate_dev(torch, gi):
+    ve, x = (_to_dev(torch, t) for t in (gi.ve, gi.x))
+    return ve, x, torch.from_numpy(gi.gate_w.copy()).cuda()
+
+
+def _run_ve(torch, inp, gi, window, tables=None, eps=EPS):
+    import sliding_window_causal_qk_amd as sw
+    q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
+    gate = _gate_dev(torch, gi)
+    rope = None if tables is None else tuple(_to_dev(torch, t) for t in tables)
+    o, lse = sw.attn_fwd(q, k, v, window, True, eps, rope=rope, gate=gate)
+    grads = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps, rope=rope, gate=gate)
+    torch.cuda.synchronize()
+    return (o, lse) + tuple(grads)
+
+
+@pytest.mark.parametrize("B,T,H,H_kv,D,W,C,rope,seed", VE_SMALL,
+                         ids=[f"B{c[0]}T{c[1]}H{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}C{c[6]}{'rope' if c[7] else ''}"
+                              for c in VE_SMALL])
+def test_ve_small_full_parity(torch_dev, B, T, H, H_kv, D, W, C, rope, seed):
+    _say(f"[parity] ve gate B={B} T={T} H={H} H_kv={H_kv} D={D} W={W} C={C} rope={rope} seed={seed}")
+    inp = make_layer_inputs(B, T, H, D, seed, H_kv=H_kv)
+    gi = make_gate_inputs(B, T, H_kv, D, C, seed + 100)
+    tables = rope_tables_bf16(T, D) if rope else None
+    c, sn = (bf16_bits_to_f32(t) for t in tables) if rope else (None, None)
+    qf, kf, vf, dof = inp.as_f32()
+    vef, xf = bf16_bits_to_f32(gi.ve), bf16_bits_to_f32(gi.x)
+    got = _run_ve(torch_dev, inp, gi, W, tables)
+    ro, rl = oracle.attention_fwd_ve(qf, kf, vf, vef, xf, gi.gate_w, W, True, EPS, c, sn)
+    ref = oracle.attention_bwd_ve(qf, kf, vf, dof, vef, xf, gi.gate_w, W, True, EPS, c, sn)
+    for name, g, want in zip(("o", "lse", "dq", "dk", "dv", "dve", "dx32"), got, (ro, rl) + ref[:5]):
+        _close(name, _np(g), want)
+    # dgate_w sums dz x over every token: the tolerance applies to each term,
+    # so the bound is 2e-2 + 1e-2 * sum_t |dz x|, dz = (dv . ve) gate (1 - gate / 2)
+    gate = oracle.ve_gate(xf, gi.gate_w)
+    dz = np.sum(ref[2] * vef, axis=-1) * gate * (1 - gate / 2)
+    scale = np.einsum("bth,btc->hc", np.abs(dz), np.abs(xf[..., :32].astype(np.float64)))
+    _close_sum("dgate_w", _np(got[7]), ref[5], scale)
+
+
+def test_ve_autograd(torch_dev):
+    import sliding_window_causal_qk_amd as sw
+    torch = torch_dev
+    _say("[parity] ve gate autograd wrapper")
+    B, T, H, H_kv, D, C = 1, 200, 4, 2, 128, 48
+    inp = make_layer_inputs(B, T, H, D, 66, H_kv=H_kv)
+    gi = make_gate_inputs(B, T, H_kv, D, C, 166)
+    ref = _run_ve(torch, inp, gi, 50)
+    q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
+    ve, x, gw = (t.clone().requires_grad_(True) for t in _gate_dev(torch, gi))
+    qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = sw.attention(qq, kk, vv, 50, gate=(ve, x, gw))
+    o.backward(do)
+    assert torch.equal(o.detach(), ref[0])
+    for g, r in ((qq.grad, ref[2]), (kk.grad, ref[3]), (vv.grad, ref[4]), (ve.grad, ref[5]),
+                 (x.grad[..., :32], ref[6]), (gw.grad, ref[7])):
+        assert torch.equal(g, r)
+    assert float(x.grad[..., 32:].abs().max()) == 0.0
+
+
 def _sample_rows(T, W, rng, n=6):
     fixed = [0, 1, 63, 64, 127, 128, T // 2, T - 2, T - 1]
     if W >= 0:
@@ -258,7 +340,14 @@ def _sampled_check(torch, wl, layer, window, slices):
     inp = make_layer_inputs(wl.B, wl.T, wl.H, wl.D, wl.seed(layer), wl.sigma_qkv, wl.sigma_do,
                             H_kv=wl.H_kv)
     qf, kf, vf, dof = inp.as_f32()
-    if wl.rope:
+    if wl.ve_gate:
+        # the gated values are v' = v + gate ve: the oracle runs on v' (fp64)
+        gi = make_gate_inputs(wl.B, wl.T, wl.kv_heads, wl.D, wl.H * wl.D, wl.seed(layer) + 100)
+        o, lse, dq, dk, dv, dve, dx32, _ = _run_ve(torch, inp, gi, window, None, wl.eps)
+        gate = oracle.ve_gate(bf16_bits_to_f32(np.ascontiguousarray(gi.x[..., :32])), gi.gate_w)
+        vef = bf16_bits_to_f32(gi.ve)
+        vf = vf + gate[..., None] * vef
+    elif wl.rope:
         tables = rope_tables_bf16(wl.T, wl.D)
         c, sn = (bf16_bits_to_f32(t) for t in tables)
         o, lse, dq, dk, dv = _run_rope(torch, inp, tables, window, wl.eps)
@@ -285,6 +374,19 @@ def _sampled_check(torch, wl, layer, window, slices):
         _close(f"dq[{b},{h}]", _np(dq[b, rows, h]), sq)
         _close(f"dk[{b},{hk}]", _np(dk[b, keys, hk]), sk)
         _close(f"dv[{b},{hk}]", _np(dv[b, keys, hk]), sv)
+        if wl.ve_gate:
+            _close(f"dve[{b},{hk}]", _np(dve[b, keys, hk]), gate[b, keys, hk][:, None] * sv)
+    if wl.ve_gate:
+        # dx of sampled tokens: dz over every key/value head of each token
+        b = slices[0][0]
+        keys = _sample_rows(wl.T, window, rng)[:5]
+        G = wl.H // wl.kv_heads
+        dz = np.zeros((len(keys), wl.kv_heads))
+        for hk in range(wl.kv_heads):
+            _, _, sv = oracle.bwd_rows(qf, kf, vf, dof, b, hk * G, keys[:1], keys, window, True, wl.eps)
+            g = gate[b, keys, hk]
+            dz[:, hk] = np.sum(sv * vef[b, keys, hk], axis=1) * g * (1 - g / 2)
+        _close(f"dx32[{b}]", _np(dx32[b, keys]), dz @ gi.gate_w.astype(np.float64))
     for name, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
         assert bool(torch.isfinite(t).all()), f"{name} has non-finite values"
 
@@ -299,7 +401,8 @@ def test_single_layer_workloads_sampled(torch_dev, name):
 
 @pytest.mark.parametrize("name,layer", [("sssl_stack", 0), ("sssl_stack", 3), ("long", 0), ("long", 3),
                                         ("gqa_sssl_stack", 0), ("gqa_sssl_stack", 3),
-                                        ("rope_sssl_stack", 0), ("rope_sssl_stack", 3)])
+                                        ("rope_sssl_stack", 0), ("rope_sssl_stack", 3),
+                                        ("ve_sssl_stack", 0), ("ve_sssl_stack", 3)])
 def test_stack_and_long_workloads_sampled(torch_dev, name, layer):
     import sliding_window_causal_qk_amd as sw
     wl = workload(name)

@@ -98,6 +98,7 @@ class Workload:
     notes: str = ""
     H_kv: int | None = None   # key/value heads (None: H, plain multi-head attention)
     rope: bool = False        # q, k are given before the rotary embedding (base 10000)
+    ve_gate: bool = False     # value-embedding gate on v (block input width n_embd = H D)
 
     def seed(self, layer: int) -> int:
         return self.seed0 + layer
@@ -126,7 +127,31 @@ WORKLOADS: List[Workload] = [
     Workload("rope_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=4000,
              rope=True,
              notes="the SSSL stack with the rotary embedding fused ahead of the QK norm"),
+    Workload("ve_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=5000,
+             ve_gate=True,
+             notes="the SSSL stack with the value-embedding gate fused into the V load"),
 ]
+
+
+@dataclass
+class GateInputs:
+    """Value-embedding gate inputs: ve bf16 bits [B, T, H_kv, D], the block
+    input x bf16 bits [B, T, C] (its first 32 channels feed the gate) and the
+    gate map fp32 [H_kv, 32]."""
+    ve: np.ndarray
+    x: np.ndarray
+    gate_w: np.ndarray
+
+
+def make_gate_inputs(B: int, T: int, H_kv: int, D: int, C: int, seed: int,
+                     w_sigma: float = 0.2) -> GateInputs:
+    """ve ~ N(0, 1) and x ~ N(0, 1) rounded to bf16, gate_w ~ N(0, w_sigma^2) in
+    fp32, drawn in that order from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    ve = gaussian_bf16((B, T, H_kv, D), rng)
+    x = gaussian_bf16((B, T, C), rng)
+    gw = (rng.standard_normal((H_kv, 32), dtype=np.float32) * np.float32(w_sigma)).astype(np.float32)
+    return GateInputs(ve, x, gw)
 
 
 def workload(name: str) -> Workload:

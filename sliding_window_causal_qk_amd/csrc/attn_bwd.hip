@@ -483,13 +483,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       // keep B's results inside this step (the compiler would otherwise sink
       // the softmax below the barrier, away from the MFMAs it should overlap)
       asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
-      wait_vmcnt<0>();            // block it + 2 has landed
-      __syncthreads();
+      // the next plan and the buffer rotation are scalar work that overlaps the
+      // last MFMAs still in flight; the barrier only orders the buffers' contents
+      pnext = plan_next();
       const int t_ = b0;
       b0 = b1;
       b1 = b2;
       b2 = t_;
-      pnext = plan_next();
+      wait_vmcnt<0>();            // block it + 2 has landed
+      __syncthreads();
     };
 
     // Steps whose B needs the element mask sit at both ends of the band; the
@@ -708,8 +710,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
   const int nqt = (T + C::BM - 1) / C::BM;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / nqt;
-  const int qt = nqt - 1 - (lid % nqt);
+  int bh, qt;
+  query_tile_of(lid, nqt, gridDim.x / nqt, kTileGroupDq, &bh, &qt);
   const int b = bh / H, h = bh % H;
   const int i0 = qt * C::BM;
 

@@ -216,8 +216,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 
   const int nqt = (T + C::BM - 1) / C::BM;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = lid / nqt;
-  const int qt = nqt - 1 - (lid % nqt);  // heaviest query tiles of a head first
+  int bh, qt;
+  query_tile_of(lid, nqt, gridDim.x / nqt, kTileGroupFwd, &bh, &qt);
   const int b = bh / H, h = bh % H;
   const int Hkv = H / G;
   const int bhk = b * Hkv + h / G;        // key/value slice read by this head

@@ -302,6 +302,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return (bid & 7) * (nblk >> 3) + (bid >> 3);
 }
 
+// Query tile of logical workgroup `lid` for the query-tiled kernels (forward,
+// dQ), heaviest first: the nbh (batch, head) slices go in groups of gb; inside
+// a group, tile rank r (0 = the last, heaviest query tile) of every slice
+// comes before rank r + 1.  Light tiles of all slices thus end the grid, and
+// each XCD's contiguous range of logical ids still covers few slices.
+__device__ __forceinline__ void query_tile_of(int lid, int nqt, int nbh, int gb, int* bh, int* qt) {
+  const int per = gb * nqt;
+  const int grp = lid / per, r = lid - grp * per;
+  const int gsz = min(gb, nbh - grp * gb);
+  const int rank = r / gsz;
+  *bh = grp * gb + (r - rank * gsz);
+  *qt = nqt - 1 - rank;
+}
+
 // Column position of key/query offset x (0..15) inside a transposed 16-column
 // group, arranged so that the 8 values one lane feeds to an MFMA k-step are
 // contiguous: k-group 0 takes offsets {0..3, 8..11}, k-group 1 {4..7, 12..15}.

@@ -65,6 +65,11 @@ struct BwdArgs {
   float eps;
 };
 
+// (batch, head) slices per group of the query-tiled kernels' heaviest-first
+// order (see query_tile_of); measured best on the SSSL stack's layers
+constexpr int kTileGroupFwd = 4;
+constexpr int kTileGroupDq = 2;
+
 // tokens per block of the first pass of the gate's weight-gradient reduction
 constexpr int kGateTokens = 64;
 

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* qh;
     const uint16_t* dO;
     const float* st;
-    long long nbytes;
+    uint32_t nbytes;    // remaining bytes of the slice, below 2^32
     int nst;
     int r0;
   };
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const uint16_t* cq = qhat;
   const uint16_t* cdo = dout;
   const float* cst = w == 2 ? lse2 : delta;
-  long long cbytes = 0;
+  uint32_t cbytes = 0;
   int cr0 = 0;
   auto seek_head = [&]() {
     const int hq = dgeo.hk * G + dgi;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     cr0 = dgeo.qb0 * C::BMQ;
     cq = qhat + sbase + (size_t)cr0 * rs;
     cdo = dout + sbase + (size_t)cr0 * rs;
-    cbytes = slice_bytes - cr0 * rsb;
+    cbytes = (uint32_t)(slice_bytes - cr0 * rsb);
     cst = (w == 2 ? lse2 : delta) + (size_t)(dgeo.b * H + hq) * T;
   };
   int tcur = tile_at(0);
@@ -312,20 +312,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     pl.dO = cdo;
     pl.st = cst;
     pl.r0 = ok ? cr0 : 0;
-    pl.nbytes = ok ? cbytes : 0;
+    pl.nbytes = ok ? cbytes : 0u;
     pl.nst = (ok && w >= 2) ? 4 * T : 0;
     if (ok) {
       ++ds;
       cq += (size_t)C::BMQ * rs;
       cdo += (size_t)C::BMQ * rs;
-      cbytes -= C::BMQ * rsb;
+      cbytes -= (uint32_t)(C::BMQ * rsb);
       cr0 += C::BMQ;
     }
     return pl;
   };
   auto issue_plan = [&](const DmaPlan& pl, int base) {
-    tile.issue(make_rsrc(pl.qh, pl.nbytes), smem, base, w);
-    tile.issue(make_rsrc(pl.dO, pl.nbytes), smem, base + C::DO_B, w);
+    tile.issue(make_rsrc_u(pl.qh, pl.nbytes), smem, base, w);
+    tile.issue(make_rsrc_u(pl.dO, pl.nbytes), smem, base + C::DO_B, w);
     dma_row4(make_rsrc(pl.st, pl.nst), smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
   };
   auto issue_kv = [&](const TileGeo& tg) {
@@ -787,10 +787,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const rsrc_t rks = make_rsrc(kscale + (size_t)(b * Hkv + h / G) * T, w == 0 ? 4LL * T : 0);   // wave 0 loads kscale
   const uint16_t* k_s = k + kvbase;
   const uint16_t* v_s = v + kvbase;
+  // remaining bytes of the key slices from row r0 on, below 2^32 (unsigned arithmetic)
+  const uint32_t kbytes_u = (uint32_t)kslice_bytes, krow_u = (uint32_t)rsb_kv;
   auto issue_step = [&](int step, int base) {
     const int r0 = (jb0 + step) * C::BN;
-    tile.issue(make_rsrc(k_s + (size_t)r0 * rs_kv, kslice_bytes - r0 * rsb_kv), smem, base, w);
-    tile.issue(make_rsrc(v_s + (size_t)r0 * rs_kv, kslice_bytes - r0 * rsb_kv), smem, base + C::V_B, w);
+    const uint32_t nb = kbytes_u - (uint32_t)r0 * krow_u;
+    tile.issue(make_rsrc_u(k_s + (size_t)r0 * rs_kv, nb), smem, base, w);
+    tile.issue(make_rsrc_u(v_s + (size_t)r0 * rs_kv, nb), smem, base + C::V_B, w);
     dma_row4(rks, smem, base + C::ST_B + 256 * w, (r0 + lane) * 4);
   };
 

@@ -271,10 +271,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const uint16_t* k_s = k + ((size_t)b * T * Hkv + (h / G)) * D;
   const uint16_t* vt_s = vt + (size_t)bhk * D * LT;
   const long long vt_bytes = 2LL * D * LT;
+  // remaining bytes of the slices from key j0 on, below 2^32 (unsigned arithmetic)
+  const uint32_t kbytes_u = (uint32_t)kslice_bytes, krow_u = (uint32_t)rsb_kv, vtbytes_u = (uint32_t)vt_bytes;
   auto issue_step = [&](int step, int base) {
     const int j0 = (jb0 + step) * C::BN;
-    ktile.issue(make_rsrc(k_s + (size_t)j0 * rs_kv, kslice_bytes - j0 * rsb_kv), smem, base, w);
-    vtile.issue(make_rsrc(vt_s + j0, vt_bytes - 2LL * j0), smem, base + C::V_B, w);
+    ktile.issue(make_rsrc_u(k_s + (size_t)j0 * rs_kv, kbytes_u - (uint32_t)j0 * krow_u), smem, base, w);
+    vtile.issue(make_rsrc_u(vt_s + j0, vtbytes_u - 2u * (uint32_t)j0), smem, base + C::V_B, w);
     if (w == 0) dma_row4(rks, smem, base + C::ST_B, (j0 + lane) * 4);   // wave 0 loads kscale
   };
 

@@ -60,6 +60,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long nbytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcFlags);
 }
 
+// The same for a byte count known to be non-negative and below 2^32 (the
+// remaining bytes of one (batch, head) slice): the clamp is one unsigned
+// scalar compare instead of a 64-bit vector compare.
+__device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t nbytes) {
+  const int n = nbytes > 0x7fffffffu ? 0x7fffffff : (int)nbytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcFlags);
+}
+
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }

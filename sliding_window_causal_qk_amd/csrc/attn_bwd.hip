@@ -177,12 +177,16 @@ struct DkdvCfg {
   static constexpr int ST_B = 2 * Tile::BYTES;      // 4 x 256 B: spare, spare, lse2, Delta
   static constexpr int STAGE = ST_B + 1024;
   static constexpr int KV_B = NBUF * STAGE;         // K rows, then V rows of the next tile
+  // the next tile's K / V rows are prefetched into LDS up to D = 128; at
+  // D = 256 they would not fit, and each tile loads them into registers
+  static constexpr bool KV_PREFETCH = D <= 128;
   static constexpr int OP = D + 8;                  // output staging row pitch (bf16)
   static constexpr int OUT_SLOT = 32 * OP * 2;      // one wave's 32 x D bf16 block
-  static constexpr int XO_B = KV_B + 2 * KVTile::BYTES;   // staging slots of waves 2 and 3
+  static constexpr int XO_B = KV_B + (KV_PREFETCH ? 2 * KVTile::BYTES : 0);   // staging slots of waves 2 and 3
   static constexpr int LDS_BYTES = XO_B + 2 * OUT_SLOT;
   static constexpr int NSTORE = 2 * (32 * D / 8 / 64);    // epilogue stores per lane (dK and dV)
   static_assert(2 * OUT_SLOT <= STAGE, "waves 0 and 1 stage their outputs in a freed step buffer");
+  static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
 };
 
 // GROUPED = false is the plain multi-head case, compiled with G = 1 so that the
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // prologue of the stream: K / V rows of the first tile, blocks 0 and 1.
   // Invariant at a step's start: b0 holds block it, b1 block it + 1, b2 is free.
   int b0 = 2 * C::STAGE, b1 = 0, b2 = C::STAGE;
-  if (tcur >= 0) issue_kv(dgeo);
+  if (C::KV_PREFETCH && tcur >= 0) issue_kv(dgeo);
   issue_plan(plan_next(), b1);
   issue_plan(plan_next(), b2);
   DmaPlan pnext = plan_next();
@@ -382,14 +386,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       b1 = b2;
       b2 = t_;
     }
+    if constexpr (C::KV_PREFETCH) {
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      kf[ks] = lds16(smem, kv_off + 32 * ks);
-      vf[ks] = lds16(smem, kv_off + C::KVTile::BYTES + 32 * ks);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        kf[ks] = lds16(smem, kv_off + 32 * ks);
+        vf[ks] = lds16(smem, kv_off + C::KVTile::BYTES + 32 * ks);
+      }
+    } else {
+      const rsrc_t rk = make_rsrc(k + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+      const rsrc_t rv = make_rsrc(v + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        kf[ks] = bload16(rk, (c * rs_kv + 16 * ks + 8 * g) * 2);
+        vf[ks] = bload16(rv, (c * rs_kv + 16 * ks + 8 * g) * 2);
+      }
     }
 #pragma unroll
     for (int n = 0; n < C::NB; ++n) { acc_dv[n] = f32x16{}; acc_dk[n] = f32x16{}; }
-    const bool kv_pending = tile_at(ti + 1) >= 0;   // prefetch of the next tile's K / V rows
+    const bool kv_pending = C::KV_PREFETCH && tile_at(ti + 1) >= 0;   // prefetch of the next tile's K / V rows
 
     // A: scores and dP of one step
     auto stage_a = [&](int base) {
@@ -698,7 +712,7 @@ struct DqCfg {
 // ROPE: k holds the rotated keys; the queries are rotated in the prologue and
 // dQ goes back through the transposed rotation in the epilogue.
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse,
@@ -1153,6 +1167,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const bool rope = a.rcos != nullptr;
+  if (a.D == 256) return rope ? launch_bwd_d<256, true>(a, stream) : launch_bwd_d<256, false>(a, stream);
   if (a.D == 128) return rope ? launch_bwd_d<128, true>(a, stream) : launch_bwd_d<128, false>(a, stream);
   return rope ? launch_bwd_d<64, true>(a, stream) : launch_bwd_d<64, false>(a, stream);
 }

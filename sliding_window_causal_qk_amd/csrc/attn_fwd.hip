@@ -197,6 +197,7 @@ struct FwdCfg {
   static constexpr int ST_B = V_B + VTile::BYTES;      // kscale (128 bytes used of 256)
   static constexpr int STAGE = ST_B + 256;
   static constexpr int LDS_BYTES = NBUF * STAGE;
+  static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
 };
 
 // Chunk slot of logical chunk ch (0..3) in row r of a transposed 32-column tile.
@@ -436,6 +437,7 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const bool rope = a.rcos != nullptr;
+  if (a.D == 256) return rope ? launch_fwd_d<256, true>(a, stream) : launch_fwd_d<256, false>(a, stream);
   if (a.D == 128) return rope ? launch_fwd_d<128, true>(a, stream) : launch_fwd_d<128, false>(a, stream);
   return rope ? launch_fwd_d<64, true>(a, stream) : launch_fwd_d<64, false>(a, stream);
 }

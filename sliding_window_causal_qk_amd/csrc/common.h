@@ -137,12 +137,17 @@ __device__ __forceinline__ void rope4_bwd(float* g1, float* g2, u32x2 c, u32x2 s
 template <int NL>
 __device__ __forceinline__ float ve_gate_sum(const uint16_t* xrow, const float* w, int part, bool valid) {
   constexpr int NC = 32 / NL;
+  static_assert(NC >= 1 && 32 % NL == 0, "lanes per token divide the 32 gate channels");
   float z = 0.f;
   if (valid) {
+    if constexpr (NC == 1) {   // one channel per lane
+      z = __uint_as_float((uint32_t)xrow[part] << 16) * w[part];
+    } else {
 #pragma unroll
-    for (int j = 0; j < NC; j += 2) {
-      const uint32_t xx = *reinterpret_cast<const uint32_t*>(xrow + NC * part + j);
-      z += bf_lo(xx) * w[NC * part + j] + bf_hi(xx) * w[NC * part + j + 1];
+      for (int j = 0; j < NC; j += 2) {
+        const uint32_t xx = *reinterpret_cast<const uint32_t*>(xrow + NC * part + j);
+        z += bf_lo(xx) * w[NC * part + j] + bf_hi(xx) * w[NC * part + j + 1];
+      }
     }
   }
 #pragma unroll

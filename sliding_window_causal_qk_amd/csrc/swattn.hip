@@ -29,7 +29,7 @@ int check_common(int B, int T, int H, int H_kv, int D, int window, int causal, f
   if (window < -1) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (causal == 0) return ATTN_ERR_UNSUPPORTED;
-  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128 && D != 256) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || T == 0 || H == 0) {
     *empty = true;
     return ATTN_OK;

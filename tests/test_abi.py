@@ -159,7 +159,7 @@ def test_aliasing_rejected():
     assert _bwd(dv=ALIGNED[6]) == _lib.ATTN_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(D=32), dict(causal=0),
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=512), dict(D=32), dict(causal=0),
                                 dict(B=1 << 12, T=1 << 12, H=8, D=128)])
 def test_unsupported(kw):
     assert _fwd(**kw) == _lib.ATTN_ERR_UNSUPPORTED

@@ -93,6 +93,11 @@ SMALL = [
     (1, 512, 4, 128, 256, 11),
     (1, 448, 2, 128, 63, 12),
     (1, 448, 2, 128, 65, 13),
+    # head size 256 (the tutorial's tuning table, §10.1.1, goes up to 256)
+    (1, 300, 2, 256, 100, 14),
+    (2, 257, 2, 256, -1, 15),
+    (1, 129, 1, 256, 64, 16),
+    (1, 20, 2, 256, 3, 17),
 ]
 
 
@@ -120,6 +125,7 @@ GQA_SMALL = [
     (2, 333, 4, 2, 64, 0, 44),
     (1, 448, 8, 2, 128, 65, 45),
     (1, 129, 2, 1, 64, 2000, 46),
+    (1, 200, 4, 2, 256, 70, 47),
 ]
 
 
@@ -195,6 +201,7 @@ ROPE_SMALL = [
     (2, 333, 2, 2, 64, 0, 54),
     (1, 448, 2, 2, 128, 65, 55),
     (1, 1, 1, 1, 64, 0, 56),
+    (1, 160, 2, 1, 256, 40, 57),
 ]
 
 
@@ -265,6 +272,7 @@ VE_SMALL = [
     (1, 20, 4, 2, 128, 5, 64, True, 63),
     (2, 333, 2, 2, 64, 0, 32, False, 64),
     (1, 1, 1, 1, 64, 0, 32, False, 65),
+    (1, 150, 2, 2, 256, 30, 64, True, 67),
 ]
 
 

@@ -127,6 +127,8 @@ WORKLOADS: List[Workload] = [
     Workload("rope_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=4000,
              rope=True,
              notes="the SSSL stack with the rotary embedding fused ahead of the QK norm"),
+    Workload("d256_sssl_stack", B=64, T=2048, H=2, D=256, pattern="SSSL", n_layer=8, seed0=6000,
+             notes="the SSSL stack at head size 256 (same n_embd = 512: 2 heads)"),
     Workload("ve_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=5000,
              ve_gate=True,
              notes="the SSSL stack with the value-embedding gate fused into the V load"),

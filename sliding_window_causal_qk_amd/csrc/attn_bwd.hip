@@ -471,11 +471,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     auto step_body = [&](int s_next, auto masked_c) {   // B for step s_next of its query head
       issue_plan(pnext, b2);      // block it + 2 into the free buffer, spread over A
       stage_a(b1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
       for (int i = 0; i < 2 * C::KS - 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);

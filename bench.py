@@ -67,16 +67,13 @@ def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None, rope=False, gate=False)
     if kid in FLOPS_PER_PAIR_D:
         return FLOPS_PER_PAIR_D[kid] * D * n_vis * B * H, "flop"
     extra = (2 * E_kv + 2 * T * D) if rope else 0
-    if kid == 0:   # read K and V, write the key scales and V^T (rows padded to a multiple of 64)
-        LT = (T + 63) // 64 * 64
-        if gate:
-            extra += 2 * E_kv + 64 * B * T
-        return 2 * E_kv + 2 * E_kv + 4 * B * H_kv * T + 2 * B * H_kv * D * LT + extra, "byte"
     if kid == 5:   # read dz and x's 32 gate channels, write dx (bf16) and the partial sums
         return 4 * B * T * H_kv + 64 * B * T + 64 * B * T, "byte"
-    # bwd_kscale: read K, write the key scales
+    # the key pre-pass (kid 0 in the forward, 2 in the backward): read K, write
+    # the key scales; with the gate also read v, ve and x's 32 gate channels and
+    # write the gated values (the backward also keeps the gate)
     if gate:
-        extra += 6 * E_kv + 64 * B * T + 4 * B * H_kv * T
+        extra += 6 * E_kv + 64 * B * T + (4 * B * H_kv * T if kid == 2 else 0)
     return 2 * E_kv + 4 * B * H_kv * T + extra, "byte"
 
 

@@ -94,8 +94,7 @@ long long attn_visible_pairs(int T, int window);
 int attn_band_tiles(int T, int window, int rows, int cols, int by_key,
                     int* first, int* last, int* n_partial, int* n_empty);
 
-/* Bytes of device workspace attn_fwd needs: fp32 [B, H, T] key scales and a
- * bf16 transposed copy of V, [B, H, D, T rounded up to 64]. */
+/* Bytes of device workspace attn_fwd needs: the fp32 [B, H, T] key scales. */
 size_t attn_fwd_workspace_bytes(int B, int T, int H, int D);
 
 /*
@@ -207,7 +206,9 @@ int attn_bwd_rope(const void* q, const void* k, const void* v,
  * dgate_w (fp32 [H_kv, 32], summed over all tokens in a fixed order, so
  * deterministic); dv is the gradient of v.  Every output must be 16-byte
  * aligned and alias no input or other output.  Other rules as for the
- * *_gqa entry points; workspace sizes: *_ve_workspace_bytes.
+ * *_gqa entry points; workspace sizes: *_ve_workspace_bytes (those of the
+ * *_rope entry points plus a bf16 [B, T, H_kv, D] copy of the gated values,
+ * and for the backward the gate and its gradients).
  */
 size_t attn_fwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D);
 int attn_fwd_ve(const void* q, const void* k, const void* v, const void* ve,

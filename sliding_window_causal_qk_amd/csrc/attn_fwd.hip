@@ -29,11 +29,9 @@
 //  * S^T = K Q^T is formed on the 32x32x16 bf16 MFMA so that each lane owns one
 //    query column: its probabilities are already in the B-operand layout of the
 //    next product O^T = V^T P^T, and row sums are lane-local.
-//  * The pre-pass also writes V transposed ([B, H, D, T]) with the keys of every
-//    16-key group permuted (tpos16) into the k order of the MFMA operands, so
-//    the V^T operand is one conflict-free 16-byte LDS read per MFMA instead of
-//    two transposing reads.
-//  * K tiles (padded rows) and V^T tiles (xor-swizzled 16-byte chunks) are
+//  * The V^T operand of that product comes from V rows in LDS by transposing
+//    reads (ds_read_b64_tr_b16), so V needs no transposed copy in HBM.
+//  * K tiles (padded rows) and V tiles (xor-swizzled 16-byte chunks) are
 //    copied global -> LDS by direct-to-LDS buffer loads into three rotating
 //    buffers, one step ahead; one barrier per 32-key step.
 //  * Loads go through buffer descriptors rebased per tile: rows past T read as
@@ -49,140 +47,15 @@
 
 namespace swattn {
 
-// ------------------------------------------------------------ forward pre-pass
-// One workgroup per (batch, key/value head, block of 64 keys); H is the number
-// of key/value heads here:
-//   kscale[b, h, t] = log2(e) / sqrt(D) * r(k[b, t, h, :])
-//   vt[b, h, d, tpos(t)] = v[b, t, h, d]   (V transposed; inside every group of
-//       16 keys the columns are permuted by tpos16, so that the 8 keys one lane
-//       feeds to an MFMA k-step are one contiguous 16-byte chunk)
-// Columns of vt past T are written as zero.
-// ROPE: the key rows are rotated first; the rotated rows (bf16) go to kr, the
-// K the attention kernel reads, and kscale is taken from them.
-// VE: the rows transposed into vt are v + gate ve, gate = 2 sigmoid(W_g x[:32])
-// of the token and key/value head (x row t of batch b at xg + (b T + t) xs).
-template <int D, bool ROPE, bool VE>
-__global__ __launch_bounds__(256) void fwd_prep_kernel(const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v,
-                                                       const uint16_t* __restrict__ rcos,
-                                                       const uint16_t* __restrict__ rsin,
-                                                       const uint16_t* __restrict__ ve,
-                                                       const uint16_t* __restrict__ xg, int xs,
-                                                       const float* __restrict__ gate_w,
-                                                       float* __restrict__ kscale,
-                                                       uint16_t* __restrict__ vt,
-                                                       uint16_t* __restrict__ kr, int T, int H,
-                                                       int LT, float eps) {
-  constexpr int KB = 64;                 // keys per workgroup
-  constexpr int CH = D / 8;              // 16-byte chunks per row
-  constexpr int TPR = 256 / KB;          // threads per key row (4)
-  constexpr int CPT = CH / TPR;          // chunks per thread
-  constexpr int LP = D + 2;              // LDS pitch (bf16) of the V block: column reads hit distinct banks
-  __shared__ uint32_t vs[KB * LP / 2];
-
-  const int nkb = LT / KB;
-  const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
-  const int b = bh / H, h = bh % H;
-  const int t0 = kb * KB;
-  const int tid = threadIdx.x;
-  const int rs = H * D;
-  const long long slice_bytes = (long long)(T - 1) * rs * 2 + 2 * D;
-  const size_t sbase = ((size_t)b * T * H + h) * D;
-  const rsrc_t rk = make_rsrc(k + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
-  const rsrc_t rv = make_rsrc(v + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
-
-  // rows: thread -> key t0 + tid / TPR, CPT chunks: the first half of them
-  // first-half channels, the rest their rotation partners (the same split
-  // with and without ROPE, so that kscale sums in the same order)
-  const int r = tid / TPR, part = tid % TPR;
-  auto chunk = [&](int i) {
-    return i < CPT / 2 ? part * (CPT / 2) + i : CH / 2 + part * (CPT / 2) + i - CPT / 2;
-  };
-  u32x4 kk[CPT];
-  float gate = 0.f;
-  if constexpr (VE)
-    gate = ve_gate_sum<TPR>(xg + ((size_t)b * T + t0 + r) * xs, gate_w + h * 32, part, t0 + r < T);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int ch = chunk(i);
-    kk[i] = bload16(rk, (r * rs + 8 * ch) * 2);
-    u32x4 vv = bload16(rv, (r * rs + 8 * ch) * 2);
-    if constexpr (VE) {
-      const rsrc_t rve = make_rsrc(ve + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
-      const u32x4 ee = bload16(rve, (r * rs + 8 * ch) * 2);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vv[e] = pack_bf16(bf_lo(vv[e]) + gate * bf_lo(ee[e]), bf_hi(vv[e]) + gate * bf_hi(ee[e]));
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vs[(r * LP + 8 * ch) / 2 + e] = vv[e];
-  }
-  if constexpr (ROPE) {
-    const long long tb = (long long)(T - t0) * D;   // table rows t0 .. T-1 (D / 2 bf16 each)
-    const rsrc_t rc = make_rsrc(rcos + (size_t)t0 * (D / 2), tb);
-    const rsrc_t rn = make_rsrc(rsin + (size_t)t0 * (D / 2), tb);
-    const rsrc_t rkr = make_rsrc(kr + sbase + (size_t)t0 * rs, slice_bytes - (long long)t0 * rs * 2);
-#pragma unroll
-    for (int i = 0; i < CPT / 2; ++i) {
-      const int ch = chunk(i);
-      const u32x4 c = bload16(rc, (r * (D / 2) + 8 * ch) * 2), sn = bload16(rn, (r * (D / 2) + 8 * ch) * 2);
-      float y1[8], y2[8];
-      rope8(kk[i], kk[i + CPT / 2], c, sn, y1, y2);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kk[i][e] = pack_bf16(y1[2 * e], y1[2 * e + 1]);
-        kk[i + CPT / 2][e] = pack_bf16(y2[2 * e], y2[2 * e + 1]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) bstore16(kk[i], rkr, (r * rs + 8 * chunk(i)) * 2);
-  }
-  float ss = 0.f;   // of the keys the attention kernel multiplies (rotated, bf16)
-#pragma unroll
-  for (int i = 0; i < CPT; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = bf_lo(kk[i][e]), bb = bf_hi(kk[i][e]);
-      ss += a * a + bb * bb;
-    }
-#pragma unroll
-  for (int m = TPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, TPR);
-  if (part == 0 && t0 + r < T) {
-    const float rr = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-    kscale[(size_t)bh * T + t0 + r] = rr * (kLog2e / sqrtf((float)D));
-  }
-  __syncthreads();
-
-  // columns: thread -> (d, 8-key chunk); consecutive threads write consecutive
-  // 16-byte chunks of one row of vt
-  const uint16_t* vsh = reinterpret_cast<const uint16_t*>(vs);
-  uint16_t* vrow = vt + (size_t)bh * D * LT + t0;
-#pragma unroll
-  for (int p = 0; p < D * (KB / 8) / 256; ++p) {
-    const int idx = tid + 256 * p;
-    const int d = idx / (KB / 8), ch = idx % (KB / 8);
-    uint32_t w4[4];
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      // position 8 ch + j holds key tpos16^-1 (tpos16 is an involution)
-      const int k0 = (8 * ch + j) & ~15, x0 = (8 * ch + j) & 15;
-      const uint32_t lo = vsh[(k0 + tpos16(x0)) * LP + d];
-      const uint32_t hi = vsh[(k0 + tpos16(x0 + 1)) * LP + d];
-      w4[j / 2] = lo | (hi << 16);
-    }
-    st16(vrow + (size_t)d * LT + 8 * ch, u32x4{w4[0], w4[1], w4[2], w4[3]});
-  }
-}
-
 // ------------------------------------------------------------ forward kernel
 // Workgroup: 4 waves; wave w owns queries i0 + 32 w + c.  Key blocks of 32
-// (K rows, V^T columns and kscale) stream through the band in three LDS
-// buffers filled by direct-to-LDS loads one step ahead.  Per block i:
+// (K rows, V rows and kscale) stream through the band in three LDS buffers
+// filled by direct-to-LDS loads one step ahead.  Per block i:
 //   A(i): S^T = K Q_hat^T                      (queries in lanes, keys in registers)
 //   B(i): P = exp2(S^T kscale - sqrt(D) log2 e), masked on edge blocks; row sums
-//   C(i): O^T += V^T P^T                       (V^T from the transposed copy)
-// The loop issues A(i+1), then C(i) interleaved with B(i+1).  Every MFMA
-// operand read from LDS is one conflict-free 16-byte read.
+//   C(i): O^T += V^T P^T                       (V^T by transposing reads of V)
+// The loop issues A(i+1), then C(i) interleaved with B(i+1).  Every LDS read
+// is free of bank conflicts.
 template <int D, bool ROPE>
 struct FwdCfg {
   static constexpr int BM = 128;   // queries per workgroup (32 per wave)
@@ -192,7 +65,7 @@ struct FwdCfg {
   static constexpr int NB = D / 32;
   static constexpr int PK = D + 8;                     // K row pitch (bf16): 16-byte reads conflict-free
   using KTile = DmaTileV<BN * PK / 8, 4, 8 + ROPE>;
-  using VTile = DmaTileV<D * BN / 8, 4, 8 + ROPE>;     // D rows of 64 bytes, xor-swizzled chunks
+  using VTile = DmaTileV<BN * D / 8, 4, 8 + ROPE>;     // BN rows of D bf16, xor-swizzled chunks
   static constexpr int V_B = KTile::BYTES;
   static constexpr int ST_B = V_B + VTile::BYTES;      // kscale (128 bytes used of 256)
   static constexpr int STAGE = ST_B + 256;
@@ -200,18 +73,20 @@ struct FwdCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
 };
 
-// Chunk slot of logical chunk ch (0..3) in row r of a transposed 32-column tile.
-__device__ __forceinline__ int vt_slot(int r, int ch) { return ch ^ ((r >> 2) & 3); }
+// LDS slot of 16-byte chunk ch of V row r.  A transposing read takes two
+// chunks of each of 4 consecutive rows (32 bytes each); xor-ing bits 1-2 of
+// the chunk index with the row's position in its group of 4 spreads those 8
+// chunks over distinct banks without padding the rows.
+__device__ __forceinline__ int v_slot(int r, int ch) { return ch ^ (2 * (r & 3)); }
 
 // ROPE: k is the rotated copy written by the pre-pass, and the queries are
 // rotated in the prologue.
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ vt, const float* __restrict__ kscale,
+    const uint16_t* __restrict__ v, const float* __restrict__ kscale,
     const uint16_t* __restrict__ rcos, const uint16_t* __restrict__ rsin,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int G, int LT, int W,
-    float eps) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int G, int W, float eps) {
   using C = FwdCfg<D, ROPE>;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -264,26 +139,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     return (r < C::BN && ch < D / 8) ? (r * rs_kv + 8 * ch) * 2 : -1;
   });
   typename C::VTile vtile;
-  vtile.init(w, lane, [&](int qc) {
-    const int r = qc >> 2, s = qc & 3;
-    return (r * LT + 8 * vt_slot(r, s)) * 2;
+  vtile.init(w, lane, [&](int qc) {   // LDS chunk qc: row qc / (D / 8), slot qc % (D / 8)
+    const int r = qc / (D / 8), sl = qc % (D / 8);
+    return (r * rs_kv + 8 * v_slot(r, sl)) * 2;   // v_slot is its own inverse
   });
   const rsrc_t rks = make_rsrc(kscale + (size_t)bhk * T, 4LL * T);
-  const uint16_t* k_s = k + ((size_t)b * T * Hkv + (h / G)) * D;
-  const uint16_t* vt_s = vt + (size_t)bhk * D * LT;
-  const long long vt_bytes = 2LL * D * LT;
+  const size_t kvbase = ((size_t)b * T * Hkv + (h / G)) * D;
+  const uint16_t* k_s = k + kvbase;
+  const uint16_t* v_s = v + kvbase;
   // remaining bytes of the slices from key j0 on, below 2^32 (unsigned arithmetic)
-  const uint32_t kbytes_u = (uint32_t)kslice_bytes, krow_u = (uint32_t)rsb_kv, vtbytes_u = (uint32_t)vt_bytes;
+  const uint32_t kbytes_u = (uint32_t)kslice_bytes, krow_u = (uint32_t)rsb_kv;
   auto issue_step = [&](int step, int base) {
     const int j0 = (jb0 + step) * C::BN;
-    ktile.issue(make_rsrc_u(k_s + (size_t)j0 * rs_kv, kbytes_u - (uint32_t)j0 * krow_u), smem, base, w);
-    vtile.issue(make_rsrc_u(vt_s + j0, vtbytes_u - 2u * (uint32_t)j0), smem, base + C::V_B, w);
+    const uint32_t nb = kbytes_u - (uint32_t)j0 * krow_u;
+    ktile.issue(make_rsrc_u(k_s + (size_t)j0 * rs_kv, nb), smem, base, w);
+    vtile.issue(make_rsrc_u(v_s + (size_t)j0 * rs_kv, nb), smem, base + C::V_B, w);
     if (w == 0) dma_row4(rks, smem, base + C::ST_B, (j0 + lane) * 4);   // wave 0 loads kscale
   };
 
   const int a_off = 2 * (c * C::PK + 8 * g);                 // K rows: row c, chunk 2 ks + g
-  const int v_off0 = 64 * c + 16 * vt_slot(c, g);            // V^T rows 32 n + c, chunk g (k-step 0)
-  const int v_off1 = 64 * c + 16 * vt_slot(c, 2 + g);        // ... chunk 2 + g (k-step 1)
+  // transposing reads of the V rows (16-lane group: lane i = 4 a + e reads
+  // slot j from the 8-byte piece addressed by lane a + 4 j): lane (g, c)
+  // addresses row 4 g + li / 4 (+ 16 s2, + 8), channels 32 n + 16 hb + 4 (li % 4)
+  // .. + 3, i.e. chunk 4 n + x, x = 2 hb + (li % 4) / 2, 8-byte half li % 2.
+  // The row's swizzle xors the chunk with 2 kr, kr = li / 4: bit 0 of kr flips
+  // bit 1 of x, bit 1 of kr flips the parity of n, so even and odd n take two
+  // lane offsets and n / 2 a fixed step of 128 bytes.
+  const int li = lane & 15, hb = (lane >> 4) & 1, kr4 = li >> 2;
+  const int xs4 = (2 * hb + ((li & 3) >> 1)) ^ (2 * (kr4 & 1));
+  const int vrow = 2 * D * (4 * g + kr4) + 16 * xs4 + 8 * (li & 1);
+  const int v_even = vrow + 64 * (kr4 >> 1);
+  const int v_odd = vrow + 64 * (1 - (kr4 >> 1));
   const int k_off = C::ST_B + 16 * g;                        // kscale of the lane's key quads
 
   f32x16 s_acc;
@@ -321,14 +207,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
   };
   // O^T[d, q] += V^T[d, kv] P^T[kv, q]; element j of k-step s2 is key
-  // 16 s2 + 4 g + (j % 4) + 8 (j / 4), the order of the tpos16 columns
+  // 16 s2 + 4 g + (j % 4) + 8 (j / 4), the k order of the probabilities
   auto stage_c = [&](int base) {
     const int vb = base + C::V_B;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int n = 0; n < C::NB; ++n)
-        acc[n] = mfma32(lds16(smem, vb + (s2 ? v_off1 : v_off0) + 2048 * n), pf[s2], acc[n]);
+      for (int n = 0; n < C::NB; ++n) {
+        const int off = vb + ((n & 1) ? v_odd : v_even) + 128 * (n >> 1) + 2 * D * 16 * s2;
+        const u32x2 a0 = lds_tr4b(smem, off), a1 = lds_tr4b(smem, off + 2 * D * 8);
+        acc[n] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[s2], acc[n]);
+      }
   };
 
   // ---- prologue: steps 0, 1 in LDS, step 2 in flight; A(0), B(0)
@@ -410,14 +299,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 template <int D, bool ROPE>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, ROPE>;
-  const int nkb = a.LT / 64;
-  ProfToken t0 = prof_begin(K_FWD_PREP, stream);
-  hipLaunchKernelGGL((a.ve ? fwd_prep_kernel<D, ROPE, true> : fwd_prep_kernel<D, ROPE, false>),
-                     dim3(nkb * a.B * a.Hkv), dim3(256), 0, stream,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.rcos,
-                     (const uint16_t*)a.rsin, (const uint16_t*)a.ve, (const uint16_t*)a.xg, a.xs,
-                     a.gate_w, a.kscale, (uint16_t*)a.vt, (uint16_t*)a.kr, a.T, a.Hkv, a.LT, a.eps);
-  prof_end(t0);
+  KeyPrepArgs kp;
+  kp.k = a.k; kp.v = a.v; kp.rcos = a.rcos; kp.rsin = a.rsin; kp.ve = a.ve; kp.xg = a.xg; kp.xs = a.xs;
+  kp.gate_w = a.gate_w; kp.kscale = a.kscale; kp.kr = a.kr; kp.vr = a.vr; kp.gate = nullptr;
+  kp.B = a.B; kp.T = a.T; kp.Hkv = a.Hkv; kp.D = D; kp.eps = a.eps;
+  const hipError_t ep = launch_key_prep(kp, K_FWD_PREP, stream);
+  if (ep != hipSuccess) return ep;
   const int nqt = (a.T + C::BM - 1) / C::BM;
   const int nblk = nqt * a.B * a.H;
   const int W = eff_window(a.T, a.window);
@@ -428,9 +315,10 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   if (attr != hipSuccess) return attr;
   ProfToken t1 = prof_begin(K_FWD, stream);
   hipLaunchKernelGGL((attn_fwd_kernel<D, ROPE>), dim3(nblk), dim3(256), C::LDS_BYTES, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)(ROPE ? a.kr : a.k), (const uint16_t*)a.vt,
-                     (const float*)a.kscale, (const uint16_t*)a.rcos, (const uint16_t*)a.rsin,
-                     (uint16_t*)a.o, a.lse, a.T, a.H, a.H / a.Hkv, a.LT, W, a.eps);
+                     (const uint16_t*)a.q, (const uint16_t*)(ROPE ? a.kr : a.k),
+                     (const uint16_t*)(a.ve ? a.vr : a.v), (const float*)a.kscale,
+                     (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.o, a.lse, a.T, a.H,
+                     a.H / a.Hkv, W, a.eps);
   prof_end(t1);
   return hipGetLastError();
 }

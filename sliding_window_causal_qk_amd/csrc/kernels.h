@@ -14,11 +14,10 @@ struct FwdArgs {
   void* o;
   float* lse;
   float* kscale;  // workspace: [B, Hkv, T]
-  void* vt;       // workspace: bf16 [B, Hkv, D, LT], V transposed, keys permuted (tpos16)
-  int LT;         // row length of vt: T rounded up to a multiple of 64
   const void* rcos;  // bf16 [T, D/2] rotary tables, or null: no rotary embedding
   const void* rsin;
   void* kr;          // workspace (rotary only): bf16 [B, T, Hkv, D], the rotated keys
+  void* vr;          // workspace (gate only): bf16 [B, T, Hkv, D], v + gate ve
   const void* ve;    // bf16 [B, T, Hkv, D] value embedding, or null: no gate
   const void* xg;    // bf16 gate input: token (b, t) at xg + (b T + t) xs, channels 0..31
   int xs;
@@ -73,6 +72,27 @@ constexpr int kTileGroupDq = 2;
 // tokens per block of the first pass of the gate's weight-gradient reduction
 constexpr int kGateTokens = 64;
 
+// The key-side pre-pass of both passes (prep.hip): kscale, and the rotated
+// keys (rcos not null) and gated values (ve not null) the attention kernels
+// read.  gate may be null (the forward does not keep it).
+struct KeyPrepArgs {
+  const void* k;
+  const void* v;
+  const void* rcos;
+  const void* rsin;
+  const void* ve;
+  const void* xg;
+  int xs;
+  const float* gate_w;
+  float* kscale;
+  void* kr;
+  void* vr;
+  float* gate;
+  int B, T, Hkv, D;
+  float eps;
+};
+
+hipError_t launch_key_prep(const KeyPrepArgs& a, int prof_kernel, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 

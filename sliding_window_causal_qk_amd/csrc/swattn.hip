@@ -42,8 +42,6 @@ int check_common(int B, int T, int H, int H_kv, int D, int window, int causal, f
 size_t stats_bytes(int B, int T, int H) { return round_up((size_t)B * H * T * sizeof(float)); }
 
 // Row length of the transposed V copy of the forward: T rounded up to 64.
-int vt_cols(int T) { return (T + 63) / 64 * 64; }
-size_t vt_bytes(int B, int T, int H, int D) { return round_up((size_t)B * H * D * vt_cols(T) * 2); }
 
 }  // namespace
 
@@ -115,7 +113,7 @@ int attn_band_tiles(int T, int window, int rows, int cols, int by_key, int* firs
 
 size_t attn_fwd_gqa_workspace_bytes(int B, int T, int H, int H_kv, int D) {
   if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
-  return stats_bytes(B, T, H_kv) + vt_bytes(B, T, H_kv, D);
+  return stats_bytes(B, T, H_kv);
 }
 
 size_t attn_fwd_workspace_bytes(int B, int T, int H, int D) {
@@ -142,7 +140,8 @@ size_t attn_bwd_rope_workspace_bytes(int B, int T, int H, int H_kv, int D) {
 }
 
 size_t attn_fwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D) {
-  return attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D);
+  if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
+  return attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D) + round_up((size_t)B * T * H_kv * D * 2);
 }
 
 size_t attn_bwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D) {
@@ -217,11 +216,10 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, v
   swattn::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.kscale = static_cast<float*>(workspace);
-  a.vt = static_cast<char*>(workspace) + stats_bytes(B, T, H_kv);
-  a.LT = vt_cols(T);
   a.rcos = x.rope ? x.rcos : nullptr;
   a.rsin = x.rope ? x.rsin : nullptr;
   a.kr = x.rope ? static_cast<char*>(workspace) + attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
+  a.vr = x.gate ? static_cast<char*>(workspace) + attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D) : nullptr;
   a.ve = x.gate ? x.ve : nullptr;
   a.xg = x.xg;
   a.xs = x.xs;

@@ -27,8 +27,10 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # kernel symbol fragment -> short name used by bench.py
-SHORT = (("fwd_prep_kernel", "fwd_prep"), ("attn_fwd_kernel", "attn_fwd"), ("bwd_kscale_kernel", "bwd_kscale"),
-         ("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"))
+# (the key pre-pass is one kernel in both passes: its forward and backward
+# launches share one name and one average)
+SHORT = (("key_prep_kernel", "key_prep"), ("attn_fwd_kernel", "attn_fwd"), ("bwd_dkdv_kernel", "bwd_dkdv"),
+         ("bwd_dq_kernel", "bwd_dq"), ("ve_gate_bwd_kernel", "ve_gate_bwd"), ("ve_gate_dw_kernel", "ve_gate_dw"))
 
 
 def short_name(kernel: str) -> str | None:

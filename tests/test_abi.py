@@ -169,7 +169,7 @@ def test_unsupported(kw):
 def test_workspace_checks():
     need_f = sw.fwd_workspace_bytes(2, 64, 2, 64)
     need_b = sw.bwd_workspace_bytes(2, 64, 2, 64)
-    assert need_f >= 2 * 2 * 64 * 4 + 2 * 2 * 64 * 64 * 2
+    assert need_f >= 2 * 2 * 64 * 4                     # fp32 key scales
     assert need_b >= 2 * 64 * 2 * 64 * 2 + 3 * 2 * 2 * 64 * 4
     assert _fwd(ws=None) == _lib.ATTN_ERR_WORKSPACE
     assert _fwd(wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE
@@ -207,8 +207,8 @@ def test_gqa_validation_and_workspace():
     for H_kv in (1, 2, 4):
         need_f = sw.fwd_workspace_bytes(2, 64, 4, 64, H_kv)
         need_b = sw.bwd_workspace_bytes(2, 64, 4, 64, H_kv)
-        # key scales and V^T cover the H_kv key/value heads only
-        assert need_f >= 2 * H_kv * 64 * 4 + 2 * H_kv * 64 * 64 * 2
+        # the key scales cover the H_kv key/value heads only
+        assert need_f >= 2 * H_kv * 64 * 4
         assert need_b >= 2 * 64 * 4 * 64 * 2 + 3 * 2 * 4 * 64 * 4
         assert _fwd_gqa(H_kv, wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE
         assert _bwd_gqa(H_kv, wsb=need_b - 1) == _lib.ATTN_ERR_WORKSPACE
@@ -309,7 +309,8 @@ def test_ve_outputs_workspace_unsupported():
     assert _fwd_ve(H=32, H_kv=32) == _lib.ATTN_ERR_UNSUPPORTED      # more key/value heads than the gate kernels take
     need_f = sw.fwd_ve_workspace_bytes(2, 64, 4, 64, 2)
     need_b = sw.bwd_ve_workspace_bytes(2, 64, 4, 64, 2)
-    assert need_f == sw.fwd_rope_workspace_bytes(2, 64, 4, 64, 2)
+    # the gated values on top of the rope workspace
+    assert need_f >= sw.fwd_rope_workspace_bytes(2, 64, 4, 64, 2) + 2 * 64 * 2 * 64 * 2
     # gated values, the gate, dz and the partial sums of dgate_w on top of the rope workspace
     assert need_b >= sw.bwd_rope_workspace_bytes(2, 64, 4, 64, 2) + 2 * 64 * 2 * 64 * 2 + 2 * 2 * 2 * 64 * 4
     assert _fwd_ve(wsb=need_f - 1) == _lib.ATTN_ERR_WORKSPACE

@@ -231,9 +231,9 @@ int attn_bwd_ve(const void* q, const void* k, const void* v, const void* ve,
  * Opt-in per-kernel timing, a measurement aid (not part of the operation).
  * While enabled, every kernel launch of attn_fwd / attn_bwd is bracketed by
  * two HIP events recorded on the launch stream.  Kernel ids: 0 fwd_prep
- * (key scales and transposed V, the pre-pass of the forward), 1 attn_fwd
- * (forward attention),
- * 2 bwd_kscale (key scales of the backward), 3 bwd_dkdv (dK and dV),
+ * (the key pre-pass launched by the forward: key scales, and the rotated keys
+ * or gated values when used), 1 attn_fwd (forward attention),
+ * 2 bwd_kscale (the same pre-pass launched by the backward), 3 bwd_dkdv (dK and dV),
  * 4 bwd_dq (dQ, with q_hat, Delta and lse log2(e) for bwd_dkdv),
  * 5 bwd_gate (the value-embedding gate's dx and dW_g, attn_bwd_ve only).
  *   attn_profile_enable(on): clears the totals and starts (on != 0) or stops

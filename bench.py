@@ -14,6 +14,11 @@ number of visible (query, key) pairs: 4 D for the forward (QK^T, PV) and 10 D
 for the backward with recomputation (QK^T, dP, dV, dQ, dK).  Masked pairs,
 extra recomputation and the RMSNorm arithmetic are not credited.
 
+Per-kernel durations come from HIP events on the launch stream.  The events
+around a launch cost the stream a few microseconds, so the timed region
+records only the dominant kernel (the roofline's); the other kernels are
+recorded over a few untimed steps just before it.
+
     python bench.py [--steps K] [--warmup W] [--workload sssl_stack]
 
 Prints one JSON line.
@@ -119,6 +124,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--sample-steps", type=int, default=2,
+                    help="untimed steps before the timed region that record every kernel's launches")
     ap.add_argument("--workload", default="sssl_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -206,8 +213,47 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    import ctypes
     lib = sw.lib()
+
+    def read_kernels(kids, nsteps):
+        """Per-kernel averages of the recorded launches of kernels `kids` over nsteps steps."""
+        res = {}
+        for kid in kids:
+            name, bound = KERNELS[kid]
+            tot = ctypes.c_double()
+            cnt = ctypes.c_longlong()
+            sw.check(lib.attn_profile_read(kid, ctypes.byref(tot), ctypes.byref(cnt)), "attn_profile_read")
+            if cnt.value == 0:
+                continue
+            work = 0.0
+            unit = None
+            for L in layers:
+                amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"], H_kv, wl.rope, wl.ve_gate)
+                work += amt * nsteps
+            secs = tot.value * 1e-3
+            if unit == "flop":
+                achieved, u, peak = work / secs / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
+            else:
+                achieved, u, peak = work / secs / 1e9, "GB/s", PEAK_HBM_GBS
+            res[name] = dict(kid=kid, avg_us=tot.value * 1e3 / cnt.value, launches=cnt.value,
+                             total_ms_per_step=tot.value / nsteps, bound=bound,
+                             achieved=achieved, unit=u, peak=peak, frac=achieved / peak,
+                             work_per_launch=work / cnt.value, work_unit=unit)
+        return res
+
+    # Every kernel's launches in a short untimed sample; the events around
+    # each launch cost the stream a few microseconds, so the timed region
+    # below records only the dominant kernel, whose figures feed the roofline.
     sw.check(lib.attn_profile_enable(1), "attn_profile_enable")
+    for _ in range(args.sample_steps):
+        step()
+    torch.cuda.synchronize()
+    per_kernel = read_kernels(list(KERNELS), args.sample_steps)
+    dom_name = max(per_kernel, key=lambda n: per_kernel[n]["total_ms_per_step"])
+    dom_kid = per_kernel[dom_name]["kid"]
+
+    sw.check(lib.attn_profile_enable_mask(1 << dom_kid), "attn_profile_enable_mask")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -216,36 +262,15 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / args.steps * 1e3
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
-
-    import ctypes
-    per_kernel = {}
-    for kid, (name, bound) in KERNELS.items():
-        tot = ctypes.c_double()
-        cnt = ctypes.c_longlong()
-        sw.check(lib.attn_profile_read(kid, ctypes.byref(tot), ctypes.byref(cnt)), "attn_profile_read")
-        if cnt.value == 0:
-            continue
-        work = 0.0
-        unit = None
-        for L in layers:
-            amt, unit = algorithmic_units(kid, B, T, H, D, L["n_vis"], H_kv, wl.rope, wl.ve_gate)
-            work += amt * args.steps
-        secs = tot.value * 1e-3
-        if unit == "flop":
-            achieved, u, peak = work / secs / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
-        else:
-            achieved, u, peak = work / secs / 1e9, "GB/s", PEAK_HBM_GBS
-        per_kernel[name] = dict(avg_us=tot.value * 1e3 / cnt.value, launches=cnt.value,
-                                total_ms_per_step=tot.value / args.steps, bound=bound,
-                                achieved=achieved, unit=u, peak=peak, frac=achieved / peak,
-                                work_per_launch=work / cnt.value, work_unit=unit)
+    per_kernel.update(read_kernels([dom_kid], args.steps))   # the timed region's own figures
     sw.check(lib.attn_profile_enable(0), "attn_profile_enable")
+    for v in per_kernel.values():
+        v.pop("kid")
 
     flops_step = sum(14 * D * L["n_vis"] * B * H for L in layers)
     flops12_step = sum(12 * D * L["n_vis"] * B * H for L in layers)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    dom_name = max(per_kernel, key=lambda n: per_kernel[n]["total_ms_per_step"])
     dom = per_kernel[dom_name]
     traffic = None
     tf = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -292,6 +317,8 @@ def main():
         "cpu_baseline": cpu,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in per_kernel.items()},
+        "kernels_timing": (f"HIP events on the launch stream: {dom_name} over the timed region, the "
+                           f"other kernels over {args.sample_steps} untimed steps just before it"),
         "kernel_sources_sha": kernel_sources_sha(),
     }
     print(json.dumps(out), flush=True)

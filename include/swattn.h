@@ -238,6 +238,10 @@ int attn_bwd_ve(const void* q, const void* k, const void* v, const void* ve,
  * 5 bwd_gate (the value-embedding gate's dx and dW_g, attn_bwd_ve only).
  *   attn_profile_enable(on): clears the totals and starts (on != 0) or stops
  *     recording; returns ATTN_ERR_HIP if waiting on earlier events failed.
+ *   attn_profile_enable_mask(mask): the same, recording only the kernels
+ *     whose bit (1 << id) is set in mask (0 stops).  Each recorded launch
+ *     costs its stream a few microseconds for the two events, so a caller
+ *     that times whole steps records as few kernels as it needs.
  *   attn_profile_read(kernel, total_ms, launches): waits for the recorded
  *     events and returns the summed milliseconds and launch count of that
  *     kernel since the last enable; ATTN_ERR_INVALID_ARG for a bad id or NULL.
@@ -245,6 +249,7 @@ int attn_bwd_ve(const void* q, const void* k, const void* v, const void* ve,
  * This is the library's only mutable global state; it is mutex-protected.
  */
 int attn_profile_enable(int on);
+int attn_profile_enable_mask(unsigned mask);
 int attn_profile_read(int kernel, double* total_ms, long long* launches);
 const char* attn_kernel_name(int kernel);
 

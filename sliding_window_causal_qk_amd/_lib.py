@@ -21,7 +21,7 @@ EXPORTS = (
     "attn_bwd", "attn_fwd_gqa_workspace_bytes", "attn_fwd_gqa", "attn_bwd_gqa_workspace_bytes",
     "attn_bwd_gqa", "attn_fwd_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope_workspace_bytes",
     "attn_bwd_rope", "attn_fwd_ve_workspace_bytes", "attn_fwd_ve", "attn_bwd_ve_workspace_bytes",
-    "attn_bwd_ve", "attn_profile_enable", "attn_profile_read", "attn_kernel_name",
+    "attn_bwd_ve", "attn_profile_enable", "attn_profile_enable_mask", "attn_profile_read", "attn_kernel_name",
 )
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_ve.restype = c_int
     L.attn_profile_enable.argtypes = [c_int]
     L.attn_profile_enable.restype = c_int
+    L.attn_profile_enable_mask.argtypes = [ctypes.c_uint]
+    L.attn_profile_enable_mask.restype = c_int
     L.attn_profile_read.argtypes = [c_int, ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_longlong)]
     L.attn_profile_read.restype = c_int

@@ -1,7 +1,9 @@
-// Opt-in per-kernel timing: when enabled, every kernel launch is bracketed by
-// two HIP events recorded on the launch stream; attn_profile_read waits for
-// them and sums the elapsed times per kernel.  Disabled (the default), the
-// hooks cost one relaxed atomic load per launch.
+// Opt-in per-kernel timing: when enabled, every launch of a selected kernel is
+// bracketed by two HIP events recorded on the launch stream; attn_profile_read
+// waits for them and sums the elapsed times per kernel.  Disabled (the
+// default), the hooks cost one relaxed atomic load per launch.  The events
+// themselves cost a few microseconds of GPU time per launch, so a caller
+// timing the whole step selects only the kernels it needs.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -19,13 +21,14 @@ struct Rec {
   hipEvent_t start, stop;
 };
 
-std::atomic<bool> g_on{false};
+std::atomic<unsigned> g_mask{0u};   // bit i: kernel i is recorded
 std::mutex g_mu;
 std::vector<Rec> g_recs;
 double g_total_ms[kNumKernels];
 long long g_count[kNumKernels];
 
 const char* kNames[kNumKernels] = {"fwd_prep", "attn_fwd", "bwd_kscale", "bwd_dkdv", "bwd_dq", "bwd_gate"};
+static_assert(kNumKernels <= 32, "one mask bit per kernel");
 
 // fold finished records into the totals; returns false on a HIP error
 bool drain() {
@@ -49,7 +52,7 @@ bool drain() {
 
 ProfToken prof_begin(int kernel, hipStream_t stream) {
   ProfToken t{-1, nullptr, nullptr, stream};
-  if (!g_on.load(std::memory_order_relaxed)) return t;
+  if (((g_mask.load(std::memory_order_relaxed) >> kernel) & 1u) == 0) return t;
   if (hipEventCreate(&t.start) != hipSuccess) return t;
   if (hipEventCreate(&t.stop) != hipSuccess) {
     (void)hipEventDestroy(t.start);
@@ -71,16 +74,18 @@ void prof_end(const ProfToken& t) {
 
 extern "C" {
 
-int attn_profile_enable(int on) {
+int attn_profile_enable_mask(unsigned mask) {
   std::lock_guard<std::mutex> lk(swattn::g_mu);
   bool ok = swattn::drain();
   for (int i = 0; i < swattn::kNumKernels; ++i) {
     swattn::g_total_ms[i] = 0.0;
     swattn::g_count[i] = 0;
   }
-  swattn::g_on.store(on != 0);
+  swattn::g_mask.store(mask & ((1u << swattn::kNumKernels) - 1u));
   return ok ? ATTN_OK : ATTN_ERR_HIP;
 }
+
+int attn_profile_enable(int on) { return attn_profile_enable_mask(on ? ~0u : 0u); }
 
 int attn_profile_read(int kernel, double* total_ms, long long* launches) {
   if (kernel < 0 || kernel >= swattn::kNumKernels || !total_ms || !launches) return ATTN_ERR_INVALID_ARG;

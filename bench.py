@@ -277,7 +277,8 @@ def main():
     if os.path.exists(tf):
         try:
             rec = json.load(open(tf))
-            if rec.get("sources_sha") == kernel_sources_sha() and dom_name in rec.get("kernels", {}):
+            if (rec.get("sources_sha") == kernel_sources_sha() and rec.get("workload") == wl.name
+                    and dom_name in rec.get("kernels", {})):
                 traffic = rec["kernels"][dom_name].get("bytes_per_launch")
         except Exception:
             traffic = None

@@ -80,9 +80,11 @@ struct FwdCfg {
 __device__ __forceinline__ int v_slot(int r, int ch) { return ch ^ (2 * (r & 3)); }
 
 // ROPE: k is the rotated copy written by the pre-pass, and the queries are
-// rotated in the prologue.
+// rotated in the prologue.  At D = 256 the three stage buffers take 100 KB of
+// LDS, so one workgroup runs per CU: the kernel is then built for one wave per
+// SIMD, whose 512 registers hold the accumulators and every operand in flight.
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ kscale,
     const uint16_t* __restrict__ rcos, const uint16_t* __restrict__ rsin,

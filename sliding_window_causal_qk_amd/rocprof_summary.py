@@ -116,7 +116,7 @@ def traffic(args):
         sys.exit("calibration copy (torch.neg) not found in the counter output")
     f_fac = copy_bytes / (fetch[cf[0]] * 1024.0)
     w_fac = copy_bytes / (write[cw[0]] * 1024.0)
-    out = {"sources_sha": kernel_sources_sha(), "copy_mib": args.copy_mib,
+    out = {"sources_sha": kernel_sources_sha(), "workload": args.workload, "copy_mib": args.copy_mib,
            "fetch_factor": f_fac, "write_factor": w_fac,
            "command_fetch": args.command_fetch, "command_write": args.command_write, "kernels": {}}
     lines = [f"# HBM traffic per launch from rocprofv3 counters: {args.title}", "",
@@ -154,6 +154,7 @@ def main():
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
     c.add_argument("--copy-mib", type=int, required=True)
+    c.add_argument("--workload", required=True, help="the bench.py workload the counter runs measured")
     c.add_argument("--command-fetch", required=True)
     c.add_argument("--command-write", required=True)
     c.add_argument("--title", default="")

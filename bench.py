@@ -3,7 +3,8 @@
 on one MI355X, through the C ABI of libswattn.
 
 A step is one pass of the whole hot path over one batch: the forward of every
-layer of the workload, then the backward of every layer in reverse order.  The
+layer of the workload, then the backward of every layer in reverse order (each
+backward reuses its forward's key pre-pass, as a training step would).  The
 default workload is the depth-8 SSSL stack (8 independent layers, windows
 1024 x3, 2048, 1024 x3, 2048; B=64, T=2048, H=4, D=128, bf16), the shape of the
 pages' 5-minute training run.  Inputs are synthetic, seeded and already in HBM
@@ -206,7 +207,7 @@ def main():
         for L in reversed(layers):
             sw.attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], L["W"], True, wl.eps,
                         dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["wsb"], stream=stream, rope=rope,
-                        gate=L.get("gate"))
+                        gate=L.get("gate"), fwd_workspace=L["wsf"])
 
     for _ in range(args.warmup):
         step()

@@ -207,8 +207,8 @@ int attn_bwd_rope(const void* q, const void* k, const void* v,
  * deterministic); dv is the gradient of v.  Every output must be 16-byte
  * aligned and alias no input or other output.  Other rules as for the
  * *_gqa entry points; workspace sizes: *_ve_workspace_bytes (those of the
- * *_rope entry points plus a bf16 [B, T, H_kv, D] copy of the gated values,
- * and for the backward the gate and its gradients).
+ * *_rope entry points plus a bf16 [B, T, H_kv, D] copy of the gated values
+ * and the fp32 [B, H_kv, T] gate, and for the backward the gate's gradients).
  */
 size_t attn_fwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D);
 int attn_fwd_ve(const void* q, const void* k, const void* v, const void* ve,
@@ -226,6 +226,48 @@ int attn_bwd_ve(const void* q, const void* k, const void* v, const void* ve,
                 void* workspace, size_t workspace_bytes,
                 int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
                 void* stream);
+
+/*
+ * Backward passes that reuse the forward's key pre-pass.  Both passes start
+ * with the same per-key work (the QK-RMSNorm scale of every key row of the
+ * "Autoresearch 深度教程" §7.3 norm, and with the §7.4 rotary embedding or the
+ * §5.2.3 value-embedding gate the rotated keys, the gated values and the
+ * gate).  The forward keeps it in its workspace; these entry points read it
+ * there instead of computing it again, which saves one pass over K (and over
+ * V and ve with the gate).
+ * fwd_workspace: the workspace of the attn_fwd / attn_fwd_gqa, attn_fwd_rope
+ * or attn_fwd_ve call (the matching variant, same problem, tables, gate
+ * inputs and eps) that produced o and lse, unchanged since that call;
+ * fwd_workspace_bytes at least that variant's *_workspace_bytes, 256-byte
+ * aligned, read only, and distinct from workspace and every output.
+ * workspace: this call's own, sized as for the corresponding backward.
+ * Results are bit-identical to the corresponding backward; every other
+ * argument, rule and status code is the same.  A NULL or too small
+ * fwd_workspace returns ATTN_ERR_WORKSPACE.
+ */
+int attn_bwd_gqa_reuse(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       const void* fwd_workspace, size_t fwd_workspace_bytes,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                       void* stream);
+int attn_bwd_rope_reuse(const void* q, const void* k, const void* v,
+                        const void* rope_cos, const void* rope_sin,
+                        const void* o, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv,
+                        const void* fwd_workspace, size_t fwd_workspace_bytes,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                        void* stream);
+int attn_bwd_ve_reuse(const void* q, const void* k, const void* v, const void* ve,
+                      const void* xg, int xg_stride, const float* gate_w,
+                      const void* rope_cos, const void* rope_sin,
+                      const void* o, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, void* dve, void* dxg, float* dgate_w,
+                      const void* fwd_workspace, size_t fwd_workspace_bytes,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
+                      void* stream);
 
 /*
  * Opt-in per-kernel timing, a measurement aid (not part of the operation).

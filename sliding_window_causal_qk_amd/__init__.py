@@ -182,11 +182,14 @@ def attn_fwd(q, k, v, window: int, causal: bool = True, eps: float = 1e-6, *,
 
 
 def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float = 1e-6, *,
-             dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None, gate=None):
+             dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None, gate=None,
+             fwd_workspace=None):
     """Backward through the C ABI.  Returns (dq, dk, dv): bf16, dq [B,T,H,D],
     dk and dv shaped like k and v; with gate=(ve, x, gate_w) also dve (bf16,
     like ve), dx32 (bf16 [B, T, 32], the gradient of x's first 32 channels)
-    and dgate_w (fp32 [H_kv, 32])."""
+    and dgate_w (fp32 [H_kv, 32]).  fwd_workspace: the workspace of the
+    attn_fwd call that produced o and lse (same options), left unchanged; the
+    backward then reuses its key pre-pass (the *_reuse entry points)."""
     torch = _torch()
     B, T, H, D = q.shape
     H_kv = k.shape[2] if k.dim() == 4 else -1
@@ -209,26 +212,38 @@ def attn_bwd(q, k, v, o, lse, dout, window: int, causal: bool = True, eps: float
         dgw = torch.empty((H_kv, 32), dtype=torch.float32, device=q.device)
         nbytes = bwd_ve_workspace_bytes(B, T, H, D, H_kv)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
-        st = lib().attn_bwd_ve(_ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(x), x.shape[2], _ptr(gw),
-                               _ptr(rc), _ptr(rs), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                               _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dx32), _ptr(dgw),
-                               ws.data_ptr(), ws.numel(), B, T, H, H_kv, D, int(window),
-                               int(bool(causal)), float(eps), _stream(stream))
+        head = (_ptr(q), _ptr(k), _ptr(v), _ptr(ve), _ptr(x), x.shape[2], _ptr(gw), _ptr(rc), _ptr(rs),
+                _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dve), _ptr(dx32), _ptr(dgw))
+        tail = (ws.data_ptr(), ws.numel(), B, T, H, H_kv, D, int(window), int(bool(causal)), float(eps),
+                _stream(stream))
+        if fwd_workspace is None:
+            st = lib().attn_bwd_ve(*head, *tail)
+        else:
+            st = lib().attn_bwd_ve_reuse(*head, fwd_workspace.data_ptr(), fwd_workspace.numel(), *tail)
         check(st, "attn_bwd_ve")
         return dq, dk, dv, dve, dx32, dgw
     if rope is not None:
         rc, rs = _check_rope(rope, T, D)
         nbytes = bwd_rope_workspace_bytes(B, T, H, D, H_kv)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
-        st = lib().attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(rc), _ptr(rs), _ptr(o), _ptr(lse),
-                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(),
-                                 B, T, H, H_kv, D, int(window), int(bool(causal)), float(eps),
-                                 _stream(stream))
+        head = (_ptr(q), _ptr(k), _ptr(v), _ptr(rc), _ptr(rs), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                _ptr(dk), _ptr(dv))
+        tail = (ws.data_ptr(), ws.numel(), B, T, H, H_kv, D, int(window), int(bool(causal)), float(eps),
+                _stream(stream))
+        if fwd_workspace is None:
+            st = lib().attn_bwd_rope(*head, *tail)
+        else:
+            st = lib().attn_bwd_rope_reuse(*head, fwd_workspace.data_ptr(), fwd_workspace.numel(), *tail)
         check(st, "attn_bwd_rope")
         return dq, dk, dv
     nbytes = bwd_workspace_bytes(B, T, H, D, H_kv)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    if H_kv == H:
+    if fwd_workspace is not None:
+        st = lib().attn_bwd_gqa_reuse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), fwd_workspace.data_ptr(),
+                                      fwd_workspace.numel(), ws.data_ptr(), ws.numel(), B, T, H, H_kv, D,
+                                      int(window), int(bool(causal)), float(eps), _stream(stream))
+    elif H_kv == H:
         st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                             _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(),
                             B, T, H, D, int(window), int(bool(causal)), float(eps), _stream(stream))
@@ -249,16 +264,24 @@ def _make_function():
         def forward(ctx, q, k, v, window, causal, eps, rope_cos, rope_sin, ve, x, gate_w):
             rope = None if rope_cos is None else (rope_cos, rope_sin)
             gate = None if ve is None else (ve, x, gate_w)
-            o, lse = attn_fwd(q, k, v, window, causal, eps, rope=rope, gate=gate)
+            B, T, H, D = q.shape
+            H_kv = k.shape[2]
+            nb = (fwd_ve_workspace_bytes if gate is not None else
+                  fwd_rope_workspace_bytes if rope is not None else fwd_workspace_bytes)(B, T, H, D, H_kv)
+            fws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+            o, lse = attn_fwd(q, k, v, window, causal, eps, rope=rope, gate=gate, workspace=fws)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.cfg = (window, causal, eps, rope, gate)
+            # the forward's key pre-pass (key scales, rotated keys, gated values)
+            # serves the backward too
+            ctx.cfg = (window, causal, eps, rope, gate, fws)
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            window, causal, eps, rope, gate = ctx.cfg
-            g = attn_bwd(q, k, v, o, lse, do.contiguous(), window, causal, eps, rope=rope, gate=gate)
+            window, causal, eps, rope, gate, fws = ctx.cfg
+            g = attn_bwd(q, k, v, o, lse, do.contiguous(), window, causal, eps, rope=rope, gate=gate,
+                         fwd_workspace=fws)
             if gate is None:
                 return g[0], g[1], g[2], None, None, None, None, None, None, None, None
             dq, dk, dv, dve, dx32, dgw = g

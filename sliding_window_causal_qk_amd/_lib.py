@@ -21,7 +21,7 @@ EXPORTS = (
     "attn_bwd", "attn_fwd_gqa_workspace_bytes", "attn_fwd_gqa", "attn_bwd_gqa_workspace_bytes",
     "attn_bwd_gqa", "attn_fwd_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope_workspace_bytes",
     "attn_bwd_rope", "attn_fwd_ve_workspace_bytes", "attn_fwd_ve", "attn_bwd_ve_workspace_bytes",
-    "attn_bwd_ve", "attn_profile_enable", "attn_profile_enable_mask", "attn_profile_read", "attn_kernel_name",
+    "attn_bwd_ve", "attn_bwd_gqa_reuse", "attn_bwd_rope_reuse", "attn_bwd_ve_reuse", "attn_profile_enable", "attn_profile_enable_mask", "attn_profile_read", "attn_kernel_name",
 )
 
 
@@ -90,6 +90,13 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_ve.argtypes = ([c_vp] * 5 + [c_int] + [c_vp] * 12 + [c_vp, c_size] + [c_int] * 7
                               + [c_float, c_vp])
     L.attn_bwd_ve.restype = c_int
+    L.attn_bwd_gqa_reuse.argtypes = [c_vp] * 10 + [c_size, c_vp, c_size] + [c_int] * 7 + [c_float, c_vp]
+    L.attn_bwd_gqa_reuse.restype = c_int
+    L.attn_bwd_rope_reuse.argtypes = [c_vp] * 12 + [c_size, c_vp, c_size] + [c_int] * 7 + [c_float, c_vp]
+    L.attn_bwd_rope_reuse.restype = c_int
+    L.attn_bwd_ve_reuse.argtypes = ([c_vp] * 5 + [c_int] + [c_vp] * 13 + [c_size, c_vp, c_size] + [c_int] * 7
+                                    + [c_float, c_vp])
+    L.attn_bwd_ve_reuse.restype = c_int
     L.attn_profile_enable.argtypes = [c_int]
     L.attn_profile_enable.restype = c_int
     L.attn_profile_enable_mask.argtypes = [ctypes.c_uint]

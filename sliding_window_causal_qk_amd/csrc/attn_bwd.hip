@@ -1014,8 +1014,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   kp.k = a.k; kp.v = a.v; kp.rcos = a.rcos; kp.rsin = a.rsin; kp.ve = a.ve; kp.xg = a.xg; kp.xs = a.xs;
   kp.gate_w = a.gate_w; kp.kscale = a.kscale; kp.kr = a.kr; kp.vr = a.vr; kp.gate = a.gate;
   kp.B = a.B; kp.T = a.T; kp.Hkv = a.Hkv; kp.D = D; kp.eps = a.eps;
-  const hipError_t ep = launch_key_prep(kp, K_BWD_KSCALE, stream);
-  if (ep != hipSuccess) return ep;
+  if (!a.keys_ready) {
+    const hipError_t ep = launch_key_prep(kp, K_BWD_KSCALE, stream);
+    if (ep != hipSuccess) return ep;
+  }
   const int W = eff_window(a.T, a.window);
   {
     // dQ first: it also writes q_hat, Delta and lse log2(e) for dK/dV

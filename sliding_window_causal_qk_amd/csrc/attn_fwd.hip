@@ -303,7 +303,7 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, ROPE>;
   KeyPrepArgs kp;
   kp.k = a.k; kp.v = a.v; kp.rcos = a.rcos; kp.rsin = a.rsin; kp.ve = a.ve; kp.xg = a.xg; kp.xs = a.xs;
-  kp.gate_w = a.gate_w; kp.kscale = a.kscale; kp.kr = a.kr; kp.vr = a.vr; kp.gate = nullptr;
+  kp.gate_w = a.gate_w; kp.kscale = a.kscale; kp.kr = a.kr; kp.vr = a.vr; kp.gate = a.gate;
   kp.B = a.B; kp.T = a.T; kp.Hkv = a.Hkv; kp.D = D; kp.eps = a.eps;
   const hipError_t ep = launch_key_prep(kp, K_FWD_PREP, stream);
   if (ep != hipSuccess) return ep;

@@ -18,6 +18,7 @@ struct FwdArgs {
   const void* rsin;
   void* kr;          // workspace (rotary only): bf16 [B, T, Hkv, D], the rotated keys
   void* vr;          // workspace (gate only): bf16 [B, T, Hkv, D], v + gate ve
+  float* gate;       // workspace (gate only): [B, Hkv, T], kept for a backward that reuses it
   const void* ve;    // bf16 [B, T, Hkv, D] value embedding, or null: no gate
   const void* xg;    // bf16 gate input: token (b, t) at xg + (b T + t) xs, channels 0..31
   int xs;
@@ -58,6 +59,7 @@ struct BwdArgs {
   float* gate;       // workspace: [B, Hkv, T]
   float* dz;         // workspace: [B, T, Hkv], gradient of the gate's pre-sigmoid input
   float* dw_part;    // workspace: [ceil(B T / kGateTokens), Hkv, 32], per-block partial sums of dgate_w
+  bool keys_ready;   // kscale, kr, vr and gate already hold the forward's key pre-pass
   int B, T, H, D;
   int Hkv;        // key/value heads (H is a multiple); k, v, dk, dv have Hkv heads
   int window;

@@ -141,7 +141,8 @@ size_t attn_bwd_rope_workspace_bytes(int B, int T, int H, int H_kv, int D) {
 
 size_t attn_fwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D) {
   if (B < 0 || T < 0 || H < 0 || H_kv < 0 || D < 1) return 0;
-  return attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D) + round_up((size_t)B * T * H_kv * D * 2);
+  return attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D) + round_up((size_t)B * T * H_kv * D * 2) +
+         stats_bytes(B, T, H_kv);
 }
 
 size_t attn_bwd_ve_workspace_bytes(int B, int T, int H, int H_kv, int D) {
@@ -220,6 +221,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, v
   a.rsin = x.rope ? x.rsin : nullptr;
   a.kr = x.rope ? static_cast<char*>(workspace) + attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D) : nullptr;
   a.vr = x.gate ? static_cast<char*>(workspace) + attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D) : nullptr;
+  a.gate = x.gate ? reinterpret_cast<float*>(static_cast<char*>(a.vr) + round_up((size_t)B * T * H_kv * D * 2))
+                  : nullptr;
   a.ve = x.gate ? x.ve : nullptr;
   a.xg = x.xg;
   a.xs = x.xs;
@@ -229,10 +232,14 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, v
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+// reuse: fwd_ws is the workspace of the forward call that produced o and
+// lse; its key scales (and rotated keys, gated values, gate) are used instead
+// of running the key pre-pass again.
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window, int causal,
-             float eps, void* stream, const Extras& x) {
+             float eps, void* stream, const Extras& x, bool reuse = false, const void* fwd_ws = nullptr,
+             size_t fwd_ws_bytes = 0) {
   bool empty;
   int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
@@ -256,6 +263,15 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
                                : attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
+  if (reuse) {
+    if (!fwd_ws) return ATTN_ERR_WORKSPACE;
+    const size_t need_f = x.gate   ? attn_fwd_ve_workspace_bytes(B, T, H, H_kv, D)
+                          : x.rope ? attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D)
+                                   : attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D);
+    if (fwd_ws_bytes < need_f || !aligned(fwd_ws, kAlign) || fwd_ws == workspace) return ATTN_ERR_WORKSPACE;
+    for (int j = 0; j < nout; ++j)
+      if (outs[j] == fwd_ws) return ATTN_ERR_INVALID_ARG;
+  }
 
   char* ws = static_cast<char*>(workspace);
   const size_t qh_bytes = round_up((size_t)B * T * H * D * 2);
@@ -287,6 +303,17 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
     a.dz = reinterpret_cast<float*>(g);
     g += stats_bytes(B, T, H_kv);
     a.dw_part = reinterpret_cast<float*>(g);
+  }
+  a.keys_ready = false;
+  if (reuse) {   // the forward's key pre-pass, in the forward workspace's layout
+    char* f = static_cast<char*>(const_cast<void*>(fwd_ws));
+    a.kscale = reinterpret_cast<float*>(f);
+    if (x.rope) a.kr = f + attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D);
+    if (x.gate) {
+      a.vr = f + attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D);
+      a.gate = reinterpret_cast<float*>(static_cast<char*>(a.vr) + round_up((size_t)B * T * H_kv * D * 2));
+    }
+    a.keys_ready = true;
   }
   a.B = B; a.T = T; a.H = H; a.Hkv = H_kv; a.D = D; a.window = window; a.eps = eps;
   hipError_t e = swattn::launch_bwd(a, static_cast<hipStream_t>(stream));
@@ -386,6 +413,41 @@ int attn_bwd_ve(const void* q, const void* k, const void* v, const void* ve, con
   x.dgate_w = dgate_w;
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H_kv, D,
                   window, causal, eps, stream, x);
+}
+
+int attn_bwd_gqa_reuse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, const void* fwd_workspace,
+                       size_t fwd_workspace_bytes, void* workspace, size_t workspace_bytes, int B,
+                       int T, int H, int H_kv, int D, int window, int causal, float eps,
+                       void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H_kv, D,
+                  window, causal, eps, stream, Extras(), true, fwd_workspace, fwd_workspace_bytes);
+}
+
+int attn_bwd_rope_reuse(const void* q, const void* k, const void* v, const void* rope_cos,
+                        const void* rope_sin, const void* o, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv, const void* fwd_workspace,
+                        size_t fwd_workspace_bytes, void* workspace, size_t workspace_bytes, int B,
+                        int T, int H, int H_kv, int D, int window, int causal, float eps,
+                        void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H_kv, D,
+                  window, causal, eps, stream, rope_extras(rope_cos, rope_sin), true, fwd_workspace,
+                  fwd_workspace_bytes);
+}
+
+int attn_bwd_ve_reuse(const void* q, const void* k, const void* v, const void* ve, const void* xg,
+                      int xg_stride, const float* gate_w, const void* rope_cos,
+                      const void* rope_sin, const void* o, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, void* dve, void* dxg, float* dgate_w,
+                      const void* fwd_workspace, size_t fwd_workspace_bytes, void* workspace,
+                      size_t workspace_bytes, int B, int T, int H, int H_kv, int D, int window,
+                      int causal, float eps, void* stream) {
+  Extras x = gate_extras(ve, xg, xg_stride, gate_w, rope_cos, rope_sin);
+  x.dve = dve;
+  x.dxg = dxg;
+  x.dgate_w = dgate_w;
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, H, H_kv, D,
+                  window, causal, eps, stream, x, true, fwd_workspace, fwd_workspace_bytes);
 }
 
 }  // extern "C"

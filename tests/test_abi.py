@@ -324,3 +324,62 @@ def test_empty_problem_is_ok_and_touches_nothing(kw):
     nulls = dict(q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0)
     assert _fwd(**kw, **nulls) == _lib.ATTN_OK
     assert _bwd(**kw, **nulls, do=None, dq=None, dk=None, dv=None) == _lib.ATTN_OK
+
+
+# ---- backward entry points that reuse the forward's key pre-pass
+
+FWS = P + 20 * 0x1000000   # a distinct, 256-byte aligned fake forward workspace
+
+
+def _bwd_reuse(kind, fws=FWS, fwsb=1 << 40, wsb=1 << 40, **kw):
+    L = _lib.lib()
+    if kind == "gqa":
+        a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], o=ALIGNED[3], lse=ALIGNED[4], do=ALIGNED[5],
+                 dq=ALIGNED[6], dk=ALIGNED[7], dv=ALIGNED[8], ws=ALIGNED[9], B=2, T=64, H=4, H_kv=2, D=64,
+                 window=8, causal=1, eps=1e-6)
+        a.update(kw)
+        return L.attn_bwd_gqa_reuse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                    a["dv"], fws, fwsb, a["ws"], wsb, a["B"], a["T"], a["H"],
+                                    a["H_kv"], a["D"], a["window"], a["causal"], a["eps"], None)
+    if kind == "rope":
+        a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], c=ALIGNED[10], s=ALIGNED[11], o=ALIGNED[3],
+                 lse=ALIGNED[4], do=ALIGNED[5], dq=ALIGNED[6], dk=ALIGNED[7], dv=ALIGNED[8], ws=ALIGNED[9],
+                 B=2, T=64, H=4, H_kv=2, D=64, window=8, causal=1, eps=1e-6)
+        a.update(kw)
+        return L.attn_bwd_rope_reuse(a["q"], a["k"], a["v"], a["c"], a["s"], a["o"], a["lse"], a["do"],
+                                     a["dq"], a["dk"], a["dv"], fws, fwsb, a["ws"], wsb, a["B"], a["T"],
+                                     a["H"], a["H_kv"], a["D"], a["window"], a["causal"], a["eps"], None)
+    a = dict(q=ALIGNED[0], k=ALIGNED[1], v=ALIGNED[2], ve=ALIGNED[3], x=ALIGNED[4], xs=512, gw=ALIGNED[5],
+             c=None, s=None, o=ALIGNED[6], lse=ALIGNED[7], do=ALIGNED[8], dq=ALIGNED[9], dk=ALIGNED[10],
+             dv=ALIGNED[11], dve=P + 12 * 0x1000000, dx=P + 13 * 0x1000000, dgw=P + 14 * 0x1000000,
+             ws=P + 15 * 0x1000000, B=2, T=64, H=4, H_kv=2, D=64, window=8, causal=1, eps=1e-6)
+    a.update(kw)
+    return L.attn_bwd_ve_reuse(a["q"], a["k"], a["v"], a["ve"], a["x"], a["xs"], a["gw"], a["c"], a["s"],
+                               a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["dve"], a["dx"],
+                               a["dgw"], fws, fwsb, a["ws"], wsb, a["B"], a["T"], a["H"], a["H_kv"],
+                               a["D"], a["window"], a["causal"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kind", ["gqa", "rope", "ve"])
+def test_reuse_rejects_bad_forward_workspace(kind):
+    fwd_bytes = {"gqa": sw.fwd_workspace_bytes(2, 64, 4, 64, 2),
+                 "rope": sw.fwd_rope_workspace_bytes(2, 64, 4, 64, 2),
+                 "ve": sw.fwd_ve_workspace_bytes(2, 64, 4, 64, 2)}[kind]
+    ws = ALIGNED[9] if kind != "ve" else P + 15 * 0x1000000
+    dq = ALIGNED[6] if kind != "ve" else ALIGNED[9]
+    assert _bwd_reuse(kind, fws=None) == _lib.ATTN_ERR_WORKSPACE
+    assert _bwd_reuse(kind, fwsb=fwd_bytes - 1) == _lib.ATTN_ERR_WORKSPACE
+    assert _bwd_reuse(kind, fws=FWS + 16) == _lib.ATTN_ERR_WORKSPACE      # not 256-byte aligned
+    assert _bwd_reuse(kind, fws=ws) == _lib.ATTN_ERR_WORKSPACE            # the backward's own workspace
+    assert _bwd_reuse(kind, fws=dq) == _lib.ATTN_ERR_INVALID_ARG          # an output
+    # the other rules are those of the plain backward
+    assert _bwd_reuse(kind, eps=0.0) == _lib.ATTN_ERR_INVALID_ARG
+    assert _bwd_reuse(kind, wsb=0) == _lib.ATTN_ERR_WORKSPACE
+    # an empty problem needs no memory at all
+    assert _bwd_reuse(kind, fws=None, fwsb=0, wsb=0, B=0) == _lib.ATTN_OK
+
+
+def test_forward_ve_workspace_keeps_the_gate():
+    # the gate (fp32 [B, H_kv, T]) follows the gated values in the forward workspace
+    assert (sw.fwd_ve_workspace_bytes(2, 64, 4, 64, 2)
+            >= sw.fwd_rope_workspace_bytes(2, 64, 4, 64, 2) + 2 * 64 * 2 * 64 * 2 + 2 * 2 * 64 * 4)

@@ -497,3 +497,38 @@ def test_empty_and_errors_on_device(torch_dev):
     x = torch.zeros((1, 16, 2, 96), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sw.SwattnError):
         sw.attn_fwd(x, x, x, 4)
+
+
+REUSE_CASES = [
+    # (B, T, H, H_kv, D, W, rope, gate C or 0, seed)
+    (2, 300, 2, 2, 128, 100, False, 0, 80),
+    (1, 257, 4, 2, 64, -1, False, 0, 81),
+    (1, 200, 4, 2, 128, 60, True, 0, 82),
+    (2, 150, 2, 1, 128, 40, False, 64, 83),
+    (1, 130, 2, 2, 256, 30, True, 40, 84),
+]
+
+
+@pytest.mark.parametrize("B,T,H,H_kv,D,W,rope,C,seed", REUSE_CASES,
+                         ids=[f"B{c[0]}T{c[1]}H{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}{'rope' if c[6] else ''}C{c[7]}"
+                              for c in REUSE_CASES])
+def test_backward_reusing_the_forward_workspace_is_bit_identical(torch_dev, B, T, H, H_kv, D, W, rope, C, seed):
+    """The *_reuse entry points read the forward's key pre-pass instead of
+    running it again; every output must equal the plain backward's bit for bit."""
+    import sliding_window_causal_qk_amd as sw
+    torch = torch_dev
+    _say(f"[parity] reuse B={B} T={T} H={H} H_kv={H_kv} D={D} W={W} rope={rope} C={C} seed={seed}")
+    inp = make_layer_inputs(B, T, H, D, seed, H_kv=H_kv)
+    q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
+    tables = tuple(_to_dev(torch, t) for t in rope_tables_bf16(T, D)) if rope else None
+    gate = _gate_dev(torch, make_gate_inputs(B, T, H_kv, D, C, seed + 100)) if C else None
+    nb = (sw.fwd_ve_workspace_bytes if gate is not None else
+          sw.fwd_rope_workspace_bytes if rope else sw.fwd_workspace_bytes)(B, T, H, D, H_kv)
+    fws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    o, lse = sw.attn_fwd(q, k, v, W, True, EPS, rope=tables, gate=gate, workspace=fws)
+    plain = sw.attn_bwd(q, k, v, o, lse, do, W, True, EPS, rope=tables, gate=gate)
+    reuse = sw.attn_bwd(q, k, v, o, lse, do, W, True, EPS, rope=tables, gate=gate, fwd_workspace=fws)
+    torch.cuda.synchronize()
+    assert len(plain) == len(reuse)
+    for i, (a, b) in enumerate(zip(plain, reuse)):
+        assert torch.equal(a, b), f"output {i} differs"

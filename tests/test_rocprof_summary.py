@@ -38,12 +38,13 @@ def test_trace_and_traffic(tmp_path):
     _write(str(d / "w" / "p_counter_collection.csv"), hdr,
            [[1, neg, "WRITE_SIZE", 1024], [2, dq, "WRITE_SIZE", 10], [3, dq, "WRITE_SIZE", 30]])
     subprocess.run([sys.executable, "-m", "sliding_window_causal_qk_amd.rocprof_summary", "traffic",
-                    "--fetch", str(d / "f"), "--write", str(d / "w"), "--copy-mib", "1",
+                    "--fetch", str(d / "f"), "--write", str(d / "w"), "--copy-mib", "1", "--workload", "tiny",
                     "--command-fetch", "a", "--command-write", "b",
                     "--out-json", str(d / "t.json"), "--out-text", str(d / "t.txt")],
                    cwd=ROOT, check=True, capture_output=True)
     rec = json.load(open(d / "t.json"))
     assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
+    assert rec["workload"] == "tiny"
     k = rec["kernels"]["bwd_dq"]
     assert k["launches"] == 2
     assert k["fetch_bytes_per_launch"] == 200 * 1024 * 2.0

@@ -68,11 +68,19 @@ def _close_sum(name, got, want, scale):
                            f"max allowed {(ATOL + RTOL * scale).max():.3g}")
 
 
-def _run(torch, inp, window, eps=EPS):
+def _fwd_ws(torch, nbytes, reuse):
+    """A forward workspace kept for the backward (reuse), else None (the
+    library call allocates its own and the backward runs its own pre-pass)."""
+    return torch.empty(nbytes, dtype=torch.uint8, device="cuda") if reuse else None
+
+
+def _run(torch, inp, window, eps=EPS, reuse=False):
     import sliding_window_causal_qk_amd as sw
     q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
-    o, lse = sw.attn_fwd(q, k, v, window, True, eps)
-    dq, dk, dv = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps)
+    B, T, H, D = q.shape
+    fws = _fwd_ws(torch, sw.fwd_workspace_bytes(B, T, H, D, k.shape[2]), reuse)
+    o, lse = sw.attn_fwd(q, k, v, window, True, eps, workspace=fws)
+    dq, dk, dv = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps, fwd_workspace=fws)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -205,12 +213,14 @@ ROPE_SMALL = [
 ]
 
 
-def _run_rope(torch, inp, tables, window, eps=EPS):
+def _run_rope(torch, inp, tables, window, eps=EPS, reuse=False):
     import sliding_window_causal_qk_amd as sw
     q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
     rope = tuple(_to_dev(torch, t) for t in tables)
-    o, lse = sw.attn_fwd(q, k, v, window, True, eps, rope=rope)
-    dq, dk, dv = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps, rope=rope)
+    B, T, H, D = q.shape
+    fws = _fwd_ws(torch, sw.fwd_rope_workspace_bytes(B, T, H, D, k.shape[2]), reuse)
+    o, lse = sw.attn_fwd(q, k, v, window, True, eps, rope=rope, workspace=fws)
+    dq, dk, dv = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps, rope=rope, fwd_workspace=fws)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -281,13 +291,15 @@ def _gate_dev(torch, gi):
     return ve, x, torch.from_numpy(gi.gate_w.copy()).cuda()
 
 
-def _run_ve(torch, inp, gi, window, tables=None, eps=EPS):
+def _run_ve(torch, inp, gi, window, tables=None, eps=EPS, reuse=False):
     import sliding_window_causal_qk_amd as sw
     q, k, v, do = (_to_dev(torch, t) for t in (inp.q, inp.k, inp.v, inp.do))
     gate = _gate_dev(torch, gi)
     rope = None if tables is None else tuple(_to_dev(torch, t) for t in tables)
-    o, lse = sw.attn_fwd(q, k, v, window, True, eps, rope=rope, gate=gate)
-    grads = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps, rope=rope, gate=gate)
+    B, T, H, D = q.shape
+    fws = _fwd_ws(torch, sw.fwd_ve_workspace_bytes(B, T, H, D, k.shape[2]), reuse)
+    o, lse = sw.attn_fwd(q, k, v, window, True, eps, rope=rope, gate=gate, workspace=fws)
+    grads = sw.attn_bwd(q, k, v, o, lse, do, window, True, eps, rope=rope, gate=gate, fwd_workspace=fws)
     torch.cuda.synchronize()
     return (o, lse) + tuple(grads)
 
@@ -345,22 +357,24 @@ def _sample_rows(T, W, rng, n=6):
 
 
 def _sampled_check(torch, wl, layer, window, slices):
+    # full-size runs take the path bench.py times: the backward reuses the
+    # forward's key pre-pass
     inp = make_layer_inputs(wl.B, wl.T, wl.H, wl.D, wl.seed(layer), wl.sigma_qkv, wl.sigma_do,
                             H_kv=wl.H_kv)
     qf, kf, vf, dof = inp.as_f32()
     if wl.ve_gate:
         # the gated values are v' = v + gate ve: the oracle runs on v' (fp64)
         gi = make_gate_inputs(wl.B, wl.T, wl.kv_heads, wl.D, wl.H * wl.D, wl.seed(layer) + 100)
-        o, lse, dq, dk, dv, dve, dx32, _ = _run_ve(torch, inp, gi, window, None, wl.eps)
+        o, lse, dq, dk, dv, dve, dx32, _ = _run_ve(torch, inp, gi, window, None, wl.eps, reuse=True)
         gate = oracle.ve_gate(bf16_bits_to_f32(np.ascontiguousarray(gi.x[..., :32])), gi.gate_w)
         vef = bf16_bits_to_f32(gi.ve)
         vf = vf + gate[..., None] * vef
     elif wl.rope:
         tables = rope_tables_bf16(wl.T, wl.D)
         c, sn = (bf16_bits_to_f32(t) for t in tables)
-        o, lse, dq, dk, dv = _run_rope(torch, inp, tables, window, wl.eps)
+        o, lse, dq, dk, dv = _run_rope(torch, inp, tables, window, wl.eps, reuse=True)
     else:
-        o, lse, dq, dk, dv = _run(torch, inp, window, wl.eps)
+        o, lse, dq, dk, dv = _run(torch, inp, window, wl.eps, reuse=True)
     rng = np.random.default_rng(1234 + layer)
     for (b, h) in slices:
         rows = _sample_rows(wl.T, window, rng)

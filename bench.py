@@ -13,7 +13,10 @@ when the timed region starts.
 Effective FLOPs (F14): 14 * D * N_vis per (batch, head) and layer, N_vis the
 number of visible (query, key) pairs: 4 D for the forward (QK^T, PV) and 10 D
 for the backward with recomputation (QK^T, dP, dV, dQ, dK).  Masked pairs,
-extra recomputation and the RMSNorm arithmetic are not credited.
+extra recomputation and the RMSNorm arithmetic are not credited.  value_f12
+is the same step on the pages' 12 * D * N_vis count; value_executed_mfma is
+the MFMA work the matrix cores executed (rocprofv3 counters of the same
+workload and kernel sources, profiles/mfma.json; null when those are stale).
 
 Per-kernel durations come from HIP events on the launch stream.  The events
 around a launch cost the stream a few microseconds, so the timed region
@@ -283,6 +286,25 @@ def main():
                 traffic = rec["kernels"][dom_name].get("bytes_per_launch")
         except Exception:
             traffic = None
+    # third figure: the MFMA FLOPs the matrix cores executed (rocprofv3
+    # counters of the same workload and sources, profiles/mfma.json), masked
+    # blocks and recomputation included
+    value_executed = None
+    mf = os.path.join(ROOT, "profiles", "mfma.json")
+    if os.path.exists(mf):
+        try:
+            rec = json.load(open(mf))
+            if rec.get("sources_sha") == kernel_sources_sha() and rec.get("workload") == wl.name:
+                ex = 0.0
+                for name, v in per_kernel.items():
+                    k = rec["kernels"].get(name)
+                    if k:
+                        v["executed_flops_per_launch"] = k["executed_flops_per_launch"]
+                        v["mfma_busy"] = k["mfma_busy"]
+                        ex += k["executed_flops_per_launch"] * len(windows)
+                value_executed = ex / (ms_per_step * 1e-3) / 1e12
+        except Exception:
+            value_executed = None
     roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 3),
                 "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
                 "traffic": traffic,
@@ -315,6 +337,7 @@ def main():
                    "flops_per_step": flops_step, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "value_f12": round(flops12_step / (ms_per_step * 1e-3) / 1e12, 3),
+        "value_executed_mfma": None if value_executed is None else round(value_executed, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -9,9 +9,21 @@ bench.py reports beside its roofline.
     python -m sliding_window_causal_qk_amd.rocprof_summary traffic --fetch DIR1 --write DIR2 \\
         --copy-mib M --command-fetch "..." --command-write "..." --out-json J --out-text FILE
 
+    # executed MFMA work: one counter run of bench.py with
+    #   --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+    python -m sliding_window_causal_qk_amd.rocprof_summary mfma --dir DIR --workload W \
+        --command "..." --out-json J --out-text FILE
+
 FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Each is scaled by the
 ratio of the known byte count of the calibration copy (torch.neg over M MiB of
 fp32: M MiB read, M MiB written) to what the same counter reads for it.
+
+SQ_INSTS_VALU_MFMA_MOPS_BF16 counts bf16 MFMA operations in units of 512, so
+x 512 is the FLOPs the matrix cores executed (masked blocks and recomputation
+included).  The MFMA busy fraction follows rocprofv3's own MfmaUtil metric,
+SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (the per-XCD maximum of
+GRBM_GUI_ACTIVE x SIMDs); rocprofv3 aggregates GRBM_GUI_ACTIVE over the XCDs
+by summing, so its per-XCD value is taken as the sum / XCDS.
 """
 from __future__ import annotations
 
@@ -106,6 +118,46 @@ def _counter_means(d: str, counter: str):
     return {k: statistics.fmean(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
+XCDS, SIMDS = 8, 256 * 4   # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
+
+
+def mfma(args):
+    rows = _rows(_find(args.dir, "counter_collection.csv"))
+    per = {}
+    for r in rows:
+        name = short_name(_col(r, "Kernel_Name", "Kernel-Name"))
+        if name is None:
+            continue
+        key = (name, _col(r, "Dispatch_Id", "Dispatch-Id"))
+        d = per.setdefault(key, {})
+        d[_col(r, "Counter_Name", "Counter-Name")] = float(_col(r, "Counter_Value", "Counter-Value"))
+    agg = {}
+    for (name, _), d in per.items():
+        a = agg.setdefault(name, {"n": 0, "flops": 0.0, "busy": 0.0, "cycles": 0.0})
+        a["n"] += 1
+        a["flops"] += d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        a["busy"] += d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a["cycles"] += d.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+    out = {"sources_sha": kernel_sources_sha(), "workload": args.workload, "command": args.command,
+           "kernels": {}}
+    lines = [f"# Executed MFMA work per launch from rocprofv3 counters: {args.title}", "",
+             "Command (from the repository root):", "", "    " + args.command, "",
+             "Executed FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             f"(GRBM_GUI_ACTIVE / {XCDS} XCDs x {SIMDS} SIMDs), rocprofv3's MfmaUtil.", "",
+             f"{'kernel':<10} {'launches':>8} {'exec_GFLOP':>11} {'mfma_busy':>10}"]
+    for name, a in sorted(agg.items()):
+        n = a["n"]
+        fl = a["flops"] / n
+        busy = a["busy"] / (a["cycles"] * SIMDS) if a["cycles"] else 0.0
+        out["kernels"][name] = {"executed_flops_per_launch": fl, "mfma_busy": busy, "launches": n}
+        lines.append(f"{name:<10} {n:>8} {fl / 1e9:>11.1f} {100 * busy:>9.1f}%")
+    lines += ["", f"kernel sources sha: {out['sources_sha']}"]
+    json.dump(out, open(args.out_json, "w"), indent=1)
+    txt = "\n".join(lines) + "\n"
+    open(args.out_text, "w").write(txt)
+    print(txt)
+
+
 def traffic(args):
     fetch, nf = _counter_means(args.fetch, "FETCH_SIZE")
     write, nw = _counter_means(args.write, "WRITE_SIZE")
@@ -160,8 +212,15 @@ def main():
     c.add_argument("--title", default="")
     c.add_argument("--out-json", required=True)
     c.add_argument("--out-text", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--dir", required=True)
+    m.add_argument("--workload", required=True, help="the bench.py workload the counter run measured")
+    m.add_argument("--command", required=True)
+    m.add_argument("--title", default="")
+    m.add_argument("--out-json", required=True)
+    m.add_argument("--out-text", required=True)
     a = ap.parse_args()
-    trace(a) if a.mode == "trace" else traffic(a)
+    {"trace": trace, "traffic": traffic, "mfma": mfma}[a.mode](a)
 
 
 if __name__ == "__main__":

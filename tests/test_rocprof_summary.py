@@ -50,3 +50,28 @@ def test_trace_and_traffic(tmp_path):
     assert k["fetch_bytes_per_launch"] == 200 * 1024 * 2.0
     assert k["write_bytes_per_launch"] == 20 * 1024
     assert k["bytes_per_launch"] == k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
+
+
+def test_mfma_counters(tmp_path):
+    """Executed FLOPs are MOPS x 512 per dispatch; the busy fraction divides
+    the SIMDs' summed MFMA-busy cycles by the per-XCD active cycles (the
+    aggregated GRBM_GUI_ACTIVE / 8) times the 1024 SIMDs."""
+    d = tmp_path
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = "void swattn::bwd_dkdv_kernel<128, false, false>(int)"
+    rows = []
+    for disp, mops in ((5, 1000), (6, 3000)):
+        rows += [[disp, k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", mops],
+                 [disp, k, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 50],
+                 [disp, k, "GRBM_GUI_ACTIVE", 8 * 200]]
+    _write(str(d / "m" / "p_counter_collection.csv"), hdr, rows)
+    subprocess.run([sys.executable, "-m", "sliding_window_causal_qk_amd.rocprof_summary", "mfma",
+                    "--dir", str(d / "m"), "--workload", "tiny", "--command", "c",
+                    "--out-json", str(d / "m.json"), "--out-text", str(d / "m.txt")],
+                   cwd=ROOT, check=True, capture_output=True)
+    rec = json.load(open(d / "m.json"))
+    assert rec["workload"] == "tiny"
+    r = rec["kernels"]["bwd_dkdv"]
+    assert r["launches"] == 2
+    assert r["executed_flops_per_launch"] == 2000 * 512
+    assert abs(r["mfma_busy"] - 0.25) < 1e-12

@@ -329,10 +329,6 @@ __device__ __forceinline__ void query_tile_of(int lid, int nqt, int nbh, int gb,
   *qt = nqt - 1 - rank;
 }
 
-// Column position of key/query offset x (0..15) inside a transposed 16-column
-// group, arranged so that the 8 values one lane feeds to an MFMA k-step are
-// contiguous: k-group 0 takes offsets {0..3, 8..11}, k-group 1 {4..7, 12..15}.
-__device__ __forceinline__ int tpos16(int x) { return ((x >> 2) & 1) * 8 + (x >> 3) * 4 + (x & 3); }
 
 // Query prologue shared by the forward and dQ kernels: lane (g, c) holds
 // channels 16 ks + 8 g + 0..7 (ks < D / 16) of query qw0 + c as bf16 pairs.

@@ -41,8 +41,6 @@ int check_common(int B, int T, int H, int H_kv, int D, int window, int causal, f
 
 size_t stats_bytes(int B, int T, int H) { return round_up((size_t)B * H * T * sizeof(float)); }
 
-// Row length of the transposed V copy of the forward: T rounded up to 64.
-
 }  // namespace
 
 extern "C" {

@@ -53,6 +53,7 @@ KERNELS = {
     4: ("bwd_dq", "mfma"),
     5: ("bwd_gate", "hbm"),
 }
+FWD_KERNELS = ("fwd_prep", "attn_fwd")
 FLOPS_PER_PAIR_D = {1: 4, 3: 8, 4: 2}
 
 
@@ -338,6 +339,11 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "value_f12": round(flops12_step / (ms_per_step * 1e-3) / 1e12, 3),
         "value_executed_mfma": None if value_executed is None else round(value_executed, 3),
+        # kernel time per step of each pass, from the per-kernel event sums
+        "fwd_kernel_ms_per_step": round(sum(v["total_ms_per_step"] for k, v in per_kernel.items()
+                                            if k in FWD_KERNELS), 4),
+        "bwd_kernel_ms_per_step": round(sum(v["total_ms_per_step"] for k, v in per_kernel.items()
+                                            if k not in FWD_KERNELS), 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -265,7 +265,7 @@ def _make_function():
             rope = None if rope_cos is None else (rope_cos, rope_sin)
             gate = None if ve is None else (ve, x, gate_w)
             B, T, H, D = q.shape
-            H_kv = k.shape[2]
+            H_kv = k.shape[2] if k.dim() == 4 else H   # a malformed k is rejected by attn_fwd
             nb = (fwd_ve_workspace_bytes if gate is not None else
                   fwd_rope_workspace_bytes if rope is not None else fwd_workspace_bytes)(B, T, H, D, H_kv)
             fws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)

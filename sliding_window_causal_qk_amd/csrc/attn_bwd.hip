@@ -236,15 +236,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     return pl;
   };
   auto issue_plan = [&](const DmaPlan& pl, int base) {
-    tile.issue(make_rsrc_u(pl.qh, pl.nbytes), smem, base, w);
-    tile.issue(make_rsrc_u(pl.dO, pl.nbytes), smem, base + C::DO_B, w);
-    dma_row4(make_rsrc(pl.st, pl.nst), smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
+    tile.issue(make_desc_u(pl.qh, pl.nbytes), smem, base, w);
+    tile.issue(make_desc_u(pl.dO, pl.nbytes), smem, base + C::DO_B, w);
+    dma_row4(make_desc(pl.st, pl.nst), smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
   };
   auto issue_kv = [&](const TileGeo& tg) {
     const size_t sbase = kv_base(tg);
-    kvtile.issue(make_rsrc(k + sbase + (size_t)tg.j0 * rs_kv, kslice_bytes - tg.j0 * rsb_kv), smem,
+    kvtile.issue(make_desc(k + sbase + (size_t)tg.j0 * rs_kv, kslice_bytes - tg.j0 * rsb_kv), smem,
                  C::KV_B, w);
-    kvtile.issue(make_rsrc(v + sbase + (size_t)tg.j0 * rs_kv, kslice_bytes - tg.j0 * rsb_kv), smem,
+    kvtile.issue(make_desc(v + sbase + (size_t)tg.j0 * rs_kv, kslice_bytes - tg.j0 * rsb_kv), smem,
                  C::KV_B + C::KVTile::BYTES, w);
   };
 
@@ -588,6 +588,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
     }
   }
+  wait_vmcnt<0>();   // the stream's last (zero-filling) block loads land before the workgroup ends
 }
 
 // ------------------------------------------------------------------ dQ
@@ -705,7 +706,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
   // ---- direct-to-LDS staging of one key step
   typename C::Tile tile;
   tile.init(w, lane, rs_kv);
-  const rsrc_t rks = make_rsrc(kscale + (size_t)(b * Hkv + h / G) * T, w == 0 ? 4LL * T : 0);   // wave 0 loads kscale
+  const u32x4 rks = make_desc(kscale + (size_t)(b * Hkv + h / G) * T, w == 0 ? 4LL * T : 0);   // wave 0 loads kscale
   const uint16_t* k_s = k + kvbase;
   const uint16_t* v_s = v + kvbase;
   // remaining bytes of the key slices from row r0 on, below 2^32 (unsigned arithmetic)
@@ -713,8 +714,8 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
   auto issue_step = [&](int step, int base) {
     const int r0 = (jb0 + step) * C::BN;
     const uint32_t nb = kbytes_u - (uint32_t)r0 * krow_u;
-    tile.issue(make_rsrc_u(k_s + (size_t)r0 * rs_kv, nb), smem, base, w);
-    tile.issue(make_rsrc_u(v_s + (size_t)r0 * rs_kv, nb), smem, base + C::V_B, w);
+    tile.issue(make_desc_u(k_s + (size_t)r0 * rs_kv, nb), smem, base, w);
+    tile.issue(make_desc_u(v_s + (size_t)r0 * rs_kv, nb), smem, base + C::V_B, w);
     dma_row4(rks, smem, base + C::ST_B + 256 * w, (r0 + lane) * 4);
   };
 

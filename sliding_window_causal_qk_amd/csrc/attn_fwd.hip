@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void attn_fwd_kernel(
     const int r = qc / (D / 8), sl = qc % (D / 8);
     return (r * rs_kv + 8 * v_slot(r, sl)) * 2;   // v_slot is its own inverse
   });
-  const rsrc_t rks = make_rsrc(kscale + (size_t)bhk * T, 4LL * T);
+  const u32x4 rks = make_desc(kscale + (size_t)bhk * T, 4LL * T);
   const size_t kvbase = ((size_t)b * T * Hkv + (h / G)) * D;
   const uint16_t* k_s = k + kvbase;
   const uint16_t* v_s = v + kvbase;
@@ -154,8 +154,8 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void attn_fwd_kernel(
   auto issue_step = [&](int step, int base) {
     const int j0 = (jb0 + step) * C::BN;
     const uint32_t nb = kbytes_u - (uint32_t)j0 * krow_u;
-    ktile.issue(make_rsrc_u(k_s + (size_t)j0 * rs_kv, nb), smem, base, w);
-    vtile.issue(make_rsrc_u(v_s + (size_t)j0 * rs_kv, nb), smem, base + C::V_B, w);
+    ktile.issue(make_desc_u(k_s + (size_t)j0 * rs_kv, nb), smem, base, w);
+    vtile.issue(make_desc_u(v_s + (size_t)j0 * rs_kv, nb), smem, base + C::V_B, w);
     if (w == 0) dma_row4(rks, smem, base + C::ST_B, (j0 + lane) * 4);   // wave 0 loads kscale
   };
 

@@ -68,6 +68,44 @@ __device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t nbytes)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcFlags);
 }
 
+#define SW_LDS __attribute__((address_space(3)))   // LDS pointers
+
+// The same descriptor as four scalar words, for the direct-to-LDS loads below.
+__device__ __forceinline__ u32x4 make_desc(const void* base, long long nbytes) {
+  const uint32_t n = nbytes <= 0 ? 0u : (nbytes >= 0x7fffffffLL ? 0x7fffffffu : (uint32_t)nbytes);
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, n, (uint32_t)kRsrcFlags};
+}
+__device__ __forceinline__ u32x4 make_desc_u(const void* base, uint32_t nbytes) {
+  const uint32_t n = nbytes > 0x7fffffffu ? 0x7fffffffu : nbytes;
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, n, (uint32_t)kRsrcFlags};
+}
+
+// ---- direct-to-LDS loads (buffer_load_dword{,x4} ... lds): lane l's 4 or 16
+// bytes land at LDS (M0 + 4 l) or (M0 + 16 l); lanes whose offset is past the
+// descriptor's range write zeros.  They are written as inline assembly so that
+// the compiler does not track them.  It cannot tell which buffer a transposing
+// LDS read touches, and before each one it would otherwise wait for every such
+// load in flight -- including the one just issued for a later step, which
+// would cut the pipelines' prefetch distance to a fraction of a step.  The
+// kernels order these loads themselves: a buffer is read only after
+// s_waitcnt vmcnt and a workgroup barrier that follow its loads, a buffer is
+// refilled only after a barrier that follows its last reads, and no load is in
+// flight when a kernel exits.  The assembly sets no registers; M0 is an input
+// and the one wait state between writing M0 and the load is the s_nop.
+__device__ __forceinline__ uint32_t lds_addr(unsigned char* smem, int off) {
+  return (uint32_t)(uintptr_t)(SW_LDS void*)(smem + off);
+}
+__device__ __forceinline__ void lds_dma16(u32x4 desc, unsigned char* smem, int lds_off, int voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(desc),
+               "{m0}"(lds_addr(smem, lds_off)));
+}
+__device__ __forceinline__ void lds_dma4(u32x4 desc, unsigned char* smem, int lds_off, int voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(desc),
+               "{m0}"(lds_addr(smem, lds_off)));
+}
+
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
@@ -164,7 +202,6 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // of a row-major LDS array: lane i of the group gets the column `col0 + i`, rows
 // row0 .. row0 + 3, as two packed bf16 pairs.
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-#define SW_LDS __attribute__((address_space(3)))
 __device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
   const SW_LDS bf16x4* q = (const SW_LDS bf16x4*)(p);
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<SW_LDS bf16x4*>(q)));
@@ -216,11 +253,9 @@ struct DmaTile {
   }
   // rs_tile: descriptor starting at the tile's first source row;
   // lds_base: byte offset of the tile in dynamic LDS (wave-uniform)
-  __device__ __forceinline__ void issue(rsrc_t rs_tile, unsigned char* smem, int lds_base, int w) const {
+  __device__ __forceinline__ void issue(u32x4 desc, unsigned char* smem, int lds_base, int w) const {
 #pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs_tile, (SW_LDS void*)(smem + lds_base + 1024 * (w + 4 * i)), 16, voff[i], 0, 0, 0);
+    for (int i = 0; i < NIW; ++i) lds_dma16(desc, smem, lds_base + 1024 * (w + 4 * i), voff[i]);
   }
 };
 
@@ -250,12 +285,10 @@ struct DmaTileV {
       voff[i] = o >= 0 ? o : 0x7ffffff0;
     }
   }
-  __device__ __forceinline__ void issue(rsrc_t rs_tile, unsigned char* smem, int lds_base, int w) const {
+  __device__ __forceinline__ void issue(u32x4 desc, unsigned char* smem, int lds_base, int w) const {
 #pragma unroll
     for (int i = 0; i < NIW; ++i)
-      if (i + 1 < NIW || w + NW * i < NI)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs_tile, (SW_LDS void*)(smem + lds_base + 1024 * (w + NW * i)), 16, voff[i], 0, 0, 0);
+      if (i + 1 < NIW || w + NW * i < NI) lds_dma16(desc, smem, lds_base + 1024 * (w + NW * i), voff[i]);
   }
 };
 
@@ -296,8 +329,8 @@ struct RowStage32 {
 };
 
 // One 64-lane 4-byte direct-to-LDS load (256 bytes at lds_base + 4 lane).
-__device__ __forceinline__ void dma_row4(rsrc_t r, unsigned char* smem, int lds_base, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SW_LDS void*)(smem + lds_base), 4, voff, 0, 0, 0);
+__device__ __forceinline__ void dma_row4(u32x4 desc, unsigned char* smem, int lds_base, int voff) {
+  lds_dma4(desc, smem, lds_base, voff);
 }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained), gfx9 encoding.

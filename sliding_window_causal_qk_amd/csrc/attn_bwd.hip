@@ -324,86 +324,146 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         dp_acc = mfma32(lds16(smem, va + C::DO_B + 32 * ks), vf[ks], dp_acc);
       }
     };
-    // B: probabilities and dS of one step (lane (g, c), register r: query
-    // q0 + 8 (r/4) + 4 g + r%4, key kj).  MASKED is a compile-time flag so each
-    // loop version is one straight-line block the scheduler can interleave.
-    auto stage_b = [&](int base, int step, auto masked_c) {
+    // B for the quad q4 of one step: probabilities and dS of the lane's queries
+    // q0 + 8 q4 + 4 g + {0..3} (registers 4 q4 .. 4 q4 + 3 of S and dP), key kj,
+    // given their lse2 (l4) and Delta (d4); the packed bf16 results go to
+    // po / dso.  MASKED is a compile-time flag so each version is straight-line.
+    auto stage_b4 = [&](int step, int q4, f32x4 l4, f32x4 d4, u32x4* po, u32x4* dso, auto masked_c) {
       constexpr bool MASKED = decltype(masked_c)::value;
-      const int vl = base + l_off;
       const int tq = (qb0 + step) * C::BMQ + 4 * g - kj;
+      float p[4], dsv[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 l4 = lds16f(smem, vl + 32 * q4);
-        const f32x4 d4 = lds16f(smem, vl + 256 + 32 * q4);
-        float p[4], dsv[4];
+      for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * ksc - l4[e]);
+      if (MASKED) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[4 * q4 + e] * ksc - l4[e]);
-        if (MASKED) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(tq + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dsv[e] = p[e] * (dp_acc[4 * q4 + e] - d4[e]);
-        const int st = q4 >> 1, el = 2 * (q4 & 1);
-        pf[st][el] = pack_bf16(p[0], p[1]);
-        pf[st][el + 1] = pack_bf16(p[2], p[3]);
-        dsf[st][el] = pack_bf16(dsv[0], dsv[1]);
-        dsf[st][el + 1] = pack_bf16(dsv[2], dsv[3]);
+        for (int e = 0; e < 4; ++e) p[e] = ((unsigned)(tq + 8 * q4 + e) <= (unsigned)lim) ? p[e] : 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsv[e] = p[e] * (dp_acc[4 * q4 + e] - d4[e]);
+      const int st = q4 >> 1, el = 2 * (q4 & 1);
+      po[st][el] = pack_bf16(p[0], p[1]);
+      po[st][el + 1] = pack_bf16(p[2], p[3]);
+      dso[st][el] = pack_bf16(dsv[0], dsv[1]);
+      dso[st][el + 1] = pack_bf16(dsv[2], dsv[3]);
+    };
+    // B of a whole step (the first step of a tile)
+    auto stage_b = [&](int base, int step, auto masked_c) {
+      const int vl = base + l_off;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        stage_b4(step, q4, lds16f(smem, vl + 32 * q4), lds16f(smem, vl + 256 + 32 * q4), pf, dsf, masked_c);
     };
     // C: dV^T[d, kv] += dO^T[d, q] P[q, kv];  dK_hat^T[d, kv] += Q_hat^T[d, q] dS[q, kv]
-    // (element j of a k-step s2 is query 16 s2 + 4 g + (j % 4) + 8 (j / 4))
+    // (element j of a k-step s2 is query 16 s2 + 4 g + (j % 4) + 8 (j / 4)).
+    // Product m = 2 (NB s2 + n) + x: x = 0 adds to dV^T block n, x = 1 to
+    // dK_hat^T block n; its A operand comes from two transposing reads.
+    constexpr int NM = 4 * C::NB;
+    auto c_read = [&](int base, int m) {
+      constexpr int R8 = 2 * 8 * C::P;
+      const int s2 = m / (2 * C::NB), n = (m >> 1) % C::NB;
+      const int off = base + t_off + ((m & 1) ? 0 : C::DO_B) + 2 * (16 * s2 * C::P + 32 * n);
+      const u32x2 x0 = lds_tr4b(smem, off), x1 = lds_tr4b(smem, off + R8);
+      return u32x4{x0[0], x0[1], x1[0], x1[1]};
+    };
+    auto c_mfma = [&](int m, u32x4 a) {
+      const int s2 = m / (2 * C::NB), n = (m >> 1) % C::NB;
+      if (m & 1) acc_dk[n] = mfma32(a, dsf[s2], acc_dk[n]);
+      else acc_dv[n] = mfma32(a, pf[s2], acc_dv[n]);
+    };
     auto stage_c = [&](int base) {
-      const int vt = base + t_off;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int n = 0; n < C::NB; ++n) {
-          constexpr int R8 = 2 * 8 * C::P;
-          const int o = 2 * (16 * s2 * C::P + 32 * n);
-          const u32x2 a0 = lds_tr4b(smem, vt + C::DO_B + o), a1 = lds_tr4b(smem, vt + C::DO_B + o + R8);
-          const u32x2 bb0 = lds_tr4b(smem, vt + o), bb1 = lds_tr4b(smem, vt + o + R8);
-          acc_dv[n] = mfma32(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[s2], acc_dv[n]);
-          acc_dk[n] = mfma32(u32x4{bb0[0], bb0[1], bb1[0], bb1[1]}, dsf[s2], acc_dk[n]);
-        }
-      }
+      for (int m = 0; m < NM; ++m) c_mfma(m, c_read(base, m));
     };
 
     stage_a(b0);
     stage_b(b0, 0, masked);
 
     // One pipelined step: A(it+1), C(it), B(it+1), then the hand-off of the
-    // buffers.  The instruction order inside a step is fixed with schedule
-    // groups: A(it+1)'s reads and MFMAs first, then C(it)'s MFMAs with their
-    // transposed reads, with B(it+1)'s VALU work slotted between.
+    // buffers.  The order is written out and fenced with scheduling barriers
+    // (left to itself the compiler issued each LDS read right before its
+    // product and waited for it there):
+    //   the loads of block it + 2; every read of A(it+1) and C(it)'s first
+    //   reads; A(it+1)'s products; then C(it)'s products, each after the reads
+    //   of the product CA places later, with a quarter of B(it+1) after every
+    //   fourth product (the first once A's results are in), B's lse2 / Delta
+    //   read one quarter ahead.  B(it+1) writes separate registers that C(it+1)
+    //   takes over at the step's end.  At D = 256 the operands of that order do
+    //   not fit in registers and the step keeps the compiler's order.
     auto step_body = [&](int s_next, auto masked_c) {   // B for step s_next of its query head
-      issue_plan(pnext, b2);      // block it + 2 into the free buffer, spread over A
-      stage_a(b1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      issue_plan(pnext, b2);      // block it + 2 into the free buffer
+      if constexpr (D <= 128) {
+        constexpr int CA = 4;     // C operands read ahead
+        const int va = b1 + a_off, vl = b1 + l_off;
+        u32x4 qa[C::KS], da[C::KS], cop[NM];
 #pragma unroll
-      for (int i = 0; i < 2 * C::KS - 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      __builtin_amdgcn_sched_barrier(0);   // A stays ahead of C and B
-      stage_c(b0);
-      stage_b(b1, s_next, masked_c);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          qa[ks] = lds16(smem, va + 32 * ks);
+          da[ks] = lds16(smem, va + C::DO_B + 32 * ks);
+        }
 #pragma unroll
-      for (int i = 0; i < 4 * C::NB - 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-      }
+        for (int m = 0; m < CA; ++m) cop[m] = c_read(b0, m);
+        __builtin_amdgcn_sched_barrier(0);
+        s_acc = f32x16{};
+        dp_acc = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          s_acc = mfma32(qa[ks], kf[ks], s_acc);
+          dp_acc = mfma32(da[ks], vf[ks], dp_acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 pn[2], dn[2];
+        f32x4 l4 = lds16f(smem, vl), d4 = lds16f(smem, vl + 256);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if (m + CA < NM) cop[m + CA] = c_read(b0, m + CA);
+          c_mfma(m, cop[m]);
+          if (m % (NM / 4) == 1) {
+            const int q4 = m / (NM / 4);
+            const f32x4 l4c = l4, d4c = d4;
+            if (q4 < 3) {
+              l4 = lds16f(smem, vl + 32 * (q4 + 1));
+              d4 = lds16f(smem, vl + 256 + 32 * (q4 + 1));
+            }
+            stage_b4(s_next, q4, l4c, d4c, pn, dn, masked_c);
+            // pin the quarter here (its results are otherwise used only at the
+            // step's end, and the optimiser would sink it there)
+            const int st = q4 >> 1, el = 2 * (q4 & 1);
+            asm volatile("" : "+v"(pn[st][el]), "+v"(pn[st][el + 1]), "+v"(dn[st][el]), "+v"(dn[st][el + 1]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        pf[0] = pn[0];
+        pf[1] = pn[1];
+        dsf[0] = dn[0];
+        dsf[1] = dn[1];
+      } else {
+        stage_a(b1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::KS - 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);   // A stays ahead of C and B
+        stage_c(b0);
+        stage_b(b1, s_next, masked_c);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * C::NB - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        // keep B's results inside this step (the compiler would otherwise sink
+        // the softmax below the barrier, away from the MFMAs it should overlap)
+        asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
       }
-      // keep B's results inside this step (the compiler would otherwise sink
-      // the softmax below the barrier, away from the MFMAs it should overlap)
-      asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
       // the next plan and the buffer rotation are scalar work that overlaps the
       // last MFMAs still in flight; the barrier only orders the buffers' contents
       pnext = plan_next();

@@ -240,6 +240,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     tile.issue(make_desc_u(pl.dO, pl.nbytes), smem, base + C::DO_B, w);
     dma_row4(make_desc(pl.st, pl.nst), smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
   };
+  // the same loads one instruction at a time: j < NDMA (q_hat, then dO, then
+  // the statistics row)
+  constexpr int NDMA = 2 * C::Tile::NIW + 1;
+  auto issue_plan_one = [&](const u32x4& dq_, const u32x4& ddo, const u32x4& dst, const DmaPlan& pl, int base,
+                            int j) {
+    if (j < C::Tile::NIW) tile.issue_one(dq_, smem, base, w, j);
+    else if (j < 2 * C::Tile::NIW) tile.issue_one(ddo, smem, base + C::DO_B, w, j - C::Tile::NIW);
+    else dma_row4(dst, smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
+  };
   auto issue_kv = [&](const TileGeo& tg) {
     const size_t sbase = kv_base(tg);
     kvtile.issue(make_desc(k + sbase + (size_t)tg.j0 * rs_kv, kslice_bytes - tg.j0 * rsb_kv), smem,
@@ -382,15 +391,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // buffers.  The order is written out and fenced with scheduling barriers
     // (left to itself the compiler issued each LDS read right before its
     // product and waited for it there):
-    //   the loads of block it + 2; every read of A(it+1) and C(it)'s first
-    //   reads; A(it+1)'s products; then C(it)'s products, each after the reads
+    //   every read of A(it+1) and C(it)'s first reads; A(it+1)'s products with
+    //   the loads of block it + 2 among them, one instruction per pair (a wave
+    //   issues in order, so scalar and memory instructions cost nothing only in
+    //   the shadow of a product); then C(it)'s products, each after the reads
     //   of the product CA places later, with a quarter of B(it+1) after every
-    //   fourth product (the first once A's results are in), B's lse2 / Delta
-    //   read one quarter ahead.  B(it+1) writes separate registers that C(it+1)
-    //   takes over at the step's end.  At D = 256 the operands of that order do
-    //   not fit in registers and the step keeps the compiler's order.
+    //   fourth product (the first once A's results are in) and the next block's
+    //   plan halfway, B's lse2 / Delta read one quarter ahead.  B(it+1) writes
+    //   separate registers that C(it+1) takes over at the step's end.  At
+    //   D = 256 the operands of that order do not fit in registers and the step
+    //   keeps the compiler's order.
     auto step_body = [&](int s_next, auto masked_c) {   // B for step s_next of its query head
-      issue_plan(pnext, b2);      // block it + 2 into the free buffer
       if constexpr (D <= 128) {
         constexpr int CA = 4;     // C operands read ahead
         const int va = b1 + a_off, vl = b1 + l_off;
@@ -402,6 +413,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         }
 #pragma unroll
         for (int m = 0; m < CA; ++m) cop[m] = c_read(b0, m);
+        // block it + 2's loads go out one instruction per pair of A's
+        // products, in the shadow of the matrix pipe
+        const u32x4 dq_ = make_desc_u(pnext.qh, pnext.nbytes), ddo = make_desc_u(pnext.dO, pnext.nbytes);
+        const u32x4 dst = make_desc(pnext.st, pnext.nst);
         __builtin_amdgcn_sched_barrier(0);
         s_acc = f32x16{};
         dp_acc = f32x16{};
@@ -409,7 +424,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         for (int ks = 0; ks < C::KS; ++ks) {
           s_acc = mfma32(qa[ks], kf[ks], s_acc);
           dp_acc = mfma32(da[ks], vf[ks], dp_acc);
+          if (ks < NDMA) issue_plan_one(dq_, ddo, dst, pnext, b2, ks);
+          __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int j = C::KS; j < NDMA; ++j) issue_plan_one(dq_, ddo, dst, pnext, b2, j);
         __builtin_amdgcn_sched_barrier(0);
         u32x4 pn[2], dn[2];
         f32x4 l4 = lds16f(smem, vl), d4 = lds16f(smem, vl + 256);
@@ -430,6 +449,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             const int st = q4 >> 1, el = 2 * (q4 & 1);
             asm volatile("" : "+v"(pn[st][el]), "+v"(pn[st][el + 1]), "+v"(dn[st][el]), "+v"(dn[st][el + 1]));
           }
+          if (m == NM / 2) pnext = plan_next();   // scalar work beside the products
           __builtin_amdgcn_sched_barrier(0);
         }
         pf[0] = pn[0];
@@ -437,6 +457,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         dsf[0] = dn[0];
         dsf[1] = dn[1];
       } else {
+        issue_plan(pnext, b2);      // block it + 2 into the free buffer
         stage_a(b1);
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
@@ -464,9 +485,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         // the softmax below the barrier, away from the MFMAs it should overlap)
         asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
       }
-      // the next plan and the buffer rotation are scalar work that overlaps the
-      // last MFMAs still in flight; the barrier only orders the buffers' contents
-      pnext = plan_next();
+      // the buffer rotation is scalar work that overlaps the last MFMAs still in
+      // flight; the barrier only orders the buffers' contents
+      if constexpr (D > 128) pnext = plan_next();
       const int t_ = b0;
       b0 = b1;
       b1 = b2;

@@ -287,8 +287,11 @@ struct DmaTileV {
   }
   __device__ __forceinline__ void issue(u32x4 desc, unsigned char* smem, int lds_base, int w) const {
 #pragma unroll
-    for (int i = 0; i < NIW; ++i)
-      if (i + 1 < NIW || w + NW * i < NI) lds_dma16(desc, smem, lds_base + 1024 * (w + NW * i), voff[i]);
+    for (int i = 0; i < NIW; ++i) issue_one(desc, smem, lds_base, w, i);
+  }
+  // the wave's i-th instruction alone (i < NIW), for spreading a tile's loads
+  __device__ __forceinline__ void issue_one(u32x4 desc, unsigned char* smem, int lds_base, int w, int i) const {
+    if (i + 1 < NIW || w + NW * i < NI) lds_dma16(desc, smem, lds_base + 1024 * (w + NW * i), voff[i]);
   }
 };
 

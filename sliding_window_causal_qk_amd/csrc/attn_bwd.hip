@@ -413,41 +413,71 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         }
 #pragma unroll
         for (int m = 0; m < CA; ++m) cop[m] = c_read(b0, m);
-        // block it + 2's loads go out one instruction per pair of A's
-        // products, in the shadow of the matrix pipe
+        // block it + 2's loads go out one instruction per product of S, in the
+        // shadow of the matrix pipe
         const u32x4 dq_ = make_desc_u(pnext.qh, pnext.nbytes), ddo = make_desc_u(pnext.dO, pnext.nbytes);
         const u32x4 dst = make_desc(pnext.st, pnext.nst);
+        constexpr bool MASKED = decltype(masked_c)::value;
+        const int tq = (qb0 + s_next) * C::BMQ + 4 * g - kj;
+        f32x4 l4s[4], d4s[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) l4s[q4] = lds16f(smem, vl + 32 * q4);
         __builtin_amdgcn_sched_barrier(0);
         s_acc = f32x16{};
-        dp_acc = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           s_acc = mfma32(qa[ks], kf[ks], s_acc);
-          dp_acc = mfma32(da[ks], vf[ks], dp_acc);
           if (ks < NDMA) issue_plan_one(dq_, ddo, dst, pnext, b2, ks);
           __builtin_amdgcn_sched_barrier(0);
         }
+        // B(it+1) element r (register r of S and dP: query q0 + 8 (r / 4) + 4 g
+        // + r % 4, key kj), as stage_b4 computes it, in two halves: P (the
+        // exponential and the mask) needs only S and runs beside dP's products,
+        // NPA elements there and the rest beside C's first; dS = P (dP - Delta)
+        // and the bf16 packing run beside C(it)'s products.  Each value is pinned
+        // where it is made.
+        float pe[16], de[16];
+        auto p_elem = [&](int r) {
+          const int q4 = r >> 2, i = r & 3;
+          float pr = __builtin_amdgcn_exp2f(s_acc[r] * ksc - l4s[q4][i]);
+          if (MASKED) pr = ((unsigned)(tq + 8 * q4 + i) <= (unsigned)lim) ? pr : 0.f;
+          pe[r] = pr;
+          asm volatile("" : "+v"(pe[r]));
+        };
+        constexpr int NPA = 12;
+        dp_acc = f32x16{};
 #pragma unroll
-        for (int j = C::KS; j < NDMA; ++j) issue_plan_one(dq_, ddo, dst, pnext, b2, j);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          dp_acc = mfma32(da[ks], vf[ks], dp_acc);
+          if (ks + C::KS < NDMA) issue_plan_one(dq_, ddo, dst, pnext, b2, ks + C::KS);
+          if (ks == 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) d4s[q4] = lds16f(smem, vl + 256 + 32 * q4);
+          }
+#pragma unroll
+          for (int r = NPA * ks / C::KS; r < NPA * (ks + 1) / C::KS; ++r) p_elem(r);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 2 * C::KS; j < NDMA; ++j) issue_plan_one(dq_, ddo, dst, pnext, b2, j);
+        constexpr int EPM = 16 / NM;   // dS elements per product of C
         u32x4 pn[2], dn[2];
-        f32x4 l4 = lds16f(smem, vl), d4 = lds16f(smem, vl + 256);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           if (m + CA < NM) cop[m + CA] = c_read(b0, m + CA);
           c_mfma(m, cop[m]);
-          if (m % (NM / 4) == 1) {
-            const int q4 = m / (NM / 4);
-            const f32x4 l4c = l4, d4c = d4;
-            if (q4 < 3) {
-              l4 = lds16f(smem, vl + 32 * (q4 + 1));
-              d4 = lds16f(smem, vl + 256 + 32 * (q4 + 1));
+          if (NPA + m < 16) p_elem(NPA + m);
+#pragma unroll
+          for (int k = 0; k < EPM; ++k) {
+            const int r = EPM * m + k, q4 = r >> 2, i = r & 3;
+            de[r] = pe[r] * (dp_acc[r] - d4s[q4][i]);
+            asm volatile("" : "+v"(de[r]));
+            if (r & 1) {
+              const int st = q4 >> 1, el = 2 * (q4 & 1) + (i >> 1);
+              pn[st][el] = pack_bf16(pe[r - 1], pe[r]);
+              dn[st][el] = pack_bf16(de[r - 1], de[r]);
+              asm volatile("" : "+v"(pn[st][el]), "+v"(dn[st][el]));
             }
-            stage_b4(s_next, q4, l4c, d4c, pn, dn, masked_c);
-            // pin the quarter here (its results are otherwise used only at the
-            // step's end, and the optimiser would sink it there)
-            const int st = q4 >> 1, el = 2 * (q4 & 1);
-            asm volatile("" : "+v"(pn[st][el]), "+v"(pn[st][el + 1]), "+v"(dn[st][el]), "+v"(dn[st][el + 1]));
           }
           if (m == NM / 2) pnext = plan_next();   // scalar work beside the products
           __builtin_amdgcn_sched_barrier(0);

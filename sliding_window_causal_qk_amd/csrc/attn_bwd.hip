@@ -897,19 +897,105 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     stage_b(b0, 0, masked);
   }
 
+  // One step: A(it+1), C(it), B(it+1).  At D <= 128 the order is written out
+  // in fenced regions, as in the dK/dV kernel: S's products (the V operands
+  // read among them), then dP's with twelve of B's sixteen exponentials (P
+  // needs only S), then C's products, each after the transposing reads of the
+  // product CA places later, with the last four exponentials and dS' = P (dP -
+  // Delta) kscale with its packing.  B(it+1) writes separate registers that
+  // C(it+1) takes over.  At D = 256 the compiler orders the step.
   auto step_body = [&](int it, auto masked_c) {
-    stage_a(b1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    if constexpr (D <= 128) {
+      constexpr bool MASKED = decltype(masked_c)::value;
+      constexpr int NC = 2 * C::NB;   // C's products, m = NB s2 + n
+      constexpr int CA = 2;
+      constexpr int R8 = 2 * 8 * C::P;
+      const int va = b1 + a_off, vk = b1 + k_off, vt = b0 + t_off;
+      auto c_read = [&](int m) {
+        const int s2 = m / C::NB, n = m % C::NB;
+        const int off = vt + 2 * (16 * s2 * C::P + 32 * n);
+        const u32x2 x0 = lds_tr4b(smem, off), x1 = lds_tr4b(smem, off + R8);
+        return u32x4{x0[0], x0[1], x1[0], x1[1]};
+      };
+      constexpr int KA = 4;   // S operands read ahead
+      u32x4 ka[C::KS], vv[C::KS], cop[NC];
+      f32x4 k4s[4];
 #pragma unroll
-    for (int i = 0; i < 2 * C::KS - 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int ks = 0; ks < KA; ++ks) ka[ks] = lds16(smem, va + 32 * ks);
+#pragma unroll
+      for (int m = 0; m < CA; ++m) cop[m] = c_read(m);
+      __builtin_amdgcn_sched_barrier(0);
+      s_acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + KA < C::KS) ka[ks + KA] = lds16(smem, va + 32 * (ks + KA));
+        s_acc = mfma32(ka[ks], qf[ks], s_acc);
+        if (ks >= C::KS - KA) vv[ks - (C::KS - KA)] = lds16(smem, va + C::V_B + 32 * (ks - (C::KS - KA)));
+        if (ks == C::KS - 2) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) k4s[q4] = lds16f(smem, vk + 32 * q4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // B(it+1) element r (register r: key j0 + 8 (r / 4) + 4 g + r % 4, query
+      // qi), as stage_b computes it, each value pinned where it is made
+      const int t0 = (jb0 + it + 1) * C::BN + 4 * g + W - qi;
+      float pe[16], de[16];
+      auto p_elem = [&](int r) {
+        const int q4 = r >> 2, i = r & 3;
+        float pr = __builtin_amdgcn_exp2f(s_acc[r] * k4s[q4][i] - lq);
+        if (MASKED) pr = ((unsigned)(t0 + 8 * q4 + i) <= (unsigned)W) ? pr : 0.f;
+        pe[r] = pr;
+        asm volatile("" : "+v"(pe[r]));
+      };
+      constexpr int NPA = 12;
+      dp_acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + KA < C::KS) vv[ks + KA] = lds16(smem, va + C::V_B + 32 * (ks + KA));
+        dp_acc = mfma32(vv[ks], df[ks], dp_acc);
+#pragma unroll
+        for (int r = NPA * ks / C::KS; r < NPA * (ks + 1) / C::KS; ++r) p_elem(r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      constexpr int EPM = 16 / NC;   // dS elements per product of C
+      u32x4 dn[2];
+#pragma unroll
+      for (int m = 0; m < NC; ++m) {
+        if (m + CA < NC) cop[m + CA] = c_read(m + CA);
+        const int s2 = m / C::NB, n = m % C::NB;
+        acc[n] = mfma32(cop[m], dsf[s2], acc[n]);
+#pragma unroll
+        for (int r = NPA + 4 * m / NC; r < NPA + 4 * (m + 1) / NC; ++r) p_elem(r);
+#pragma unroll
+        for (int k = 0; k < EPM; ++k) {
+          const int r = EPM * m + k, q4 = r >> 2, i = r & 3;
+          de[r] = pe[r] * (dp_acc[r] - dlt) * k4s[q4][i];
+          asm volatile("" : "+v"(de[r]));
+          if (r & 1) {
+            const int st = q4 >> 1, el = 2 * (q4 & 1) + (i >> 1);
+            dn[st][el] = pack_bf16(de[r - 1], de[r]);
+            asm volatile("" : "+v"(dn[st][el]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dsf[0] = dn[0];
+      dsf[1] = dn[1];
+    } else {
+      stage_a(b1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * C::KS - 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_c(b0);
+      stage_b(b1, it + 1, masked_c);
+      asm volatile("" ::"v"(dsf[0]), "v"(dsf[1]));
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_c(b0);
-    stage_b(b1, it + 1, masked_c);
-    asm volatile("" ::"v"(dsf[0]), "v"(dsf[1]));
     wait_vmcnt<0>();            // step it + 2 landed
     __syncthreads();
     if (it + 3 < nsteps) issue_step(it + 3, b0);   // buffer of step it, consumed

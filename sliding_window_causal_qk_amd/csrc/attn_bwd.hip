@@ -966,7 +966,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
         const int s2 = m / C::NB, n = m % C::NB;
         acc[n] = mfma32(cop[m], dsf[s2], acc[n]);
 #pragma unroll
-        for (int r = NPA + 4 * m / NC; r < NPA + 4 * (m + 1) / NC; ++r) p_elem(r);
+        for (int r = NPA + (16 - NPA) * m / NC; r < NPA + (16 - NPA) * (m + 1) / NC; ++r) p_elem(r);
 #pragma unroll
         for (int k = 0; k < EPM; ++k) {
           const int r = EPM * m + k, q4 = r >> 2, i = r & 3;

@@ -388,19 +388,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     stage_b(b0, 0, masked);
 
     // One pipelined step: A(it+1), C(it), B(it+1), then the hand-off of the
-    // buffers.  The order is written out and fenced with scheduling barriers
-    // (left to itself the compiler issued each LDS read right before its
-    // product and waited for it there):
-    //   every read of A(it+1) and C(it)'s first reads; A(it+1)'s products with
-    //   the loads of block it + 2 among them, one instruction per pair (a wave
-    //   issues in order, so scalar and memory instructions cost nothing only in
-    //   the shadow of a product); then C(it)'s products, each after the reads
-    //   of the product CA places later, with a quarter of B(it+1) after every
-    //   fourth product (the first once A's results are in) and the next block's
-    //   plan halfway, B's lse2 / Delta read one quarter ahead.  B(it+1) writes
-    //   separate registers that C(it+1) takes over at the step's end.  At
-    //   D = 256 the operands of that order do not fit in registers and the step
-    //   keeps the compiler's order.
+    // buffers.  One wave per SIMD issues in order, so a VALU, scalar or memory
+    // instruction costs nothing only in the shadow of a product it does not
+    // depend on.  Left to itself the compiler issued each LDS read right before
+    // its product and waited for it there, and sank the softmax next to C's
+    // products alone; the order is therefore written out in regions fenced with
+    // scheduling barriers:
+    //   every read of A(it+1), C(it)'s first CA and B's lse2;
+    //   S's products, with block it + 2's loads between them (one each);
+    //   dP's products, with NPA of B(it+1)'s exponentials between them (P needs
+    //   only S) and B's Delta read;
+    //   C(it)'s products, each after the reads of the product CA places later,
+    //   with the remaining exponentials, dS = P (dP - Delta) and the bf16
+    //   packing between them, and the next block's plan halfway.
+    // B(it+1) writes separate registers that C(it+1) takes over at the step's
+    // end.  At D = 256 the operands of that order do not fit in registers and
+    // the step keeps the compiler's order.
     auto step_body = [&](int s_next, auto masked_c) {   // B for step s_next of its query head
       if constexpr (D <= 128) {
         constexpr int CA = 4;     // C operands read ahead

@@ -18,10 +18,20 @@ is the same step on the pages' 12 * D * N_vis count; value_executed_mfma is
 the MFMA work the matrix cores executed (rocprofv3 counters of the same
 workload and kernel sources, profiles/mfma.json; null when those are stale).
 
-Per-kernel durations come from HIP events on the launch stream.  The events
-around a launch cost the stream a few microseconds, so the timed region
-records only the dominant kernel (the roofline's); the other kernels are
-recorded over a few untimed steps just before it.
+Timing: `value` and `ms_per_step` come from the wall clock over exactly K
+steps between two device synchronisations.  Every timed step also records HIP
+events on the launch stream at its start, after its forwards and at its end;
+their medians give the forward, backward and whole-step times.  Per-kernel
+durations come from HIP events around each launch; they cost the stream a few
+microseconds each, so the timed region brackets only the dominant kernel (the
+roofline's) and the other kernels are recorded over a few untimed steps just
+before it.
+
+After the headline workload the same run measures the other single-GPU
+workloads of the method's configuration list (the S layer, the L layer and the
+long-context SSSL period: keys s_layer, l_layer, long) with the same step
+definition.  The CPU baseline (the fp64 oracle) runs first, before anything
+touches the GPU, over a process pool with one BLAS thread per process.
 
     python bench.py [--steps K] [--warmup W] [--workload sssl_stack]
 
@@ -33,6 +43,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -41,7 +52,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (AMD's published figure)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+BF16_FLOP_PER_CLK_CU = 4096   # gfx950 dense bf16 MFMA FLOP per clock per compute unit
 METRIC = "attn fwd+bwd effective TFLOP/s & % bf16 MFMA peak, T=2048 H=4 D=128 SSSL"
+EXTRA_WORKLOADS = ("s_layer", "l_layer", "long")
+MAX_POOL = 16                 # host worker processes at most (one GPU's share of the host)
 
 # algorithmic work credited to each kernel, per visible pair (FLOPs = c * D * N_vis)
 # or per launch bytes for the memory-bound passes
@@ -87,91 +101,84 @@ def algorithmic_units(kid, B, T, H, D, n_vis, H_kv=None, rope=False, gate=False)
     return 2 * E_kv + 4 * B * H_kv * T + extra, "byte"
 
 
-def cpu_baseline(wl, windows, budget_s):
-    """Time the fp64 oracle (as it stands) on (batch, head) slices of the
-    workload's layers, cycling through the layer windows, for about budget_s."""
-    import numpy as np
+# ------------------------------------------------------------------ CPU baseline
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_slice(task):
+    """One (batch, head) slice through the fp64 oracle, forward then backward,
+    on one BLAS thread.  Returns (seconds, F14 FLOPs credited)."""
+    T, D, W, seed, sigma_qkv, sigma_do, eps = task
+    from threadpoolctl import threadpool_limits
     import oracle
     from workloads import make_layer_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    flops = 0.0
-    n = 0
-    dt = 0.0
-    layer = 0
-    while dt < budget_s:
-        W = windows[layer % len(windows)]
-        inp = make_layer_inputs(1, wl.T, 1, wl.D, wl.seed(layer), wl.sigma_qkv, wl.sigma_do)
+    with threadpool_limits(limits=1):
+        inp = make_layer_inputs(1, T, 1, D, seed, sigma_qkv, sigma_do)
         q, k, v, do = inp.as_f32()
-        ts = time.perf_counter()
-        oracle.attention_fwd(q, k, v, W, True, wl.eps)
-        oracle.attention_bwd(q, k, v, do, W, True, wl.eps)
-        dt += time.perf_counter() - ts
-        flops += 14 * wl.D * oracle.n_visible(wl.T, W)
-        n += 1
-        layer += 1
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, W, True, eps)
+        oracle.attention_bwd(q, k, v, do, W, True, eps)
+        dt = time.perf_counter() - t0
+    return dt, 14 * D * oracle.n_visible(T, W)
+
+
+def cpu_baseline(wl, windows, budget_s):
+    """Time the fp64 oracle (as it stands) on (batch, head) slices of the
+    workload's layers, cycling through the layer windows, over a pool of
+    worker processes with one BLAS thread each, for about budget_s of wall
+    time.  Runs before the GPU is touched, so the workers start from a clean
+    interpreter."""
+    import multiprocessing as mp
+    affinity = len(os.sched_getaffinity(0))
+    n = max(1, min(affinity, MAX_POOL))
+    tasks = [(wl.T, wl.D, windows[i % len(windows)], wl.seed(i % len(windows)) + 7919 * (i // len(windows)),
+              wl.sigma_qkv, wl.sigma_do, wl.eps) for i in range(100000)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(n) as pool:
+        pool.map(_oracle_slice, tasks[:n])                       # warm the workers (imports)
+        t0 = time.perf_counter()
+        first = pool.map(_oracle_slice, tasks[n:2 * n])          # one round to size the sample
+        t1 = time.perf_counter() - t0
+        rounds = max(1, int(budget_s / max(t1, 1e-3)) - 1)
+        rest = pool.map(_oracle_slice, tasks[2 * n:2 * n + rounds * n])
+        wall = time.perf_counter() - t0
+    done = first + rest
+    flops = sum(f for _, f in done)
     return {
-        "value": flops / dt / 1e12,
+        "value": flops / wall / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": n,
         "kind": "oracle",
-        "sample": (f"{n} (batch, head) slices of T={wl.T}, D={wl.D} cycling through the layer "
-                   f"windows {sorted(set(windows))}, fp64 numpy forward + backward, {dt:.1f} s "
-                   f"of oracle time; F14 credited per slice"),
+        "sample": (f"{len(done)} (batch, head) slices of T={wl.T}, D={wl.D} cycling through the layer "
+                   f"windows {sorted(set(windows))}, fp64 numpy forward + backward, one slice per task on "
+                   f"{n} worker processes with one BLAS thread each, {wall:.1f} s wall; F14 credited per "
+                   f"slice"),
+        "affinity_cores": affinity,
+        "cpu_count": os.cpu_count(),
+        "cpu_model": _cpu_model(),
+        "busy_s": round(sum(t for t, _ in done), 2),
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--sample-steps", type=int, default=2,
-                    help="untimed steps before the timed region that record every kernel's launches")
-    ap.add_argument("--workload", default="sssl_stack")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="first run a plain elementwise copy (torch.neg, fp32) over this many MiB, "
-                         "the reference point for scaling HBM counters")
-    args = ap.parse_args()
+# ------------------------------------------------------------------ GPU side
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this attention path has no multi-GPU mode: every (batch, head) is independent, so a "
-              "data-parallel run is N independent copies of the one-GPU figure.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import sliding_window_causal_qk_amd as sw
-    from workloads import make_layer_inputs_device, rope_tables_bf16, workload
-
-    wl = workload(args.workload)
+def _setup(wl, sw, torch, dev):
+    """Inputs, outputs and workspaces of every layer of the workload."""
+    from workloads import make_layer_inputs_device, rope_tables_bf16
     B, T, H, D, H_kv = wl.B, wl.T, wl.H, wl.D, wl.kv_heads
     if wl.explicit_window is not None:
         windows = [wl.explicit_window] * wl.n_layer
     else:
         windows = sw.layer_windows(wl.pattern, wl.n_layer, T)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    print(f"[bench] workload {wl.name}: B={B} T={T} H={H} H_kv={H_kv} D={D} windows={windows}",
-          file=sys.stderr, flush=True)
-
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 18          # fp32 elements
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            torch.neg(src, out=dst)              # reads and writes n * 4 bytes
-        torch.cuda.synchronize()
-        del src, dst
-        print(f"[bench] copy calibration: 2 launches of {args.copy_calibration_mib} MiB read + "
-              f"{args.copy_calibration_mib} MiB written", file=sys.stderr, flush=True)
-
     rope = None
     if wl.rope:
         rope = tuple(torch.from_numpy(t.view("int16")).view(torch.bfloat16).to(dev)
@@ -200,25 +207,37 @@ def main():
                 torch.randn((B, T, H * D), generator=g, device=dev).to(torch.bfloat16),
                 torch.randn((H_kv, 32), generator=g, device=dev) * 0.2)
     torch.cuda.synchronize()
+    return layers, windows, rope
 
+
+def measure(wl, args, sw, torch, dev, want_traffic=True):
+    """Times the workload's step; returns a dict of figures."""
+    import ctypes
+    B, T, H, D, H_kv = wl.B, wl.T, wl.H, wl.D, wl.kv_heads
+    layers, windows, rope = _setup(wl, sw, torch, dev)
+    print(f"[bench] workload {wl.name}: B={B} T={T} H={H} H_kv={H_kv} D={D} windows={windows}",
+          file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def fwd_all():
         for L in layers:
             sw.attn_fwd(L["q"], L["k"], L["v"], L["W"], True, wl.eps,
                         out=L["o"], lse=L["lse"], workspace=L["wsf"], stream=stream, rope=rope,
                         gate=L.get("gate"))
+
+    def bwd_all():
         for L in reversed(layers):
             sw.attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], L["W"], True, wl.eps,
                         dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=L["wsb"], stream=stream, rope=rope,
                         gate=L.get("gate"), fwd_workspace=L["wsf"])
 
+    steps = args.steps if wl.name == args.workload else max(args.steps, args.extra_steps)
     for _ in range(args.warmup):
-        step()
+        fwd_all()
+        bwd_all()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    import ctypes
     lib = sw.lib()
 
     def read_kernels(kids, nsteps):
@@ -247,46 +266,55 @@ def main():
                              work_per_launch=work / cnt.value, work_unit=unit)
         return res
 
-    # Every kernel's launches in a short untimed sample; the events around
-    # each launch cost the stream a few microseconds, so the timed region
-    # below records only the dominant kernel, whose figures feed the roofline.
+    # every kernel's launches over a short untimed sample
     sw.check(lib.attn_profile_enable(1), "attn_profile_enable")
     for _ in range(args.sample_steps):
-        step()
+        fwd_all()
+        bwd_all()
     torch.cuda.synchronize()
     per_kernel = read_kernels(list(KERNELS), args.sample_steps)
     dom_name = max(per_kernel, key=lambda n: per_kernel[n]["total_ms_per_step"])
     dom_kid = per_kernel[dom_name]["kid"]
 
+    # the timed region: K steps between two synchronisations; per-step events on
+    # the launch stream, and events around the dominant kernel's launches only
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     sw.check(lib.attn_profile_enable_mask(1 << dom_kid), "attn_profile_enable_mask")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        fwd_all()
+        ev[s][1].record(stream)
+        bwd_all()
+        ev[s][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) / args.steps * 1e3
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
-    per_kernel.update(read_kernels([dom_kid], args.steps))   # the timed region's own figures
+    ms_per_step = (t1 - t0) / steps * 1e3
+    per_kernel.update(read_kernels([dom_kid], steps))   # the timed region's own figures
     sw.check(lib.attn_profile_enable(0), "attn_profile_enable")
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    print(f"[bench] {wl.name}: timed {steps} steps: {ms_per_step:.3f} ms/step (wall), "
+          f"{statistics.median(step_ms):.3f} ms median (events)", file=sys.stderr, flush=True)
     for v in per_kernel.values():
         v.pop("kid")
 
     flops_step = sum(14 * D * L["n_vis"] * B * H for L in layers)
     flops12_step = sum(12 * D * L["n_vis"] * B * H for L in layers)
-    value = flops_step / (ms_per_step * 1e-3) / 1e12
-
     dom = per_kernel[dom_name]
     traffic = None
-    tf = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if os.path.exists(tf):
-        try:
-            rec = json.load(open(tf))
-            if (rec.get("sources_sha") == kernel_sources_sha() and rec.get("workload") == wl.name
-                    and dom_name in rec.get("kernels", {})):
-                traffic = rec["kernels"][dom_name].get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    if want_traffic:
+        tf = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+        if os.path.exists(tf):
+            try:
+                rec = json.load(open(tf))
+                if (rec.get("sources_sha") == kernel_sources_sha() and rec.get("workload") == wl.name
+                        and dom_name in rec.get("kernels", {})):
+                    traffic = rec["kernels"][dom_name].get("bytes_per_launch")
+            except Exception:
+                traffic = None
     # third figure: the MFMA FLOPs the matrix cores executed (rocprofv3
     # counters of the same workload and sources, profiles/mfma.json), masked
     # blocks and recomputation included
@@ -306,25 +334,130 @@ def main():
                 value_executed = ex / (ms_per_step * 1e-3) / 1e12
         except Exception:
             value_executed = None
-    roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 3),
-                "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
-                "traffic": traffic,
-                "work_per_launch": dom["work_per_launch"], "work_unit": dom["work_unit"],
-                "avg_launch_us": round(dom["avg_us"], 2)}
+    res = dict(
+        wl=wl, windows=windows, steps=steps, ms_per_step=ms_per_step,
+        step_ms_median=statistics.median(step_ms), fwd_ms_median=statistics.median(fwd_ms),
+        bwd_ms_median=statistics.median(bwd_ms), flops_step=flops_step, flops12_step=flops12_step,
+        value=flops_step / (ms_per_step * 1e-3) / 1e12, per_kernel=per_kernel, dom_name=dom_name,
+        traffic=traffic, value_executed=value_executed,
+    )
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
+
+def _r(x, n=4):
+    return None if x is None else round(x, n)
+
+
+def summary(res, peak):
+    """The compact figures of one workload (for the extra keys)."""
+    dom = res["per_kernel"][res["dom_name"]]
+    return {
+        "config": {"B": res["wl"].B, "T": res["wl"].T, "H": res["wl"].H, "D": res["wl"].D,
+                   "windows": res["windows"]},
+        "steps": res["steps"],
+        "ms_per_step": _r(res["ms_per_step"]),
+        "value": _r(res["value"], 3),
+        "pct_of_bf16_peak": _r(100.0 * res["value"] / peak, 2),
+        "step_ms_median_events": _r(res["step_ms_median"]),
+        "fwd_ms_median_events": _r(res["fwd_ms_median"]),
+        "bwd_ms_median_events": _r(res["bwd_ms_median"]),
+        "dominant_kernel": res["dom_name"],
+        "dominant_frac": _r(dom["frac"]),
+        "dominant_avg_us": _r(dom["avg_us"], 2),
+        "kernels": {k: {"avg_us": _r(v["avg_us"], 2), "frac": _r(v["frac"])}
+                    for k, v in res["per_kernel"].items()},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--sample-steps", type=int, default=2,
+                    help="untimed steps before the timed region that record every kernel's launches")
+    ap.add_argument("--workload", default="sssl_stack")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other single-GPU workloads (s_layer, l_layer, long)")
+    ap.add_argument("--extra-steps", type=int, default=50,
+                    help="timed steps of each extra workload (at least --steps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain elementwise copy (torch.neg, fp32) over this many MiB, "
+                         "the reference point for scaling HBM counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this attention path has no multi-GPU mode: every (batch, head) is independent, so a "
+              "data-parallel run is N independent copies of the one-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import workload
+    wl = workload(args.workload)
+
+    # the CPU baseline first: its worker processes start before anything touches the GPU
     cpu = None
     if not args.no_cpu_baseline:
+        import oracle   # the library is not loaded yet: the windows from the oracle's layer rule
+        windows = ([wl.explicit_window] * wl.n_layer if wl.explicit_window is not None
+                   else oracle.layer_windows(wl.pattern, wl.n_layer, wl.T))
         print(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, windows, args.cpu_seconds)
+        print(f"[bench] cpu baseline: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} processes",
+              file=sys.stderr, flush=True)
 
+    import torch
+    import sliding_window_causal_qk_amd as sw
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cus, clk = ctypes_device_info(sw)
+    peak_derived = cus * BF16_FLOP_PER_CLK_CU * clk * 1e3 / 1e12 if cus and clk else None
+    print(f"[bench] device: {cus} compute units, peak clock {clk / 1e3:.0f} MHz -> bf16 dense peak "
+          f"{peak_derived:.1f} TFLOP/s (published {PEAK_BF16_TFLOPS:.0f})", file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 18          # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)              # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] copy calibration: 2 launches of {args.copy_calibration_mib} MiB read + "
+              f"{args.copy_calibration_mib} MiB written", file=sys.stderr, flush=True)
+
+    main_res = measure(wl, args, sw, torch, dev)
+    extras = {}
+    if not args.no_extra and args.workload == "sssl_stack":
+        for name in EXTRA_WORKLOADS:
+            extras[name] = summary(measure(workload(name), args, sw, torch, dev, want_traffic=False),
+                                   PEAK_BF16_TFLOPS)
+
+    r = main_res
+    B, T, H, D, H_kv = wl.B, wl.T, wl.H, wl.D, wl.kv_heads
+    per_kernel = r["per_kernel"]
+    dom_name = r["dom_name"]
+    dom = per_kernel[dom_name]
+    roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 3),
+                "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
+                "traffic": r["traffic"],
+                "work_per_launch": dom["work_per_launch"], "work_unit": dom["work_unit"],
+                "avg_launch_us": round(dom["avg_us"], 2)}
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": round(r["value"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -333,17 +466,20 @@ def main():
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "H_kv": H_kv, "D": D, "rope": wl.rope,
                    "ve_gate": wl.ve_gate,
                    "pattern": wl.pattern,
-                   "n_layer": len(windows), "windows": windows, "eps": wl.eps,
+                   "n_layer": len(r["windows"]), "windows": r["windows"], "eps": wl.eps,
                    "flop_convention": "F14 = 14*D*N_vis per (batch, head, layer)",
-                   "flops_per_step": flops_step, "parallelism": "single GPU"},
-        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "value_f12": round(flops12_step / (ms_per_step * 1e-3) / 1e12, 3),
-        "value_executed_mfma": None if value_executed is None else round(value_executed, 3),
-        # kernel time per step of each pass, from the per-kernel event sums
-        "fwd_kernel_ms_per_step": round(sum(v["total_ms_per_step"] for k, v in per_kernel.items()
-                                            if k in FWD_KERNELS), 4),
-        "bwd_kernel_ms_per_step": round(sum(v["total_ms_per_step"] for k, v in per_kernel.items()
-                                            if k not in FWD_KERNELS), 4),
+                   "flops_per_step": r["flops_step"], "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * r["value"] / PEAK_BF16_TFLOPS, 2),
+        "peak_bf16_published_tflops": PEAK_BF16_TFLOPS,
+        "peak_bf16_derived_tflops": _r(peak_derived, 1),
+        "device": {"compute_units": cus, "peak_clock_mhz": clk / 1e3 if clk else None,
+                   "bf16_flop_per_clk_per_cu": BF16_FLOP_PER_CLK_CU},
+        "value_f12": round(r["flops12_step"] / (r["ms_per_step"] * 1e-3) / 1e12, 3),
+        "value_executed_mfma": _r(r["value_executed"], 3),
+        # medians over the timed steps of HIP events on the launch stream
+        "step_ms_median_events": round(r["step_ms_median"], 4),
+        "fwd_ms_median_events": round(r["fwd_ms_median"], 4),
+        "bwd_ms_median_events": round(r["bwd_ms_median"], 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
@@ -352,7 +488,16 @@ def main():
                            f"other kernels over {args.sample_steps} untimed steps just before it"),
         "kernel_sources_sha": kernel_sources_sha(),
     }
+    out.update(extras)
     print(json.dumps(out), flush=True)
+
+
+def ctypes_device_info(sw):
+    import ctypes
+    cus, clk = ctypes.c_int(), ctypes.c_int()
+    if sw.lib().attn_device_info(0, ctypes.byref(cus), ctypes.byref(clk)) != 0:
+        return None, None
+    return cus.value, clk.value
 
 
 if __name__ == "__main__":

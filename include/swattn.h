@@ -25,7 +25,12 @@
  * tutorial's CausalSelfAttention views its projections in.  lse is fp32
  * [B, H, T].  All tensor and workspace pointers are DEVICE pointers owned by
  * the caller and must be 16-byte aligned (workspaces 256-byte aligned).
- * Outputs are overwritten, never accumulated, and must not alias inputs.
+ * Outputs are overwritten, never accumulated.  No output may share a byte
+ * with an input, another output or the workspace, and the workspace may
+ * share none with an input or an output; the library checks this on the
+ * byte ranges the sizes imply and rejects a call that breaks it (an output:
+ * ATTN_ERR_INVALID_ARG; the workspace: ATTN_ERR_WORKSPACE).  Inputs may
+ * overlap each other.
  *
  * Threading / streams: calls are asynchronous on `stream` (a hipStream_t; NULL
  * means the default stream).  The library allocates no device memory, does
@@ -52,7 +57,7 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad eps / window, misalignment */
   ATTN_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
-  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_bytes */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing, too small, misaligned or overlapping a tensor */
   ATTN_ERR_HIP = 4          /* a HIP launch failed */
 };
 
@@ -104,7 +109,7 @@ size_t attn_fwd_workspace_bytes(int B, int T, int H, int D);
  * window: W >= 0 keys to the left (W >= T - 1 is full causal), or -1 for full
  * causal.  causal must be 1 (0 returns ATTN_ERR_UNSUPPORTED: the pages never
  * use bidirectional attention).  eps: RMSNorm epsilon, finite and > 0.
- * D must be 64 or 128 (else ATTN_ERR_UNSUPPORTED).  B*T*H*D must stay below
+ * D must be 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).  B*T*H*D must stay below
  * 2^31 (else ATTN_ERR_UNSUPPORTED).  B, T or H equal to 0 is an empty problem:
  * returns ATTN_OK and touches nothing (pointers may then be NULL).
  * workspace: device memory of at least attn_fwd_workspace_bytes(B, T, H, D)
@@ -294,6 +299,16 @@ int attn_profile_enable(int on);
 int attn_profile_enable_mask(unsigned mask);
 int attn_profile_read(int kernel, double* total_ms, long long* launches);
 const char* attn_kernel_name(int kernel);
+
+/*
+ * Device facts a roofline needs, another measurement aid: the number of
+ * compute units of HIP device `device` and its peak shader clock in kHz (HIP's
+ * hipDeviceAttributeClockRate).  A bf16 dense MFMA peak follows as
+ * compute_units x 4096 FLOP per clock x clock on gfx950.  Returns
+ * ATTN_ERR_INVALID_ARG for a NULL output or a negative device, ATTN_ERR_HIP if
+ * the runtime cannot answer (no such device).  Initialises the HIP runtime.
+ */
+int attn_device_info(int device, int* compute_units, int* max_clock_khz);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,7 @@ memory and the current stream.
     windows = layer_windows("SSSL", n_layer=8, seq_len=2048)   # [1024, ..., 2048]
     o = attention(q, k, v, window=windows[l])                    # autograd-aware
 
-q: bf16 CUDA tensor [B, T, H, D] (contiguous), D in {64, 128}; k, v: bf16
+q: bf16 CUDA tensor [B, T, H, D] (contiguous), D in {64, 128, 256}; k, v: bf16
 [B, T, H_kv, D] with H_kv dividing H (grouped key/value heads: query head h
 reads key/value head h // (H // H_kv); H_kv = H is plain multi-head attention).
 rope=(cos, sin): bf16 [T, D/2] tables; q and k are then the projections before

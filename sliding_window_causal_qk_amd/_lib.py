@@ -22,6 +22,7 @@ EXPORTS = (
     "attn_bwd_gqa", "attn_fwd_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope_workspace_bytes",
     "attn_bwd_rope", "attn_fwd_ve_workspace_bytes", "attn_fwd_ve", "attn_bwd_ve_workspace_bytes",
     "attn_bwd_ve", "attn_bwd_gqa_reuse", "attn_bwd_rope_reuse", "attn_bwd_ve_reuse", "attn_profile_enable", "attn_profile_enable_mask", "attn_profile_read", "attn_kernel_name",
+    "attn_device_info",
 )
 
 
@@ -106,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.attn_profile_read.restype = c_int
     L.attn_kernel_name.argtypes = [c_int]
     L.attn_kernel_name.restype = ctypes.c_char_p
+    L.attn_device_info.argtypes = [c_int, P_int, P_int]
+    L.attn_device_info.restype = c_int
     _lib = L
     return L
 

@@ -96,6 +96,14 @@ int attn_profile_read(int kernel, double* total_ms, long long* launches) {
   return ok ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+int attn_device_info(int device, int* compute_units, int* max_clock_khz) {
+  if (!compute_units || !max_clock_khz || device < 0) return ATTN_ERR_INVALID_ARG;
+  if (hipDeviceGetAttribute(compute_units, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipDeviceGetAttribute(max_clock_khz, hipDeviceAttributeClockRate, device) != hipSuccess)
+    return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 const char* attn_kernel_name(int kernel) {
   if (kernel < 0 || kernel >= swattn::kNumKernels) return "unknown";
   return swattn::kNames[kernel];

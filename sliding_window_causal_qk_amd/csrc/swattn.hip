@@ -18,6 +18,25 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Byte range [lo, hi) of one buffer, for the no-overlap rules: an output may
+// share no byte with an input, another output or the workspace, and the
+// workspace none with any input or output.
+struct Span {
+  uintptr_t lo = 0, hi = 0;
+};
+Span span(const void* p, size_t nbytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + nbytes};
+}
+bool overlap(const Span& a, const Span& b) {
+  return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi;
+}
+bool overlaps_any(const Span& a, const Span* set, int n) {
+  for (int i = 0; i < n; ++i)
+    if (overlap(a, set[i])) return true;
+  return false;
+}
+
 // Shared checks of the forward / backward entry points.  Returns ATTN_OK to
 // proceed, or a status; *empty is set for problems with no rows.
 int check_common(int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
@@ -172,21 +191,23 @@ struct Extras {
 
 constexpr int kGateMaxKvHeads = 16;
 
-// Checks of the optional inputs; appends them to `ins` for the aliasing test.
-int check_extras(const Extras& x, int H_kv, const void** ins, int* nin) {
+// Checks of the optional inputs; appends their byte ranges to `ins` for the
+// overlap rules.
+int check_extras(const Extras& x, int B, int T, int H_kv, int D, Span* ins, int* nin) {
   if (x.rope) {
     if (!x.rcos || !x.rsin || !aligned(x.rcos, 16) || !aligned(x.rsin, 16)) return ATTN_ERR_INVALID_ARG;
-    ins[(*nin)++] = x.rcos;
-    ins[(*nin)++] = x.rsin;
+    const size_t tb = (size_t)T * (D / 2) * 2;
+    ins[(*nin)++] = span(x.rcos, tb);
+    ins[(*nin)++] = span(x.rsin, tb);
   }
   if (x.gate) {
     if (!x.ve || !x.xg || !x.gate_w || !aligned(x.ve, 16) || !aligned(x.xg, 16) || !aligned(x.gate_w, 16))
       return ATTN_ERR_INVALID_ARG;
     if (x.xs < 32 || x.xs % 8 != 0) return ATTN_ERR_INVALID_ARG;
     if (H_kv > kGateMaxKvHeads) return ATTN_ERR_UNSUPPORTED;
-    ins[(*nin)++] = x.ve;
-    ins[(*nin)++] = x.xg;
-    ins[(*nin)++] = x.gate_w;
+    ins[(*nin)++] = span(x.ve, (size_t)B * T * H_kv * D * 2);
+    ins[(*nin)++] = span(x.xg, (((size_t)B * T - 1) * x.xs + 32) * 2);   // the 32 channels read per token
+    ins[(*nin)++] = span(x.gate_w, (size_t)H_kv * 32 * 4);
   }
   return ATTN_OK;
 }
@@ -197,20 +218,24 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, v
   bool empty;
   int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
-  const void* ins[8] = {q, k, v};
+  for (const void* p : {q, k, v})
+    if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * T * H * D * 2, kb = (size_t)B * T * H_kv * D * 2;
+  Span ins[8] = {span(q, qb), span(k, kb), span(v, kb)};
   int nin = 3;
-  st = check_extras(x, H_kv, ins, &nin);
+  st = check_extras(x, B, T, H_kv, D, ins, &nin);
   if (st != ATTN_OK) return st;
-  for (int i = 0; i < 3; ++i)
-    if (!ins[i] || !aligned(ins[i], 16)) return ATTN_ERR_INVALID_ARG;
   if (!o || !lse || !aligned(o, 16) || !aligned(lse, 16)) return ATTN_ERR_INVALID_ARG;
-  for (int i = 0; i < nin; ++i)
-    if (ins[i] == o || ins[i] == (const void*)lse) return ATTN_ERR_INVALID_ARG;
+  const Span outs[2] = {span(o, qb), span(lse, (size_t)B * H * T * 4)};
+  for (int j = 0; j < 2; ++j)
+    if (overlaps_any(outs[j], ins, nin) || overlaps_any(outs[j], outs, j)) return ATTN_ERR_INVALID_ARG;
   const size_t need = x.gate   ? attn_fwd_ve_workspace_bytes(B, T, H, H_kv, D)
                       : x.rope ? attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D)
                                : attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
+  const Span wsp = span(workspace, need);
+  if (overlaps_any(wsp, ins, nin) || overlaps_any(wsp, outs, 2)) return ATTN_ERR_WORKSPACE;
 
   swattn::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -241,34 +266,39 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   bool empty;
   int st = check_common(B, T, H, H_kv, D, window, causal, eps, &empty);
   if (st != ATTN_OK || empty) return st;
-  const void* ins[12] = {q, k, v, o, lse, dout};
+  for (const void* p : {q, k, v, o, (const void*)lse, dout})
+    if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * T * H * D * 2, kb = (size_t)B * T * H_kv * D * 2;
+  const size_t sb_h = (size_t)B * H * T * 4;
+  Span ins[12] = {span(q, qb), span(k, kb), span(v, kb), span(o, qb), span(lse, sb_h), span(dout, qb)};
   int nin = 6;
-  st = check_extras(x, H_kv, ins, &nin);
+  st = check_extras(x, B, T, H_kv, D, ins, &nin);
   if (st != ATTN_OK) return st;
-  for (int i = 0; i < 6; ++i)
-    if (!ins[i] || !aligned(ins[i], 16)) return ATTN_ERR_INVALID_ARG;
-  void* outs[6] = {dq, dk, dv, x.dve, x.dxg, x.dgate_w};
+  void* const outp[6] = {dq, dk, dv, x.dve, x.dxg, x.dgate_w};
+  const size_t outb[6] = {qb, kb, kb, kb, (size_t)B * T * 32 * 2, (size_t)H_kv * 32 * 4};
   const int nout = x.gate ? 6 : 3;
+  Span outs[6];
   for (int j = 0; j < nout; ++j) {
-    if (!outs[j] || !aligned(outs[j], 16)) return ATTN_ERR_INVALID_ARG;
-    for (int i = 0; i < nin; ++i)
-      if (ins[i] == outs[j]) return ATTN_ERR_INVALID_ARG;
-    for (int i = 0; i < j; ++i)
-      if (outs[i] == outs[j]) return ATTN_ERR_INVALID_ARG;
+    if (!outp[j] || !aligned(outp[j], 16)) return ATTN_ERR_INVALID_ARG;
+    outs[j] = span(outp[j], outb[j]);
+    if (overlaps_any(outs[j], ins, nin) || overlaps_any(outs[j], outs, j)) return ATTN_ERR_INVALID_ARG;
   }
   const size_t need = x.gate   ? attn_bwd_ve_workspace_bytes(B, T, H, H_kv, D)
                       : x.rope ? attn_bwd_rope_workspace_bytes(B, T, H, H_kv, D)
                                : attn_bwd_gqa_workspace_bytes(B, T, H, H_kv, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return ATTN_ERR_WORKSPACE;
+  const Span wsp = span(workspace, need);
+  if (overlaps_any(wsp, ins, nin) || overlaps_any(wsp, outs, nout)) return ATTN_ERR_WORKSPACE;
   if (reuse) {
     if (!fwd_ws) return ATTN_ERR_WORKSPACE;
     const size_t need_f = x.gate   ? attn_fwd_ve_workspace_bytes(B, T, H, H_kv, D)
                           : x.rope ? attn_fwd_rope_workspace_bytes(B, T, H, H_kv, D)
                                    : attn_fwd_gqa_workspace_bytes(B, T, H, H_kv, D);
-    if (fwd_ws_bytes < need_f || !aligned(fwd_ws, kAlign) || fwd_ws == workspace) return ATTN_ERR_WORKSPACE;
-    for (int j = 0; j < nout; ++j)
-      if (outs[j] == fwd_ws) return ATTN_ERR_INVALID_ARG;
+    if (fwd_ws_bytes < need_f || !aligned(fwd_ws, kAlign)) return ATTN_ERR_WORKSPACE;
+    const Span fws = span(fwd_ws, need_f);
+    if (overlap(fws, wsp)) return ATTN_ERR_WORKSPACE;
+    if (overlaps_any(fws, outs, nout)) return ATTN_ERR_INVALID_ARG;
   }
 
   char* ws = static_cast<char*>(workspace);

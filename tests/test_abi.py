@@ -159,6 +159,39 @@ def test_aliasing_rejected():
     assert _bwd(dv=ALIGNED[6]) == _lib.ATTN_ERR_INVALID_ARG
 
 
+QB = 2 * 64 * 2 * 64 * 2       # bytes of q (and of o, dq, ...) at the default B=2, T=64, H=2, D=64
+
+
+def test_partial_overlap_rejected():
+    """Outputs may share no byte with an input, another output or the
+    workspace, and the workspace none with an input or output: ranges that
+    overlap by a single 16-byte chunk are rejected, not only equal pointers."""
+    inv, wsc = _lib.ATTN_ERR_INVALID_ARG, _lib.ATTN_ERR_WORKSPACE
+    assert _fwd(o=ALIGNED[0] + QB - 16) == inv          # o starts in q's last chunk
+    assert _fwd(o=ALIGNED[2] - QB + 16) == inv          # o ends in v's first chunk
+    assert _fwd(lse=ALIGNED[3] + QB - 16) == inv        # lse inside o
+    assert _fwd(o=ALIGNED[4] - QB + 16) == inv          # o over lse's first bytes
+    assert _fwd(ws=ALIGNED[1] + QB - 256) == wsc        # workspace over k's tail
+    assert _fwd(ws=ALIGNED[3] - 256) == wsc             # workspace runs into o
+    assert _bwd(dq=ALIGNED[5] + QB - 16) == inv         # dq starts in dout's last chunk
+    assert _bwd(dv=ALIGNED[7] + QB - 16) == inv         # dv overlaps dk
+    assert _bwd(dk=ALIGNED[4] + 2 * 2 * 64 * 4 - 16) == inv   # dk over lse's last chunk
+    assert _bwd(ws=ALIGNED[8] + 256) == wsc             # workspace inside dv
+    assert _bwd(ws=ALIGNED[0] + 256) == wsc             # workspace inside q
+
+
+@pytest.mark.parametrize("kind", ["gqa", "rope", "ve"])
+def test_reuse_partial_overlap_rejected(kind):
+    ws = ALIGNED[9] if kind != "ve" else P + 15 * 0x1000000
+    dv = ALIGNED[8] if kind != "ve" else ALIGNED[11]
+    assert _bwd_reuse(kind, fws=dv + 256) == _lib.ATTN_ERR_INVALID_ARG     # forward workspace inside dv
+    assert _bwd_reuse(kind, fws=ws + 256) == _lib.ATTN_ERR_WORKSPACE       # inside this call's workspace
+    if kind == "rope":   # an output over the tail of the sin table (T rows of D/2 bf16)
+        assert _bwd_reuse(kind, dq=ALIGNED[11] + 64 * 32 * 2 - 16) == _lib.ATTN_ERR_INVALID_ARG
+    if kind == "ve":     # dx over the gate input's last token (32 channels read at stride 512)
+        assert _bwd_reuse(kind, dx=ALIGNED[4] + (2 * 64 - 1) * 512 * 2) == _lib.ATTN_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("kw", [dict(D=96), dict(D=512), dict(D=32), dict(causal=0),
                                 dict(B=1 << 12, T=1 << 12, H=8, D=128)])
 def test_unsupported(kw):

@@ -4,23 +4,25 @@ Every option the entry points take is mixed at random: batch and length
 (ragged T from 1 up), query and key/value heads (grouped heads included),
 head sizes 64 / 128 / 256, windows from 0 to unbounded, the rotary tables,
 the value-embedding gate (block inputs of several widths) and the backward
-that reuses the forward's workspace.  Each case is compared element by
-element with the fp64 oracle.  o and lse take the stated tolerance
-|g - o| <= 2e-2 + 1e-2 |o|.  Each gradient element is a sum of terms (dv:
-P dO over queries and grouped heads; dq, dk: dS k_hat, dS q_hat, then the
-RMSNorm backward's projection; dx: dz W_g), so the gradients take it per
-term, the reading the gate's dW_g uses: |g - o| <= 2e-2 + 1e-2 max(|o|, S),
-S the row's sum of term magnitudes.  A few large terms that cancel -- G
-terms with P = 1 at a window of 0, the first queries of a causal sequence,
-whose dS q_hat the norm's projection then mostly removes -- leave the bf16
-rounding of P, dS and q_hat above the element-wise bound.  The cases are
-drawn once from a fixed seed, so a failure names a reproducible case."""
+that reuses the forward's workspace.  The cases are drawn once from a fixed
+seed, so a failure names a reproducible case.
+
+Each case is compared element by element twice:
+  * with the fp64 oracle, at the stated tolerance |g - o| <= 2e-2 + 1e-2 |o|
+    on every output, except the (case, tensor) pairs that
+    tests/precision_exceptions.py names, where the kernels' stated precision
+    itself misses it (and dW_g, a sum over every token);
+  * with tests/rounding_model.py, the CPU model of the kernels' stated
+    rounding, at the same tolerance on every output: the GPU computes the
+    arithmetic it states.
+"""
 import numpy as np
 import pytest
 
 import oracle
+from tests import rounding_model
 from workloads import make_layer_inputs, make_gate_inputs, bf16_bits_to_f32, rope_tables_bf16
-from tests.test_gpu_parity import EPS, _close, _close_sum, _np, _run, _run_rope, _run_ve, _say, torch_dev  # noqa: F401
+from tests.test_gpu_parity import EPS, _check, _np, _run, _run_rope, _run_ve, _say, torch_dev  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -44,84 +46,38 @@ def _cases(n=24, seed=2026):
 
 
 CASES = _cases()
+IDS = [f"B{c[0]}T{c[1]}H{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}{'rope' if c[6] else ''}C{c[7]}{'reuse' if c[8] else ''}"
+       for c in CASES]
 
 
-def _term_scales(qf, kf, vf, dof, W, c=None, sn=None):
-    """Per row, the summed magnitude of the terms each gradient element adds up
-    (fp64, from the oracle's P and dS = P (dP - Delta)):
-      sv [B, T, H_kv]: sum over the group's heads h and queries i of P_hij max|dO_hi|
-      sq [B, T, H]:    r_q sum_j |dS_ij| max|k_hat_j| / sqrt(D)
-      sk [B, T, H_kv]: r_k sum over h, i of |dS_hij| max|q_hat_hi| / sqrt(D)
-    vf are the values attention multiplies (the gated ones with the gate)."""
-    q, k = (oracle.rope(qf, c, sn), oracle.rope(kf, c, sn)) if c is not None else (qf, kf)
-    B, T, H, D = q.shape
-    H_kv = k.shape[2]
-    qh, rq = oracle.rms_norm(q, EPS)
-    kh, rk = oracle.rms_norm(k, EPS)
-    sv, sq, sk = np.zeros((B, T, H_kv)), np.zeros((B, T, H)), np.zeros((B, T, H_kv))
-    for b in range(B):
-        for h in range(H):
-            hk = oracle.kv_head(h, H, H_kv)
-            P, _ = oracle.probabilities(q, k, b, h, W, True, EPS)
-            do = dof[b, :, h].astype(np.float64)
-            dP = do @ np.asarray(vf[b, :, hk], dtype=np.float64).T
-            dS = np.abs(P * (dP - np.sum(P * dP, axis=1)[:, None]))
-            sv[b, :, hk] += P.T @ np.abs(do).max(axis=1)
-            sq[b, :, h] = rq[b, :, h] * (dS @ np.abs(kh[b, :, hk]).max(axis=1)) / np.sqrt(D)
-            sk[b, :, hk] += rk[b, :, hk] * (dS.T @ np.abs(qh[b, :, h]).max(axis=1)) / np.sqrt(D)
-    return sv, sq, sk
-
-
-def _close_terms(name, got, want, scale):
-    """Element-wise check against 2e-2 + 1e-2 max(|want|, scale of the row)."""
-    want = np.asarray(want, dtype=np.float64)
-    _close_sum(name, got, want, np.maximum(np.abs(want), scale[..., None]))
-
-
-@pytest.mark.parametrize("B,T,H,H_kv,D,W,rope,C,reuse,seed", CASES,
-                         ids=[f"B{c[0]}T{c[1]}H{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}{'rope' if c[6] else ''}"
-                              f"C{c[7]}{'reuse' if c[8] else ''}" for c in CASES])
+@pytest.mark.parametrize("B,T,H,H_kv,D,W,rope,C,reuse,seed", CASES, ids=IDS)
 def test_random_shape_parity(torch_dev, B, T, H, H_kv, D, W, rope, C, reuse, seed):
-    _say(f"[random] B={B} T={T} H={H} H_kv={H_kv} D={D} W={W} rope={rope} C={C} reuse={reuse} seed={seed}")
+    cid = IDS[CASES.index((B, T, H, H_kv, D, W, rope, C, reuse, seed))]
+    _say(f"[random] {cid} seed={seed}")
     inp = make_layer_inputs(B, T, H, D, seed, H_kv=H_kv)
     qf, kf, vf, dof = inp.as_f32()
     tables = rope_tables_bf16(T, D) if rope else None
     c, sn = (bf16_bits_to_f32(t) for t in tables) if rope else (None, None)
+    gk = {}
     if C:
         gi = make_gate_inputs(B, T, H_kv, D, C, seed + 100)
         vef, xf = bf16_bits_to_f32(gi.ve), bf16_bits_to_f32(gi.x)
+        gk = dict(ve=vef, xg=xf, gate_w=gi.gate_w)
         got = _run_ve(torch_dev, inp, gi, W, tables, reuse=reuse)
-        ro, rl = oracle.attention_fwd_ve(qf, kf, vf, vef, xf, gi.gate_w, W, True, EPS, c, sn)
-        ref = oracle.attention_bwd_ve(qf, kf, vf, dof, vef, xf, gi.gate_w, W, True, EPS, c, sn)
-        gate = oracle.ve_gate(xf, gi.gate_w)
-        vg = vf + gate[..., None] * vef
-        sv, sq, sk = _term_scales(qf, kf, vg, dof, W, c, sn)
-        for name, g, want in zip(("o", "lse"), got[:2], (ro, rl)):
-            _close(name, _np(g), want)
-        _close_terms("dq", _np(got[2]), ref[0], sq)
-        _close_terms("dk", _np(got[3]), ref[1], sk)
-        _close_terms("dv", _np(got[4]), ref[2], sv)
-        _close_terms("dve", _np(got[5]), ref[3], gate * sv)
-        # dx[c] = sum_h dz_h W_g[h, c], dz_h = (dv_h . ve_h) gate (1 - gate / 2)
-        sz = sv * np.abs(vef).sum(axis=-1) * gate * (1 - gate / 2)
-        _close_sum("dx32", _np(got[6]), ref[4],
-                   np.maximum(np.abs(ref[4]), sz @ np.abs(gi.gate_w.astype(np.float64))))
-        # dW_g[h, c] = sum_t dz_h x_c, each term bounded by its dz's term scale
-        dz = np.sum(ref[2] * vef, axis=-1) * gate * (1 - gate / 2)
-        scale = np.einsum("bth,btc->hc", np.maximum(np.abs(dz), sz), np.abs(xf[..., :32].astype(np.float64)))
-        _close_sum("dgate_w", _np(got[7]), ref[5], scale)
-        return
-    if rope:
+        want = oracle.attention_fwd_ve(qf, kf, vf, vef, xf, gi.gate_w, W, True, EPS, c, sn) + \
+            oracle.attention_bwd_ve(qf, kf, vf, dof, vef, xf, gi.gate_w, W, True, EPS, c, sn)
+        names = ("o", "lse", "dq", "dk", "dv", "dve", "dx32", "dgate_w")
+    elif rope:
         got = _run_rope(torch_dev, inp, tables, W, reuse=reuse)
-        ro, rl = oracle.attention_fwd_rope(qf, kf, vf, c, sn, W, True, EPS)
-        ref = oracle.attention_bwd_rope(qf, kf, vf, dof, c, sn, W, True, EPS)
+        want = oracle.attention_fwd_rope(qf, kf, vf, c, sn, W, True, EPS) + \
+            oracle.attention_bwd_rope(qf, kf, vf, dof, c, sn, W, True, EPS)
+        names = ("o", "lse", "dq", "dk", "dv")
     else:
         got = _run(torch_dev, inp, W, reuse=reuse)
-        ro, rl = oracle.attention_fwd(qf, kf, vf, W, True, EPS)
-        ref = oracle.attention_bwd(qf, kf, vf, dof, W, True, EPS)
-    for name, g, want in zip(("o", "lse"), got[:2], (ro, rl)):
-        _close(name, _np(g), want)
-    sv, sq, sk = _term_scales(qf, kf, vf, dof, W, c, sn)
-    _close_terms("dq", _np(got[2]), ref[0], sq)
-    _close_terms("dk", _np(got[3]), ref[1], sk)
-    _close_terms("dv", _np(got[4]), ref[2], sv)
+        want = oracle.attention_fwd(qf, kf, vf, W, True, EPS) + oracle.attention_bwd(qf, kf, vf, dof, W, True, EPS)
+        names = ("o", "lse", "dq", "dk", "dv")
+    mo, ml = rounding_model.forward(qf, kf, vf, W, EPS, c, sn, **gk)
+    model = (mo, ml) + rounding_model.backward(qf, kf, vf, mo, ml, dof, W, EPS, c, sn, **gk)
+    assert len(got) == len(want) == len(model) == len(names)
+    for name, g, w, m in zip(names, got, want, model):
+        _check(cid, name, _np(g), w, m)

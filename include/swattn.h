@@ -35,8 +35,9 @@
  * Threading / streams: calls are asynchronous on `stream` (a hipStream_t; NULL
  * means the default stream).  The library allocates no device memory, does
  * not synchronise, and keeps no mutable global state apart from the opt-in
- * timing counters below; concurrent calls on
- * different streams are safe if their buffers are disjoint.
+ * timing counters below and the device array of attn_fwd_noalloc; concurrent
+ * calls on different streams are safe if their buffers are disjoint (for
+ * attn_fwd_noalloc, see there).
  *
  * Errors: every argument check runs on the host before any HIP call; a
  * rejected call returns its status and touches nothing.  A failed launch
@@ -273,6 +274,25 @@ int attn_bwd_ve_reuse(const void* q, const void* k, const void* v, const void* v
                       void* workspace, size_t workspace_bytes,
                       int B, int T, int H, int H_kv, int D, int window, int causal, float eps,
                       void* stream);
+
+/*
+ * Forward that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid allocation.  Same operation, arguments, rules and status codes
+ * as attn_fwd, without the workspace: the key scales live in a device array
+ * of the library (attn_fwd_noalloc_max_bytes() = 8 MiB, so B*H*T <= 2^21),
+ * which each GPU holds from the library's first use on it until the process
+ * ends.  A problem whose attn_fwd_workspace_bytes exceed that size returns
+ * ATTN_ERR_WORKSPACE and touches nothing.  Every call on one GPU shares the
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it.  A backward may not reuse it as a forward workspace
+ * (the next call overwrites it); run attn_bwd.  Results equal attn_fwd's bit
+ * for bit.
+ */
+size_t attn_fwd_noalloc_max_bytes(void);
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int T, int H, int D, int window, int causal, float eps,
+                     void* stream);
 
 /*
  * Opt-in per-kernel timing, a measurement aid (not part of the operation).

@@ -22,7 +22,7 @@ EXPORTS = (
     "attn_bwd_gqa", "attn_fwd_rope_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope_workspace_bytes",
     "attn_bwd_rope", "attn_fwd_ve_workspace_bytes", "attn_fwd_ve", "attn_bwd_ve_workspace_bytes",
     "attn_bwd_ve", "attn_bwd_gqa_reuse", "attn_bwd_rope_reuse", "attn_bwd_ve_reuse", "attn_profile_enable", "attn_profile_enable_mask", "attn_profile_read", "attn_kernel_name",
-    "attn_device_info",
+    "attn_device_info", "attn_fwd_noalloc_max_bytes", "attn_fwd_noalloc",
 )
 
 
@@ -109,6 +109,10 @@ def lib() -> ctypes.CDLL:
     L.attn_kernel_name.restype = ctypes.c_char_p
     L.attn_device_info.argtypes = [c_int, P_int, P_int]
     L.attn_device_info.restype = c_int
+    L.attn_fwd_noalloc_max_bytes.argtypes = []
+    L.attn_fwd_noalloc_max_bytes.restype = c_size
+    L.attn_fwd_noalloc.argtypes = [c_vp] * 5 + [c_int] * 6 + [c_float, c_vp]
+    L.attn_fwd_noalloc.restype = c_int
     _lib = L
     return L
 

@@ -29,7 +29,10 @@ before it.
 
 After the headline workload the same run measures the other single-GPU
 workloads of the method's configuration list (the S layer, the L layer and the
-long-context SSSL period: keys s_layer, l_layer, long) with the same step
+long-context SSSL period: keys s_layer, l_layer, long) and the shorter
+sequences and other window patterns of the pages' tuning space (SSSL at
+T = 512 and 1024 with the same tokens per step, patterns L and SLLL: keys
+t512_sssl_stack, t1024_sssl_stack, l_stack, slll_stack), with the same step
 definition.  The CPU baseline (the fp64 oracle) runs first, before anything
 touches the GPU, over a process pool with one BLAS thread per process.
 
@@ -54,7 +57,10 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (AMD's published figure)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 BF16_FLOP_PER_CLK_CU = 4096   # gfx950 dense bf16 MFMA FLOP per clock per compute unit
 METRIC = "attn fwd+bwd effective TFLOP/s & % bf16 MFMA peak, T=2048 H=4 D=128 SSSL"
-EXTRA_WORKLOADS = ("s_layer", "l_layer", "long")
+# the method's other single-GPU configurations, then the shorter sequences and
+# other window patterns of the pages' tuning space
+EXTRA_WORKLOADS = ("s_layer", "l_layer", "long", "t512_sssl_stack", "t1024_sssl_stack", "l_stack",
+                   "slll_stack")
 MAX_POOL = 16                 # host worker processes at most (one GPU's share of the host)
 
 # algorithmic work credited to each kernel, per visible pair (FLOPs = c * D * N_vis)
@@ -382,7 +388,7 @@ def main():
     ap.add_argument("--workload", default="sssl_stack")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other single-GPU workloads (s_layer, l_layer, long)")
-    ap.add_argument("--extra-steps", type=int, default=50,
+    ap.add_argument("--extra-steps", type=int, default=20,
                     help="timed steps of each extra workload (at least --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

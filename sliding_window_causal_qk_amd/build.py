@@ -2,8 +2,8 @@
 
     python -m sliding_window_causal_qk_amd.build
 
-Every call recompiles.  The library lands next to this file; the Python
-binding loads it from there.
+Every call recompiles (the sources in parallel, then one link).  The library
+lands next to this file; the Python binding loads it from there.
 """
 from __future__ import annotations
 
@@ -25,7 +25,7 @@ def hipcc() -> str:
 
 def flags(extra=()):
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # keep the compiler from forming packed fp32 instructions on its own
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
@@ -34,21 +34,37 @@ def flags(extra=()):
     ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{out}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+
+
+def build(verbose: bool = False, csrc: str | None = None, out: str | None = None) -> str:
+    """Compiles every source of `csrc` (default: the package's) to an object,
+    in parallel, and links the shared library `out` (default: the package's
+    libswattn.so)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import tempfile
+    csrc = csrc or os.path.join(PKG, "csrc")
+    out = out or LIB
+    srcs = sorted(glob.glob(os.path.join(csrc, "*.hip")))
+    with tempfile.TemporaryDirectory(prefix="swattn_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+        jobs = min(len(srcs), os.cpu_count() or 1, 16)
+        with ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda so: _run([hipcc(), *flags(), "-c", so[0], "-o", so[1]], verbose),
+                        zip(srcs, objs)))
+        tmp = out + ".tmp"
+        _run([hipcc(), *flags(), "-shared", *objs, "-o", tmp], verbose)
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -528,7 +528,9 @@ def test_single_layer_workloads(torch_dev, name):
                                         ("gqa_sssl_stack", 0), ("gqa_sssl_stack", 3),
                                         ("rope_sssl_stack", 0), ("rope_sssl_stack", 3),
                                         ("ve_sssl_stack", 0), ("ve_sssl_stack", 3),
-                                        ("d256_sssl_stack", 0), ("d256_sssl_stack", 3)])
+                                        ("d256_sssl_stack", 0), ("d256_sssl_stack", 3),
+                                        ("t512_sssl_stack", 0), ("t512_sssl_stack", 7),
+                                        ("t1024_sssl_stack", 0), ("slll_stack", 0), ("l_stack", 0)])
 def test_stack_and_long_workloads_sampled(torch_dev, name, layer):
     import sliding_window_causal_qk_amd as sw
     wl = workload(name)

@@ -132,6 +132,16 @@ WORKLOADS: List[Workload] = [
     Workload("ve_sssl_stack", B=64, T=2048, H=4, D=128, pattern="SSSL", n_layer=8, seed0=5000,
              ve_gate=True,
              notes="the SSSL stack with the value-embedding gate fused into the V load"),
+    # the tutorial's tuning space (§10.1.1): shorter sequences and the other
+    # window patterns, at the stack's 131072 tokens per step
+    Workload("t512_sssl_stack", B=256, T=512, H=4, D=128, pattern="SSSL", n_layer=8, seed0=7000,
+             notes="the SSSL stack at sequence length 512 (windows 256 / 512), same tokens per step"),
+    Workload("t1024_sssl_stack", B=128, T=1024, H=4, D=128, pattern="SSSL", n_layer=8, seed0=7100,
+             notes="the SSSL stack at sequence length 1024 (windows 512 / 1024), same tokens per step"),
+    Workload("l_stack", B=64, T=2048, H=4, D=128, pattern="L", n_layer=8, seed0=7200,
+             notes="pattern L: every layer full causal"),
+    Workload("slll_stack", B=64, T=2048, H=4, D=128, pattern="SLLL", n_layer=8, seed0=7300,
+             notes="pattern SLLL: one sliding-window layer in four"),
 ]
 
 

@@ -27,7 +27,9 @@
 //   bwd_dkdv:   persistent; a tile is 128 keys (32 per wave) of one key/value
 //               head, walking the query blocks of its band in each of the
 //               head's G query heads; dV^T and dK_hat^T stay in registers; the
-//               RMSNorm backward of K runs in the epilogue.
+//               RMSNorm backward of K runs in the epilogue.  At head size 256,
+//               bwd_dkdv_split takes its place: two waves share each 32-key
+//               block, one for S, P and dV, the other for dP, dS and dK.
 #include <type_traits>
 
 #include "common.h"
@@ -85,16 +87,14 @@ struct DkdvCfg {
   static constexpr int ST_B = 2 * Tile::BYTES;      // 4 x 256 B: spare, spare, lse2, Delta
   static constexpr int STAGE = ST_B + 1024;
   static constexpr int KV_B = NBUF * STAGE;         // K rows, then V rows of the next tile
-  // the next tile's K / V rows are prefetched into LDS up to D = 128; at
-  // D = 256 they would not fit, and each tile loads them into registers
-  static constexpr bool KV_PREFETCH = D <= 128;
   static constexpr int OP = D + 8;                  // output staging row pitch (bf16)
   static constexpr int OUT_SLOT = 32 * OP * 2;      // one wave's 32 x D bf16 block
-  static constexpr int XO_B = KV_B + (KV_PREFETCH ? 2 * KVTile::BYTES : 0);   // staging slots of waves 2 and 3
+  static constexpr int XO_B = KV_B + 2 * KVTile::BYTES;   // staging slots of waves 2 and 3
   static constexpr int LDS_BYTES = XO_B + 2 * OUT_SLOT;
   static constexpr int NSTORE = 2 * (32 * D / 8 / 64);    // epilogue stores per lane (dK and dV)
   static_assert(2 * OUT_SLOT <= STAGE, "waves 0 and 1 stage their outputs in a freed step buffer");
   static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
+  static_assert(D <= 128, "head size 256 takes bwd_dkdv_split_kernel");
 };
 
 // GROUPED = false is the plain multi-head case, compiled with G = 1 so that the
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // prologue of the stream: K / V rows of the first tile, blocks 0 and 1.
   // Invariant at a step's start: b0 holds block it, b1 block it + 1, b2 is free.
   int b0 = 2 * C::STAGE, b1 = 0, b2 = C::STAGE;
-  if (C::KV_PREFETCH && tcur >= 0) issue_kv(dgeo);
+  if (tcur >= 0) issue_kv(dgeo);
   issue_plan(plan_next(), b1);
   issue_plan(plan_next(), b2);
   DmaPlan pnext = plan_next();
@@ -303,24 +303,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       b1 = b2;
       b2 = t_;
     }
-    if constexpr (C::KV_PREFETCH) {
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        kf[ks] = lds16(smem, kv_off + 32 * ks);
-        vf[ks] = lds16(smem, kv_off + C::KVTile::BYTES + 32 * ks);
-      }
-    } else {
-      const rsrc_t rk = make_rsrc(k + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
-      const rsrc_t rv = make_rsrc(v + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        kf[ks] = bload16(rk, (c * rs_kv + 16 * ks + 8 * g) * 2);
-        vf[ks] = bload16(rv, (c * rs_kv + 16 * ks + 8 * g) * 2);
-      }
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks] = lds16(smem, kv_off + 32 * ks);
+      vf[ks] = lds16(smem, kv_off + C::KVTile::BYTES + 32 * ks);
     }
 #pragma unroll
     for (int n = 0; n < C::NB; ++n) { acc_dv[n] = f32x16{}; acc_dk[n] = f32x16{}; }
-    const bool kv_pending = C::KV_PREFETCH && tile_at(ti + 1) >= 0;   // prefetch of the next tile's K / V rows
+    const bool kv_pending = tile_at(ti + 1) >= 0;   // prefetch of the next tile's K / V rows
 
     // A: scores and dP of one step
     auto stage_a = [&](int base) {
@@ -402,10 +392,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     //   with the remaining exponentials, dS = P (dP - Delta) and the bf16
     //   packing between them, and the next block's plan halfway.
     // B(it+1) writes separate registers that C(it+1) takes over at the step's
-    // end.  At D = 256 the operands of that order do not fit in registers and
-    // the step keeps the compiler's order.
+    // end.
     auto step_body = [&](int s_next, auto masked_c) {   // B for step s_next of its query head
-      if constexpr (D <= 128) {
+      {
         constexpr int CA = 4;     // C operands read ahead
         const int va = b1 + a_off, vl = b1 + l_off;
         u32x4 qa[C::KS], da[C::KS], cop[NM];
@@ -489,38 +478,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         pf[1] = pn[1];
         dsf[0] = dn[0];
         dsf[1] = dn[1];
-      } else {
-        issue_plan(pnext, b2);      // block it + 2 into the free buffer
-        stage_a(b1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * C::KS - 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        __builtin_amdgcn_sched_barrier(0);   // A stays ahead of C and B
-        stage_c(b0);
-        stage_b(b1, s_next, masked_c);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int i = 0; i < 4 * C::NB - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS reads
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        }
-        // keep B's results inside this step (the compiler would otherwise sink
-        // the softmax below the barrier, away from the MFMAs it should overlap)
-        asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(dsf[0]), "v"(dsf[1]));
       }
       // the buffer rotation is scalar work that overlaps the last MFMAs still in
       // flight; the barrier only orders the buffers' contents
-      if constexpr (D > 128) pnext = plan_next();
       const int t_ = b0;
       b0 = b1;
       b1 = b2;
@@ -702,6 +662,573 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
     }
   }
+  wait_vmcnt<0>();   // the stream's last (zero-filling) block loads land before the workgroup ends
+}
+
+// ------------------------------------------------------------ dK / dV, D = 256
+// At D = 256 one wave of the kernel above would need 2 x 128 accumulation
+// registers for the dV and dK blocks of its 32 keys plus 128 for their K and
+// V rows: more than a wave's 512.  Here two waves share each 32-key block
+// and split the work by role:
+//   role 0 (waves 0, 2): S = Q_hat K^T, P = exp2(S kscale - lse log2 e),
+//                        dV^T += dO^T P
+//   role 1 (waves 1, 3): dP = dO V^T, dS = P (dP - Delta),
+//                        dK_hat^T += Q_hat^T dS
+// Each wave holds one accumulator (128 registers) and one operand row set
+// (K for role 0, V for role 1: 64 registers), and issues per step the same
+// 32 products as a wave of the kernel above.  A tile is 64 keys (two pairs of waves).  Role 0
+// hands P to role 1 through LDS in fp32, so dS is formed from the unrounded
+// probabilities as in the kernel above: role 0 writes P of block it + 1 during
+// step it, role 1 reads it after the step's barrier and forms dS of that
+// block beside its next dP products, one step behind role 0 (its dP
+// accumulators alternate between two register sets).  The query-block stream,
+// the tile list and the epilogues are those of the kernel above; the K and V
+// rows go straight to registers at each tile's start.
+template <bool GROUPED, bool ROPE>
+struct DkdvSplitCfg {
+  static constexpr int D = 256;
+  static constexpr int BNK = 64;        // keys per tile (32 per pair of waves)
+  static constexpr int BMQ = 32;        // queries per step
+  static constexpr int NBUF = 3;
+  static constexpr int KS = D / 16;
+  static constexpr int NB = D / 32;
+  static constexpr int P = D + 24;      // q_hat / dO row pitch (bf16): odd multiple of 16 bytes
+  using Tile = DmaTileV<BMQ * P / 8, 4, 12 + GROUPED + 2 * ROPE>;
+  static constexpr int DO_B = Tile::BYTES;          // dO tile after the q_hat tile
+  static constexpr int ST_B = 2 * Tile::BYTES;      // 4 x 256 B: spare, spare, lse2, Delta
+  static constexpr int STAGE = ST_B + 1024;
+  static constexpr int XP_B = NBUF * STAGE;         // P of each pair, two buffers: 16 fp32 per lane
+  static constexpr int XP_SLOT = 64 * 64;
+  static constexpr int OP = D + 8;                  // output staging row pitch (bf16)
+  static constexpr int OUT_SLOT = 32 * OP * 2;      // one wave's 32 x D bf16 block
+  static constexpr int XO_B = XP_B + 4 * XP_SLOT;   // staging slots of waves 2 and 3
+  static constexpr int LDS_BYTES = XO_B + 2 * OUT_SLOT;
+  static constexpr int NSTORE = 32 * D / 8 / 64;    // epilogue stores per lane of one output
+  static_assert(2 * OUT_SLOT <= STAGE, "waves 0 and 1 stage their outputs in a freed step buffer");
+  static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
+};
+
+template <bool GROUPED, bool ROPE>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
+    const uint16_t* __restrict__ qhat, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse2, const float* __restrict__ delta,
+    const float* __restrict__ kscale, const uint16_t* __restrict__ rcos,
+    const uint16_t* __restrict__ rsin, const uint16_t* __restrict__ ve,
+    const float* __restrict__ gate, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    uint16_t* __restrict__ dve, float* __restrict__ dz, int T, int H, int G_arg, int W, int nkt,
+    int ntiles) {
+  using C = DkdvSplitCfg<GROUPED, ROPE>;
+  constexpr int D = C::D;
+  const int G = GROUPED ? G_arg : 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int w = uniform(tid >> 6);
+  const int pair = w >> 1;
+  const int lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int rs = H * D;                 // query-side row stride (q_hat, dO)
+  const long long rsb = 2LL * rs;
+  const long long slice_bytes = (long long)(T - 1) * rsb + 2 * D;
+  const int Hkv = H / G;
+  const int rs_kv = Hkv * D;            // key-side row stride (K, V, dK, dV)
+  const long long rsb_kv = 2LL * rs_kv;
+  const long long kslice_bytes = (long long)(T - 1) * rsb_kv + 2 * D;
+
+  // Each role runs its own copy of the whole walk (the role is fixed per
+  // wave), so the two roles' registers never meet; both copies pass the same
+  // barriers in the same order.
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+  constexpr int role = decltype(role_c)::value ? 1 : 0;
+    // ---- tile list of this workgroup (as in the kernel above)
+    int xr = 0, ws = blockIdx.x, G8 = gridDim.x, N8 = ntiles;
+    if ((ntiles & 7) == 0 && (gridDim.x & 7) == 0) {
+      xr = blockIdx.x & 7;
+      ws = blockIdx.x >> 3;
+      G8 = gridDim.x >> 3;
+      N8 = ntiles >> 3;
+    }
+    auto tile_at = [&](int i) {
+      const int r = i * G8 + (ws + 7 * i) % G8;
+      return (i * G8 < N8 && r < N8) ? xr * N8 + r : -1;
+    };
+    struct TileGeo {
+      int bh, b, hk, j0, qb0, nsteps;
+    };
+    auto geo = [&](int t) {
+      TileGeo tg;
+      tg.bh = t / nkt;
+      tg.b = tg.bh / Hkv;
+      tg.hk = tg.bh - tg.b * Hkv;
+      tg.j0 = (t % nkt) * C::BNK;
+      int q_lo, q_hi;
+      const bool any = q_range(tg.j0, tg.j0 + C::BNK - 1, T, W, &q_lo, &q_hi);
+      tg.qb0 = any ? q_lo / C::BMQ : 0;
+      tg.nsteps = any ? q_hi / C::BMQ - tg.qb0 + 1 : 0;
+      return tg;
+    };
+  
+    // ---- the stream of query blocks across tiles and query heads (as above)
+    typename C::Tile tile;
+    tile.init(w, lane, [&](int qc) {
+      const int r = qc / (C::P / 8), ch = qc % (C::P / 8);
+      return (r < C::BMQ && ch < D / 8) ? (r * rs + 8 * ch) * 2 : -1;
+    });
+    struct DmaPlan {
+      const uint16_t* qh;
+      const uint16_t* dO;
+      const float* st;
+      uint32_t nbytes;
+      int nst;
+      int r0;
+    };
+    int dt = 0, ds = 0, dgi = 0;
+    TileGeo dgeo;
+    const uint16_t* cq = qhat;
+    const uint16_t* cdo = dout;
+    const float* cst = w == 2 ? lse2 : delta;
+    uint32_t cbytes = 0;
+    int cr0 = 0;
+    auto seek_head = [&]() {
+      const int hq = dgeo.hk * G + dgi;
+      const size_t sbase = ((size_t)dgeo.b * T * H + hq) * D;
+      cr0 = dgeo.qb0 * C::BMQ;
+      cq = qhat + sbase + (size_t)cr0 * rs;
+      cdo = dout + sbase + (size_t)cr0 * rs;
+      cbytes = (uint32_t)(slice_bytes - cr0 * rsb);
+      cst = (w == 2 ? lse2 : delta) + (size_t)(dgeo.b * H + hq) * T;
+    };
+    int tcur = tile_at(0);
+    if (tcur >= 0) {
+      dgeo = geo(tcur);
+      seek_head();
+    }
+    auto plan_next = [&]() {
+      while (tcur >= 0 && ds >= dgeo.nsteps) {
+        ds = 0;
+        if (++dgi >= G) {
+          dgi = 0;
+          ++dt;
+          tcur = tile_at(dt);
+          if (tcur >= 0) dgeo = geo(tcur);
+        }
+        if (tcur >= 0) seek_head();
+      }
+      DmaPlan pl;
+      const bool ok = tcur >= 0;
+      pl.qh = cq;
+      pl.dO = cdo;
+      pl.st = cst;
+      pl.r0 = ok ? cr0 : 0;
+      pl.nbytes = ok ? cbytes : 0u;
+      pl.nst = (ok && w >= 2) ? 4 * T : 0;
+      if (ok) {
+        ++ds;
+        cq += (size_t)C::BMQ * rs;
+        cdo += (size_t)C::BMQ * rs;
+        cbytes -= (uint32_t)(C::BMQ * rsb);
+        cr0 += C::BMQ;
+      }
+      return pl;
+    };
+    auto issue_plan = [&](const DmaPlan& pl, int base) {
+      tile.issue(make_desc_u(pl.qh, pl.nbytes), smem, base, w);
+      tile.issue(make_desc_u(pl.dO, pl.nbytes), smem, base + C::DO_B, w);
+      dma_row4(make_desc(pl.st, pl.nst), smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
+    };
+    constexpr int NDMA = 2 * C::Tile::NIW + 1;
+    auto issue_plan_one = [&](const u32x4& dq_, const u32x4& ddo, const u32x4& dst, const DmaPlan& pl, int base,
+                              int j) {
+      if (j < C::Tile::NIW) tile.issue_one(dq_, smem, base, w, j);
+      else if (j < 2 * C::Tile::NIW) tile.issue_one(ddo, smem, base + C::DO_B, w, j - C::Tile::NIW);
+      else dma_row4(dst, smem, base + C::ST_B + 256 * w, (pl.r0 + lane) * 4);
+    };
+  
+    // per-lane byte offsets inside a stage buffer
+    const int a_off = 2 * (c * C::P + 8 * g);          // row-major A operands (16-byte reads)
+    const int t_off = 2 * tr_off(lane, C::P);          // transposed A operands
+    const int l_off = C::ST_B + 512 + 16 * g;          // lse2 (+ 0) / Delta (+ 256) of the lane's query quads
+    const int x_off = C::XP_B + 2 * C::XP_SLOT * pair + 16 * lane;   // P of the pair: + XP_SLOT * buffer + 1024 q4
+  
+    int b0 = 2 * C::STAGE, b1 = 0, b2 = C::STAGE;
+    issue_plan(plan_next(), b1);
+    issue_plan(plan_next(), b2);
+    DmaPlan pnext = plan_next();
+  
+    u32x4 kv[C::KS];              // role 0: the tile's K rows of the pair's keys; role 1: V rows
+    f32x16 acc[C::NB];            // role 0: dV^T blocks; role 1: dK_hat^T blocks
+    f32x16 dpa, dpb;              // role 0: S in dpa; role 1: dP of block it in dpa (even it) or dpb (odd)
+    u32x4 pf[2];                  // role 0: bf16 P of the block C works on
+    const std::integral_constant<bool, true> masked{};
+    const std::integral_constant<bool, false> unmasked{};
+  
+    for (int ti = 0;; ++ti) {
+      const int t = tile_at(ti);
+      if (t < 0) break;
+      const TileGeo tg = geo(t);
+      const int bh = tg.bh, j0 = tg.j0, qb0 = tg.qb0, nsteps = tg.nsteps;
+      const size_t sbase = ((size_t)tg.b * T * Hkv + tg.hk) * D;
+      const int kw0 = j0 + 32 * pair;
+      const int kj = kw0 + c;
+  
+      // ---- tile prologue: blocks 0 and 1 have landed (older than the previous
+      // tile's output stores, which may stay in flight)
+      if (ti == 0) wait_vmcnt<0>();
+      else wait_vmcnt<C::NSTORE>();
+      __syncthreads();
+      const float ksc = bload4f(make_rsrc(kscale + (size_t)bh * T, 4LL * T), kj * 4);
+      const int lim = imin(W, T - 1 - kj);
+      {
+        const int t_ = b0;
+        b0 = b1;
+        b1 = b2;
+        b2 = t_;
+      }
+      {
+        const rsrc_t rkv = make_rsrc((role == 0 ? k : v) + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) kv[ks] = bload16(rkv, (c * rs_kv + 16 * ks + 8 * g) * 2);
+      }
+#pragma unroll
+      for (int n = 0; n < C::NB; ++n) acc[n] = f32x16{};
+  
+      // C's transposed A operand of product m = NB s2 + n: dO^T (role 0) or
+      // Q_hat^T (role 1) of the block in buffer `base`, rows 16 s2 .., column
+      // block n (element j of k-step s2 is query 16 s2 + 4 g + (j % 4) + 8 (j / 4))
+      constexpr int NC = 2 * C::NB;
+      auto c_read = [&](int base, int m) {
+        constexpr int R8 = 2 * 8 * C::P;
+        const int s2 = m / C::NB, n = m % C::NB;
+        const int off = base + t_off + (role == 0 ? C::DO_B : 0) + 2 * (16 * s2 * C::P + 32 * n);
+        const u32x2 x0 = lds_tr4b(smem, off), x1 = lds_tr4b(smem, off + R8);
+        return u32x4{x0[0], x0[1], x1[0], x1[1]};
+      };
+      // role 0: P of the block's register r (query q0 + 8 (r / 4) + 4 g + r % 4, key kj)
+      auto p_value = [&](int r, f32x4 l4, int tq, bool msk) {
+        float p = __builtin_amdgcn_exp2f(dpa[r] * ksc - l4[r & 3]);
+        if (msk) p = ((unsigned)(tq + 8 * (r >> 2) + (r & 3)) <= (unsigned)lim) ? p : 0.f;
+        return p;
+      };
+  
+      // prologue products: role 0 S and P of block 0 (P to the exchange buffer
+      // 0), role 1 dP of block 0
+      if constexpr (role == 0) {
+        const int va = b0 + a_off, vl = b0 + l_off;
+        dpa = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) dpa = mfma32(lds16(smem, va + 32 * ks), kv[ks], dpa);
+        const int tq = qb0 * C::BMQ + 4 * g - kj;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 l4 = lds16f(smem, vl + 32 * q4);
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[e] = p_value(4 * q4 + e, l4, tq, true);
+          *reinterpret_cast<f32x4*>(smem + x_off + 1024 * q4) = f32x4{p[0], p[1], p[2], p[3]};
+          const int st = q4 >> 1, el = 2 * (q4 & 1);
+          pf[st][el] = pack_bf16(p[0], p[1]);
+          pf[st][el + 1] = pack_bf16(p[2], p[3]);
+        }
+      } else {
+        const int va = b0 + a_off + C::DO_B;
+        dpa = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) dpa = mfma32(lds16(smem, va + 32 * ks), kv[ks], dpa);
+      }
+      __syncthreads();   // P of block 0 is visible to role 1
+  
+      // One step `it`: A(it+1), B, C(it) as in the kernel above, written out in
+      // fenced regions.  Role 0: S(it+1)'s products with block it + 2's loads
+      // between them, then C(it)'s dV products, each beside one element of
+      // P(it+1) (written to the exchange buffer (it + 1) % 2 by quads).  Role 1:
+      // dP(it+1)'s products with the loads, each beside one element of dS(it) =
+      // P(it) (dP(it) - Delta(it)) (P(it) from the exchange buffer it % 2), then
+      // C(it)'s dK products.  PH = it % 2 picks role 1's dP registers.
+      auto step_body = [&](int it, int s_next, auto masked_c, auto ph_c) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        constexpr bool PH = decltype(ph_c)::value;
+        constexpr int KA = 2, CA = 2;
+        const u32x4 dq_ = make_desc_u(pnext.qh, pnext.nbytes), ddo = make_desc_u(pnext.dO, pnext.nbytes);
+        const u32x4 dst = make_desc(pnext.st, pnext.nst);
+        u32x4 opa[C::KS], cop[NC];
+        if constexpr (role == 0) {
+          const int va = b1 + a_off, vl = b1 + l_off;
+          f32x4 l4s[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) l4s[q4] = lds16f(smem, vl + 32 * q4);
+#pragma unroll
+          for (int ks = 0; ks < KA; ++ks) opa[ks] = lds16(smem, va + 32 * ks);
+#pragma unroll
+          for (int m = 0; m < CA; ++m) cop[m] = c_read(b0, m);
+          __builtin_amdgcn_sched_barrier(0);
+          dpa = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            if (ks + KA < C::KS) opa[ks + KA] = lds16(smem, va + 32 * (ks + KA));
+            dpa = mfma32(opa[ks], kv[ks], dpa);
+            if (ks < NDMA) issue_plan_one(dq_, ddo, dst, pnext, b2, ks);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int j = C::KS; j < NDMA; ++j) issue_plan_one(dq_, ddo, dst, pnext, b2, j);
+          const int tq = (qb0 + s_next) * C::BMQ + 4 * g - kj;
+          const int xw = x_off + C::XP_SLOT * ((it + 1) & 1);
+          float pe[16];
+          u32x4 pn[2];
+#pragma unroll
+          for (int m = 0; m < NC; ++m) {
+            if (m + CA < NC) cop[m + CA] = c_read(b0, m + CA);
+            acc[m % C::NB] = mfma32(cop[m], pf[m / C::NB], acc[m % C::NB]);
+            const int r = m, q4 = r >> 2;
+            pe[r] = p_value(r, l4s[q4], tq, MASKED);
+            asm volatile("" : "+v"(pe[r]));
+            if (r & 1) {
+              const int st = q4 >> 1, el = 2 * (q4 & 1) + ((r & 3) >> 1);
+              pn[st][el] = pack_bf16(pe[r - 1], pe[r]);
+              asm volatile("" : "+v"(pn[st][el]));
+            }
+            if ((r & 3) == 3)
+              *reinterpret_cast<f32x4*>(smem + xw + 1024 * q4) = f32x4{pe[r - 3], pe[r - 2], pe[r - 1], pe[r]};
+            if (m == NC / 2) pnext = plan_next();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          pf[0] = pn[0];
+          pf[1] = pn[1];
+        } else {
+          f32x16& dp_cur = PH ? dpb : dpa;   // dP(it)
+          f32x16& dp_nxt = PH ? dpa : dpb;   // dP(it + 1)
+          const int va = b1 + a_off + C::DO_B, vd = b0 + l_off + 256;
+          const int xr_ = x_off + C::XP_SLOT * (it & 1);
+          f32x4 d4s[4], xp[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            xp[q4] = lds16f(smem, xr_ + 1024 * q4);
+            d4s[q4] = lds16f(smem, vd + 32 * q4);
+          }
+#pragma unroll
+          for (int ks = 0; ks < KA; ++ks) opa[ks] = lds16(smem, va + 32 * ks);
+#pragma unroll
+          for (int m = 0; m < CA; ++m) cop[m] = c_read(b0, m);
+          __builtin_amdgcn_sched_barrier(0);
+          dp_nxt = f32x16{};
+          float de[16];
+          u32x4 dn[2];
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            if (ks + KA < C::KS) opa[ks + KA] = lds16(smem, va + 32 * (ks + KA));
+            dp_nxt = mfma32(opa[ks], kv[ks], dp_nxt);
+            if (ks < NDMA) issue_plan_one(dq_, ddo, dst, pnext, b2, ks);
+            const int r = ks, q4 = r >> 2, i = r & 3;
+            de[r] = xp[q4][i] * (dp_cur[r] - d4s[q4][i]);
+            asm volatile("" : "+v"(de[r]));
+            if (r & 1) {
+              const int st = q4 >> 1, el = 2 * (q4 & 1) + (i >> 1);
+              dn[st][el] = pack_bf16(de[r - 1], de[r]);
+              asm volatile("" : "+v"(dn[st][el]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int j = C::KS; j < NDMA; ++j) issue_plan_one(dq_, ddo, dst, pnext, b2, j);
+#pragma unroll
+          for (int m = 0; m < NC; ++m) {
+            if (m + CA < NC) cop[m + CA] = c_read(b0, m + CA);
+            acc[m % C::NB] = mfma32(cop[m], dn[m / C::NB], acc[m % C::NB]);
+            if (m == NC / 2) pnext = plan_next();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        const int t_ = b0;
+        b0 = b1;
+        b1 = b2;
+        b2 = t_;
+        wait_vmcnt<0>();            // block it + 2 has landed
+        __syncthreads();            // and P(it + 1) is visible to role 1
+      };
+      auto step = [&](int it, int s_next, auto masked_c) __attribute__((always_inline)) {
+        if (it & 1) step_body(it, s_next, masked_c, masked);
+        else step_body(it, s_next, masked_c, unmasked);
+      };
+  
+      // masked head, unmasked middle and masked tail of each query head's band
+      // (as in the kernel above; body `it` prepares block it + 1)
+      const int kv_last = imin(j0 + C::BNK - 1, T - 1);
+      int full_lo = 0, full_hi = -1;
+      if (nsteps > 0) {
+        const int qf0 = kv_last;
+        const int qf1 = imin(j0 + W, T) - (C::BMQ - 1);
+        full_lo = imax(0, (qf0 + C::BMQ - 1) / C::BMQ - qb0);
+        full_hi = qf1 >= 0 ? qf1 / C::BMQ - qb0 : -1;
+        full_hi = imin(full_hi, nsteps - 1);
+      }
+      const int nloop = G * nsteps - 1;
+      int it = 0;
+      for (int gi = 0; gi < G; ++gi) {
+        const int base = gi * nsteps;
+        const int it_end = imin(base + nsteps - 1, nloop);
+        for (; it < imin(base + full_lo - 1, it_end); ++it) step(it, it + 1 - base, masked);
+        for (; it < imin(base + full_hi, it_end); ++it) step(it, it + 1 - base, unmasked);
+        for (; it < it_end; ++it) step(it, it + 1 - base, masked);
+      }
+  
+      // rotary tables of key kj for role 1's epilogue, in flight with the last
+      // products
+      u32x2 tc[C::NB / 2][4], tsn[C::NB / 2][4];
+      if constexpr (ROPE && role == 1) {
+        const long long tb = (long long)(T - kw0) * D;
+        const rsrc_t rc = make_rsrc(rcos + (size_t)kw0 * (D / 2), tb);
+        const rsrc_t rn = make_rsrc(rsin + (size_t)kw0 * (D / 2), tb);
+#pragma unroll
+        for (int n = 0; n < C::NB / 2; ++n)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int off = (c * (D / 2) + 32 * n + 8 * q4 + 4 * g) * 2;
+            tc[n][q4] = bload8(rc, off);
+            tsn[n][q4] = bload8(rn, off);
+          }
+      }
+      const bool has_ve = ve != nullptr;
+      issue_plan(pnext, b2);          // the next tile's block 1 (or later) into the free buffer
+      pnext = plan_next();
+      // the last block's C: role 0 with its P, role 1 with dS formed from the
+      // P in exchange buffer nloop % 2
+#pragma unroll
+      for (int m = 0; m < NC; ++m) {
+        if constexpr (role == 0) acc[m % C::NB] = mfma32(c_read(b0, m), pf[m / C::NB], acc[m % C::NB]);
+      }
+      if constexpr (role == 1) {
+        const f32x16 dpl = (nloop & 1) ? dpb : dpa;
+        const int xr_ = x_off + C::XP_SLOT * (nloop & 1), vd = b0 + l_off + 256;
+        u32x4 dn[2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 xp = lds16f(smem, xr_ + 1024 * q4), d4 = lds16f(smem, vd + 32 * q4);
+          float de[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) de[e] = xp[e] * (dpl[4 * q4 + e] - d4[e]);
+          const int st = q4 >> 1, el = 2 * (q4 & 1);
+          dn[st][el] = pack_bf16(de[0], de[1]);
+          dn[st][el + 1] = pack_bf16(de[2], de[3]);
+        }
+#pragma unroll
+        for (int m = 0; m < NC; ++m) acc[m % C::NB] = mfma32(c_read(b0, m), dn[m / C::NB], acc[m % C::NB]);
+      }
+  
+      // ---- epilogue.  Lane (g, c) holds key kj, d = 32 n + 8 q4 + 4 g + e.
+      // Role 1: dK, the RMSNorm backward of K with the rotary embedding turned
+      // back; K of the key is read again in that order (role 1 held V), in
+      // pieces, twice (the second time from L2), so it never occupies 64
+      // registers beside the accumulators.  Role 0: dV, and with the gate
+      // dve = gate dV and dz = (dV . ve) gate (1 - gate / 2).  The outputs
+      // leave through LDS as whole rows (waves 0 and 1 stage in the buffer of
+      // the last step, free after the barrier; waves 2 and 3 in their own
+      // slots).  Addresses are one per-lane base plus uniform or immediate
+      // offsets.
+      const float rk = ksc * (sqrtf((float)D) / kLog2e);
+      const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+      const int lane_kv = (c * rs_kv + 4 * g) * 2;                 // + 2 (32 n + 8 q4): key kj's pieces
+      const int slot = w < 2 ? b0 + C::OUT_SLOT * w : C::XO_B + C::OUT_SLOT * (w - 2);
+      const int st_lane = slot + 2 * (c * C::OP + 4 * g);          // + 2 (32 n + 8 q4)
+      const int rd_lane = slot + 2 * ((lane >> 5) * C::OP + 8 * (lane & 31));   // + 4 OP i
+      const int gl_lane = ((lane >> 5) * rs_kv + 8 * (lane & 31)) * 2;         // + 4 rs_kv i (bytes)
+      const rsrc_t rrow = make_rsrc(k + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+      auto stage8 = [&](int n, int q4, const float* y) {
+        st8(smem + st_lane + 2 * (32 * n + 8 * q4), u32x2{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])});
+      };
+      auto store_rows = [&](uint16_t* dst) {
+        const rsrc_t ro = make_rsrc(dst + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+#pragma unroll
+        for (int i = 0; i < C::NSTORE; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(lds16(smem, rd_lane + 4 * C::OP * i), ro, gl_lane,
+                                                 4 * rs_kv * i, 0);
+      };
+      if constexpr (role == 1) {
+        auto khat4 = [&](int n, int q4, float* x) {
+          const u32x2 u = bload8(rrow, lane_kv + 2 * (32 * n + 8 * q4));
+          x[0] = bf_lo(u[0]) * rk;
+          x[1] = bf_hi(u[0]) * rk;
+          x[2] = bf_lo(u[1]) * rk;
+          x[3] = bf_hi(u[1]) * rk;
+        };
+        float dot = 0.f;
+#pragma unroll
+        for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float x[4];
+            khat4(n, q4, x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dot += acc[n][4 * q4 + e] * x[e];
+          }
+        dot = (dot + __shfl_xor(dot, 32)) * inv_sqrt_d;
+        const float mean = dot * (1.0f / D);
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < (ROPE ? C::NB / 2 : C::NB); ++n)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float x1[4], y1[4];
+            khat4(n, q4, x1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y1[e] = rk * (acc[n][4 * q4 + e] * inv_sqrt_d - x1[e] * mean);
+            if constexpr (ROPE) {
+              float x2[4], y2[4];
+              khat4(n + C::NB / 2, q4, x2);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                y2[e] = rk * (acc[n + C::NB / 2][4 * q4 + e] * inv_sqrt_d - x2[e] * mean);
+              rope4_bwd(y1, y2, tc[n][q4], tsn[n][q4]);
+              stage8(n + C::NB / 2, q4, y2);
+            }
+            stage8(n, q4, y1);
+          }
+        store_rows(dk);
+      } else {
+        float gk = 0.f;
+        if (has_ve) {   // dz of key kj: dV . ve over the key's 256 channels
+          const rsrc_t rve = make_rsrc(ve + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+          gk = bload4f(make_rsrc(gate + (size_t)bh * T, 4LL * T), kj * 4);
+          float dg = 0.f;
+#pragma unroll
+          for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const u32x2 u = bload8(rve, lane_kv + 2 * (32 * n + 8 * q4));
+              const float x[4] = {bf_lo(u[0]), bf_hi(u[0]), bf_lo(u[1]), bf_hi(u[1])};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dg += acc[n][4 * q4 + e] * x[e];
+            }
+          dg += __shfl_xor(dg, 32);
+          if (g == 0)
+            bstore4f(dg * gk * (1.0f - 0.5f * gk),
+                     make_rsrc(dz + (size_t)tg.b * T * Hkv, 4LL * T * Hkv), (kj * Hkv + tg.hk) * 4);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float y[4] = {acc[n][4 * q4], acc[n][4 * q4 + 1], acc[n][4 * q4 + 2], acc[n][4 * q4 + 3]};
+            stage8(n, q4, y);
+          }
+        store_rows(dv);
+        if (has_ve) {
+#pragma unroll
+          for (int n = 0; n < C::NB; ++n)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              float y[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] = gk * acc[n][4 * q4 + e];
+              stage8(n, q4, y);
+            }
+          store_rows(dve);
+        }
+      }
+    }
+  };
+  if (w & 1) run(std::integral_constant<bool, true>{});
+  else run(std::integral_constant<bool, false>{});
   wait_vmcnt<0>();   // the stream's last (zero-filling) block loads land before the workgroup ends
 }
 
@@ -1204,6 +1731,15 @@ static hipError_t set_dkdv_lds() {
   return attr;
 }
 
+template <bool GROUPED, bool ROPE>
+static hipError_t set_dkdv_split_lds() {
+  using C = DkdvSplitCfg<GROUPED, ROPE>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(bwd_dkdv_split_kernel<GROUPED, ROPE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  return attr;
+}
+
 template <int D, bool ROPE>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const int G = a.H / a.Hkv;
@@ -1237,26 +1773,45 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     prof_end(t2);
   }
   {
-    using C = DkdvCfg<D, false, ROPE>;
-    static_assert(C::LDS_BYTES == DkdvCfg<D, true, ROPE>::LDS_BYTES, "one LDS size for both versions");
-    const hipError_t attr = G == 1 ? set_dkdv_lds<D, false, ROPE>() : set_dkdv_lds<D, true, ROPE>();
-    if (attr != hipSuccess) return attr;
-    const int nkt = (a.T + C::BNK - 1) / C::BNK;
-    const int ntiles = nkt * a.B * a.Hkv;
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
       return hipErrorInvalidDevice;
-    const int grid = imin(ncu, ntiles);   // persistent: one workgroup per CU
-    ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
-    hipLaunchKernelGGL((G == 1 ? bwd_dkdv_kernel<D, false, ROPE> : bwd_dkdv_kernel<D, true, ROPE>),
-                       dim3(grid), dim3(256), C::LDS_BYTES, stream,
-                       (const uint16_t*)a.qhat, kk, vv, (const uint16_t*)a.dout,
-                       (const float*)a.lse2, (const float*)a.delta, (const float*)a.kscale,
-                       (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (const uint16_t*)a.ve,
-                       (const float*)a.gate, (uint16_t*)a.dk, (uint16_t*)a.dv, (uint16_t*)a.dve, a.dz,
-                       a.T, a.H, G, W, nkt, ntiles);
-    prof_end(t1);
+    if constexpr (D <= 128) {
+      using C = DkdvCfg<D, false, ROPE>;
+      static_assert(C::LDS_BYTES == DkdvCfg<D, true, ROPE>::LDS_BYTES, "one LDS size for both versions");
+      const hipError_t attr = G == 1 ? set_dkdv_lds<D, false, ROPE>() : set_dkdv_lds<D, true, ROPE>();
+      if (attr != hipSuccess) return attr;
+      const int nkt = (a.T + C::BNK - 1) / C::BNK;
+      const int ntiles = nkt * a.B * a.Hkv;
+      const int grid = imin(ncu, ntiles);   // persistent: one workgroup per CU
+      ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
+      hipLaunchKernelGGL((G == 1 ? bwd_dkdv_kernel<D, false, ROPE> : bwd_dkdv_kernel<D, true, ROPE>),
+                         dim3(grid), dim3(256), C::LDS_BYTES, stream,
+                         (const uint16_t*)a.qhat, kk, vv, (const uint16_t*)a.dout,
+                         (const float*)a.lse2, (const float*)a.delta, (const float*)a.kscale,
+                         (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (const uint16_t*)a.ve,
+                         (const float*)a.gate, (uint16_t*)a.dk, (uint16_t*)a.dv, (uint16_t*)a.dve, a.dz,
+                         a.T, a.H, G, W, nkt, ntiles);
+      prof_end(t1);
+    } else {
+      using C = DkdvSplitCfg<false, ROPE>;
+      static_assert(C::LDS_BYTES == DkdvSplitCfg<true, ROPE>::LDS_BYTES, "one LDS size for both versions");
+      const hipError_t attr = G == 1 ? set_dkdv_split_lds<false, ROPE>() : set_dkdv_split_lds<true, ROPE>();
+      if (attr != hipSuccess) return attr;
+      const int nkt = (a.T + C::BNK - 1) / C::BNK;
+      const int ntiles = nkt * a.B * a.Hkv;
+      const int grid = imin(ncu, ntiles);   // persistent: one workgroup per CU
+      ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
+      hipLaunchKernelGGL((G == 1 ? bwd_dkdv_split_kernel<false, ROPE> : bwd_dkdv_split_kernel<true, ROPE>),
+                         dim3(grid), dim3(256), C::LDS_BYTES, stream,
+                         (const uint16_t*)a.qhat, kk, vv, (const uint16_t*)a.dout,
+                         (const float*)a.lse2, (const float*)a.delta, (const float*)a.kscale,
+                         (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (const uint16_t*)a.ve,
+                         (const float*)a.gate, (uint16_t*)a.dk, (uint16_t*)a.dv, (uint16_t*)a.dve, a.dz,
+                         a.T, a.H, G, W, nkt, ntiles);
+      prof_end(t1);
+    }
   }
   if (a.ve) {
     const int nbt = a.B * a.T;

@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # (the key pre-pass is one kernel in both passes: its forward and backward
 # launches share one name and one average)
 SHORT = (("key_prep_kernel", "key_prep"), ("attn_fwd_kernel", "attn_fwd"), ("bwd_dkdv_kernel", "bwd_dkdv"),
+         ("bwd_dkdv_split_kernel", "bwd_dkdv"),
          ("bwd_dq_kernel", "bwd_dq"), ("ve_gate_bwd_kernel", "ve_gate_bwd"), ("ve_gate_dw_kernel", "ve_gate_dw"))
 
 

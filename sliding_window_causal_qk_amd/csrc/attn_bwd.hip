@@ -871,23 +871,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
       const int kw0 = j0 + 32 * pair;
       const int kj = kw0 + c;
   
-      // ---- tile prologue: blocks 0 and 1 have landed (older than the previous
-      // tile's output stores, which may stay in flight)
-      if (ti == 0) wait_vmcnt<0>();
-      else wait_vmcnt<C::NSTORE>();
-      __syncthreads();
+      // ---- tile prologue.  The pair's K (role 0) or V (role 1) rows and key
+      // scale go straight from global memory to registers (C::KS + 1 loads),
+      // issued ahead of the wait and barrier so that they are in flight while
+      // the slower role finishes the previous tile's epilogue.  Blocks 0 and 1
+      // have landed after the wait (they are older than the previous tile's
+      // output stores and these loads, which may stay in flight).
+      {
+        const rsrc_t rkv = make_rsrc((role == 0 ? k : v) + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) kv[ks] = bload16(rkv, (c * rs_kv + 16 * ks + 8 * g) * 2);
+      }
       const float ksc = bload4f(make_rsrc(kscale + (size_t)bh * T, 4LL * T), kj * 4);
+      if (ti == 0) wait_vmcnt<0>();
+      else wait_vmcnt<C::NSTORE + C::KS + 1>();
+      __syncthreads();
       const int lim = imin(W, T - 1 - kj);
       {
         const int t_ = b0;
         b0 = b1;
         b1 = b2;
         b2 = t_;
-      }
-      {
-        const rsrc_t rkv = make_rsrc((role == 0 ? k : v) + sbase + (size_t)kw0 * rs_kv, kslice_bytes - kw0 * rsb_kv);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) kv[ks] = bload16(rkv, (c * rs_kv + 16 * ks + 8 * g) * 2);
       }
 #pragma unroll
       for (int n = 0; n < C::NB; ++n) acc[n] = f32x16{};

@@ -287,14 +287,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int kw0 = j0 + 32 * w;
     const int kj = kw0 + c;
 
-    // ---- tile prologue: steps 0 and 1 of this tile and its K / V rows have
-    // landed (they are older than the previous tile's dK / dV stores, which
-    // may stay in flight); the buffer of the previous tile's last step takes
-    // step 2
-    if (ti == 0) wait_vmcnt<0>();
-    else wait_vmcnt<C::NSTORE>();
-    __syncthreads();
+    // ---- tile prologue: the key scale is issued first; then steps 0 and 1 of
+    // this tile and its K / V rows have landed (they are older than the
+    // previous tile's dK / dV stores and that load, which may stay in flight);
+    // the buffer of the previous tile's last step takes step 2
     const float ksc = bload4f(make_rsrc(kscale + (size_t)bh * T, 4LL * T), kj * 4);
+    if (ti == 0) wait_vmcnt<0>();
+    else wait_vmcnt<C::NSTORE + 1>();
+    __syncthreads();
     // visibility on partial blocks: 0 <= q - kj <= lim, lim = min(W, T - 1 - kj)
     const int lim = imin(W, T - 1 - kj);
     {
@@ -384,10 +384,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // its product and waited for it there, and sank the softmax next to C's
     // products alone; the order is therefore written out in regions fenced with
     // scheduling barriers:
-    //   every read of A(it+1), C(it)'s first CA and B's lse2;
-    //   S's products, with block it + 2's loads between them (one each);
+    //   the reads of S's first QA operands;
+    //   S's products, with block it + 2's loads between them (one each) and
+    //   the other reads of A(it+1) and B's lse2 (a burst of every read at the
+    //   step's start left the matrix pipe idle until most had landed);
     //   dP's products, with NPA of B(it+1)'s exponentials between them (P needs
-    //   only S) and B's Delta read;
+    //   only S), C(it)'s first CA operand reads and B's Delta read;
     //   C(it)'s products, each after the reads of the product CA places later,
     //   with the remaining exponentials, dS = P (dP - Delta) and the bf16
     //   packing between them, and the next block's plan halfway.
@@ -397,14 +399,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       {
         constexpr int CA = 4;     // C operands read ahead
         const int va = b1 + a_off, vl = b1 + l_off;
+        constexpr int QA = C::KS / 2;   // S operands read before the first product
         u32x4 qa[C::KS], da[C::KS], cop[NM];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          qa[ks] = lds16(smem, va + 32 * ks);
-          da[ks] = lds16(smem, va + C::DO_B + 32 * ks);
-        }
-#pragma unroll
-        for (int m = 0; m < CA; ++m) cop[m] = c_read(b0, m);
+        for (int ks = 0; ks < QA; ++ks) qa[ks] = lds16(smem, va + 32 * ks);
         // block it + 2's loads go out one instruction per product of S, in the
         // shadow of the matrix pipe
         const u32x4 dq_ = make_desc_u(pnext.qh, pnext.nbytes), ddo = make_desc_u(pnext.dO, pnext.nbytes);
@@ -412,13 +410,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         constexpr bool MASKED = decltype(masked_c)::value;
         const int tq = (qb0 + s_next) * C::BMQ + 4 * g - kj;
         f32x4 l4s[4], d4s[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) l4s[q4] = lds16f(smem, vl + 32 * q4);
         __builtin_amdgcn_sched_barrier(0);
         s_acc = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           s_acc = mfma32(qa[ks], kf[ks], s_acc);
+          // the remaining operand reads of A(it+1) and B's lse2, in the
+          // products' shadow: each lands a few products before its use
+          if (ks + QA < C::KS) qa[ks + QA] = lds16(smem, va + 32 * (ks + QA));
+          da[ks] = lds16(smem, va + C::DO_B + 32 * ks);
+          if (ks >= C::KS - 4) l4s[ks - (C::KS - 4)] = lds16f(smem, vl + 32 * (ks - (C::KS - 4)));
           if (ks < NDMA) issue_plan_one(dq_, ddo, dst, pnext, b2, ks);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -441,6 +442,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           dp_acc = mfma32(da[ks], vf[ks], dp_acc);
+          if (ks < CA) cop[ks] = c_read(b0, ks);     // C(it)'s first operands
           if (ks + C::KS < NDMA) issue_plan_one(dq_, ddo, dst, pnext, b2, ks + C::KS);
           if (ks == 0) {
 #pragma unroll

@@ -859,7 +859,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
   
     u32x4 kv[C::KS];              // role 0: the tile's K rows of the pair's keys; role 1: V rows
     f32x16 acc[C::NB];            // role 0: dV^T blocks; role 1: dK_hat^T blocks
-    f32x16 dpa, dpb;              // role 0: S in dpa; role 1: dP of block it in dpa (even it) or dpb (odd)
+    f32x16 dpa, dpb;              // role 0: S in dpa; role 1: dP of block it in dpa, of block it + 1 in dpb
     u32x4 pf[2];                  // role 0: bf16 P of the block C works on
     const std::integral_constant<bool, true> masked{};
     const std::integral_constant<bool, false> unmasked{};
@@ -949,10 +949,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
       // P(it+1) (written to the exchange buffer (it + 1) % 2 by quads).  Role 1:
       // dP(it+1)'s products with the loads, each beside one element of dS(it) =
       // P(it) (dP(it) - Delta(it)) (P(it) from the exchange buffer it % 2), then
-      // C(it)'s dK products.  PH = it % 2 picks role 1's dP registers.
-      auto step_body = [&](int it, int s_next, auto masked_c, auto ph_c) __attribute__((always_inline)) {
+      // C(it)'s dK products; dP(it + 1) then moves to dP(it)'s registers.  (A
+      // body that alternated the two by the parity of it was two bodies in one
+      // loop, and the compiler copied the accumulators between them.)
+      auto step_body = [&](int it, int s_next, auto masked_c) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_c)::value;
-        constexpr bool PH = decltype(ph_c)::value;
         constexpr int KA = 2, CA = 2;
         const u32x4 dq_ = make_desc_u(pnext.qh, pnext.nbytes), ddo = make_desc_u(pnext.dO, pnext.nbytes);
         const u32x4 dst = make_desc(pnext.st, pnext.nst);
@@ -1001,8 +1002,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
           pf[0] = pn[0];
           pf[1] = pn[1];
         } else {
-          f32x16& dp_cur = PH ? dpb : dpa;   // dP(it)
-          f32x16& dp_nxt = PH ? dpa : dpb;   // dP(it + 1)
+          f32x16& dp_cur = dpa;   // dP(it)
+          f32x16& dp_nxt = dpb;   // dP(it + 1)
           const int va = b1 + a_off + C::DO_B, vd = b0 + l_off + 256;
           const int xr_ = x_off + C::XP_SLOT * (it & 1);
           f32x4 d4s[4], xp[4];
@@ -1043,6 +1044,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
             if (m == NC / 2) pnext = plan_next();
             __builtin_amdgcn_sched_barrier(0);
           }
+          dp_cur = dp_nxt;
         }
         const int t_ = b0;
         b0 = b1;
@@ -1052,8 +1054,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
         __syncthreads();            // and P(it + 1) is visible to role 1
       };
       auto step = [&](int it, int s_next, auto masked_c) __attribute__((always_inline)) {
-        if (it & 1) step_body(it, s_next, masked_c, masked);
-        else step_body(it, s_next, masked_c, unmasked);
+        step_body(it, s_next, masked_c);
       };
   
       // masked head, unmasked middle and masked tail of each query head's band
@@ -1103,7 +1104,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
         if constexpr (role == 0) acc[m % C::NB] = mfma32(c_read(b0, m), pf[m / C::NB], acc[m % C::NB]);
       }
       if constexpr (role == 1) {
-        const f32x16 dpl = (nloop & 1) ? dpb : dpa;
+        const f32x16 dpl = dpa;
         const int xr_ = x_off + C::XP_SLOT * (nloop & 1), vd = b0 + l_off + 256;
         u32x4 dn[2];
 #pragma unroll

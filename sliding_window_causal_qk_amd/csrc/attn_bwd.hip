@@ -1307,20 +1307,28 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
   using RS = RowStage32<D>;
   static_assert(4 * RS::BYTES <= C::LDS_BYTES, "row staging fits in the step buffers");
   u32x4 qf[C::KS], df[C::KS];
-  float r_q, dlt;
+  float r_q, dlt, lse_q;
   {
     const rsrc_t rqr = make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
     const rsrc_t rdo = make_rsrc(dout + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
     const rsrc_t ror = make_rsrc(o + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb);
-    float dd = 0.f;
+    // every load goes out before the first use: left to itself the compiler
+    // issued a few, waited, and issued the rest, several round trips in a row
+    u32x4 of[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       qf[ks] = bload16(rqr, (c * rs + 16 * ks + 8 * g) * 2);
       df[ks] = bload16(rdo, (c * rs + 16 * ks + 8 * g) * 2);
-      const u32x4 of = bload16(ror, (c * rs + 16 * ks + 8 * g) * 2);
+      of[ks] = bload16(ror, (c * rs + 16 * ks + 8 * g) * 2);
+    }
+    lse_q = bload4f(make_rsrc(lse + sb, 4LL * T), qi * 4);
+    __builtin_amdgcn_sched_barrier(0);
+    float dd = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        dd += bf_lo(df[ks][e]) * bf_lo(of[e]) + bf_hi(df[ks][e]) * bf_hi(of[e]);
+        dd += bf_lo(df[ks][e]) * bf_lo(of[ks][e]) + bf_hi(df[ks][e]) * bf_hi(of[ks][e]);
     }
     dd += __shfl_xor(dd, 32);
     dlt = dd;
@@ -1335,7 +1343,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     }
     RS::store_rows(smem, slot, make_rsrc(qhat + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
   }
-  const float lq = bload4f(make_rsrc(lse + sb, 4LL * T), qi * 4) * kLog2e;
+  const float lq = lse_q * kLog2e;
   if (g == 0) {
     bstore4f(dlt, make_rsrc(delta + sb, 4LL * T), qi * 4);
     bstore4f(lq, make_rsrc(lse2 + sb, 4LL * T), qi * 4);
@@ -1557,6 +1565,10 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
   for (; it < imin(u0, nloop); ++it) step_body(it, masked);
   for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
   for (; it < nloop; ++it) step_body(it, masked);
+  // the raw q rows for the epilogue's RMSNorm backward, in flight with the
+  // last block's products
+  u32x4 qrow[RS::NCHUNK];
+  RS::load_regs(qrow, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
   if (nsteps > 0) stage_c(b0);
 
   // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past
@@ -1582,7 +1594,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
   }
   __syncthreads();
   const int slot = RS::BYTES * w;
-  RS::load_rows(smem, slot, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
+  RS::put_regs(smem, slot, qrow, lane);
   float dot = 0.f;
   f32x16 xh[C::NB];
   if constexpr (ROPE) {

@@ -322,11 +322,20 @@ struct RowStage32 {
                                              (row * rs + 8 * ch) * 2, 0, 0);
     }
   }
-  static __device__ __forceinline__ void load_rows(unsigned char* smem, int slot, rsrc_t r, int rs, int lane) {
+  // the same rows in two halves: the loads into registers, then their stores
+  // to the staging block, so that the loads can fly while other work runs
+  static __device__ __forceinline__ void load_regs(u32x4* t, rsrc_t r, int rs, int lane) {
 #pragma unroll
     for (int i = 0; i < NCHUNK; ++i) {
       const int idx = lane + 64 * i, row = idx / (D / 8), ch = idx % (D / 8);
-      st16(smem + slot + 2 * (row * OP + 8 * ch), bload16(r, (row * rs + 8 * ch) * 2));
+      t[i] = bload16(r, (row * rs + 8 * ch) * 2);
+    }
+  }
+  static __device__ __forceinline__ void put_regs(unsigned char* smem, int slot, const u32x4* t, int lane) {
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) {
+      const int idx = lane + 64 * i, row = idx / (D / 8), ch = idx % (D / 8);
+      st16(smem + slot + 2 * (row * OP + 8 * ch), t[i]);
     }
   }
 };

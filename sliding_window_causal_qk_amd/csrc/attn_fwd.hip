@@ -84,7 +84,7 @@ __device__ __forceinline__ int v_slot(int r, int ch) { return ch ^ (2 * (r & 3))
 // LDS, so one workgroup runs per CU: the kernel is then built for one wave per
 // SIMD, whose 512 registers hold the accumulators and every operand in flight.
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ kscale,
     const uint16_t* __restrict__ rcos, const uint16_t* __restrict__ rsin,
@@ -236,18 +236,37 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void attn_fwd_kernel(
     stage_b(b0, 0, masked);
   }
 
+  // In the masked steps at the band's two ends a wave skips a key block that
+  // none of its 32 queries sees (all keys after the last query, or before the
+  // first one's window): no S products, P = 0, and then no PV products for
+  // it.  Adding those zeros changed nothing, so the results are unchanged;
+  // the other waves on the SIMD take the issue slots (D <= 128: two or three
+  // workgroups per CU; at D = 256 one wave per SIMD has nobody to give them to).
+  bool c_zero = false;   // P of the block C works on is all zero for this wave
   auto step_body = [&](int it, auto masked_c) {
-    stage_a(b1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    constexpr bool MASKED = decltype(masked_c)::value && D <= 128;
+    const int kb = (jb0 + it + 1) * C::BN;
+    const bool seen = !MASKED || (kb <= qw0 + 31 && kb + C::BN - 1 >= qw0 - W);
+    if (seen) {
+      stage_a(b1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < C::KS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < C::KS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_c(b0);
-    stage_b(b1, it + 1, masked_c);
+    if (!MASKED || !c_zero) stage_c(b0);
+    if (seen) {
+      stage_b(b1, it + 1, masked_c);
+    } else {
+      pf[0] = u32x4{};
+      pf[1] = u32x4{};
+    }
+    if constexpr (MASKED) c_zero = !seen;
+    else c_zero = false;
     asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(lsum));
     wait_vmcnt<0>();            // step it + 2 landed
     __syncthreads();
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void attn_fwd_kernel(
   for (; it < imin(u0, nloop); ++it) step_body(it, masked);
   for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
   for (; it < nloop; ++it) step_body(it, masked);
-  if (nsteps > 0) stage_c(b0);
+  if (nsteps > 0 && !c_zero) stage_c(b0);
 
   // ---- epilogue: O = O^T / l, lse = shift + ln l  (stores past T are dropped)
   lsum += __shfl_xor(lsum, 32);

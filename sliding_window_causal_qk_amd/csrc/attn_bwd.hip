@@ -1442,15 +1442,15 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     stage_b(b0, 0, masked);
   }
 
-  // One step: A(it+1), C(it), B(it+1).  At D <= 128 the order is written out
-  // in fenced regions, as in the dK/dV kernel: S's products (the V operands
-  // read among them), then dP's with twelve of B's sixteen exponentials (P
-  // needs only S), then C's products, each after the transposing reads of the
-  // product CA places later, with the last four exponentials and dS' = P (dP -
-  // Delta) kscale with its packing.  B(it+1) writes separate registers that
-  // C(it+1) takes over.  At D = 256 the compiler orders the step.
+  // One step: A(it+1), C(it), B(it+1), with the order written out in fenced
+  // regions, as in the dK/dV kernel: S's products (the V operands read among
+  // them), then dP's with twelve of B's sixteen exponentials (P needs only S),
+  // then C's products, each after the transposing reads of the product CA
+  // places later, with the last four exponentials and dS' = P (dP - Delta)
+  // kscale with its packing.  B(it+1) writes separate registers that C(it+1)
+  // takes over.
   auto step_body = [&](int it, auto masked_c) {
-    if constexpr (D <= 128) {
+    {
       constexpr bool MASKED = decltype(masked_c)::value;
       constexpr int NC = 2 * C::NB;   // C's products, m = NB s2 + n
       constexpr int CA = 2;
@@ -1527,19 +1527,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
       }
       dsf[0] = dn[0];
       dsf[1] = dn[1];
-    } else {
-      stage_a(b1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * C::KS - 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      stage_c(b0);
-      stage_b(b1, it + 1, masked_c);
-      asm volatile("" ::"v"(dsf[0]), "v"(dsf[1]));
     }
     wait_vmcnt<0>();            // step it + 2 landed
     __syncthreads();

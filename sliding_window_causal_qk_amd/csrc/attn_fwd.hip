@@ -243,7 +243,79 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
   // the other waves on the SIMD take the issue slots (D <= 128: two or three
   // workgroups per CU; at D = 256 one wave per SIMD has nobody to give them to).
   bool c_zero = false;   // P of the block C works on is all zero for this wave
+  // At D = 256 (one wave per SIMD) the step's order is written out in fenced
+  // regions: S's products with the K operands read KA ahead, then C's
+  // products, each after the transposing V reads of the product CA places
+  // later, with B's elements (the exponential, the mask, the bf16 packing
+  // and the row sum) between them.  B writes separate registers that C takes
+  // over at the step's end.
+  auto step_written = [&](int it, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr int KA = 4, CA = 2, NC = 2 * C::NB, EPM = 16 / NC;
+    const int va = b1 + a_off, vk = b1 + k_off, vb = b0 + C::V_B;
+    auto v_read = [&](int m) {
+      const int s2 = m / C::NB, n = m % C::NB;
+      const int off = vb + ((n & 1) ? v_odd : v_even) + 128 * (n >> 1) + 2 * D * 16 * s2;
+      const u32x2 a0 = lds_tr4b(smem, off), a1 = lds_tr4b(smem, off + 2 * D * 8);
+      return u32x4{a0[0], a0[1], a1[0], a1[1]};
+    };
+    u32x4 ka[C::KS], cop[NC];
+    f32x4 k4s[4];
+#pragma unroll
+    for (int ks = 0; ks < KA; ++ks) ka[ks] = lds16(smem, va + 32 * ks);
+#pragma unroll
+    for (int m = 0; m < CA; ++m) cop[m] = v_read(m);
+    __builtin_amdgcn_sched_barrier(0);
+    s_acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (ks + KA < C::KS) ka[ks + KA] = lds16(smem, va + 32 * (ks + KA));
+      s_acc = mfma32(ka[ks], qf[ks], s_acc);
+      if (ks == C::KS - 2) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) k4s[q4] = lds16f(smem, vk + 32 * q4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int t0 = (jb0 + it + 1) * C::BN + 4 * g + W - qi;   // key kv visible iff 0 <= kv - (qi - W) <= W
+    float pe[16];
+    u32x4 pn[2];
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {
+      if (m + CA < NC) cop[m + CA] = v_read(m + CA);
+      const int s2 = m / C::NB, n = m % C::NB;
+      acc[n] = mfma32(cop[m], pf[s2], acc[n]);
+#pragma unroll
+      for (int k = 0; k < EPM; ++k) {
+        const int r = EPM * m + k, q4 = r >> 2, e = r & 3;
+        float pr = __builtin_amdgcn_exp2f(s_acc[r] * k4s[q4][e] - shift);
+        if (MASKED) pr = ((unsigned)(t0 + 8 * q4 + e) <= (unsigned)W) ? pr : 0.f;
+        pe[r] = pr;
+        asm volatile("" : "+v"(pe[r]));
+        if (e & 1) {
+          const uint32_t pk = pack_bf16(pe[r - 1], pe[r]);
+          pn[q4 >> 1][2 * (q4 & 1) + (e >> 1)] = pk;
+          lsum = sum_bf16x2(pk, lsum);
+          asm volatile("" : "+v"(pn[q4 >> 1][2 * (q4 & 1) + (e >> 1)]), "+v"(lsum));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pf[0] = pn[0];
+    pf[1] = pn[1];
+  };
   auto step_body = [&](int it, auto masked_c) {
+    if constexpr (D >= 256) {
+      step_written(it, masked_c);
+      wait_vmcnt<0>();            // step it + 2 landed
+      __syncthreads();
+      if (it + 3 < nsteps) issue_step(it + 3, b0);   // buffer of step it, consumed
+      const int t = b0;
+      b0 = b1;
+      b1 = b2;
+      b2 = t;
+      return;
+    }
     constexpr bool MASKED = decltype(masked_c)::value && D <= 128;
     const int kb = (jb0 + it + 1) * C::BN;
     const bool seen = !MASKED || (kb <= qw0 + 31 && kb + C::BN - 1 >= qw0 - W);

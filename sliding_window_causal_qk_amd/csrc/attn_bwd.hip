@@ -678,14 +678,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 //                        dK_hat^T += Q_hat^T dS
 // Each wave holds one accumulator (128 registers) and one operand row set
 // (K for role 0, V for role 1: 64 registers), and issues per step the same
-// 32 products as a wave of the kernel above.  A tile is 64 keys (two pairs of waves).  Role 0
-// hands P to role 1 through LDS in fp32, so dS is formed from the unrounded
-// probabilities as in the kernel above: role 0 writes P of block it + 1 during
-// step it, role 1 reads it after the step's barrier and forms dS of that
-// block beside its next dP products, one step behind role 0 (its dP
-// accumulators alternate between two register sets).  The query-block stream,
-// the tile list and the epilogues are those of the kernel above; the K and V
-// rows go straight to registers at each tile's start.
+// 32 products as a wave of the kernel above.  A tile is 64 keys (two pairs
+// of waves).  Role 0 hands P to role 1 through LDS in fp32, so dS is formed
+// from the unrounded probabilities as in the kernel above: role 0 writes P of
+// block it + 1 during step it, role 1 reads it after the step's barrier and
+// forms dS of that block beside its next dP products, one step behind role 0
+// (it keeps dP of two blocks: the one it forms dS from and the one its
+// products build).  The query-block stream, the tile list and the epilogues
+// are those of the kernel above; the K and V rows go straight to registers at
+// each tile's start.
 template <bool GROUPED, bool ROPE>
 struct DkdvSplitCfg {
   static constexpr int D = 256;

@@ -83,6 +83,9 @@ __device__ __forceinline__ int v_slot(int r, int ch) { return ch ^ (2 * (r & 3))
 // rotated in the prologue.  At D = 256 the three stage buffers take 100 KB of
 // LDS, so one workgroup runs per CU: the kernel is then built for one wave per
 // SIMD, whose 512 registers hold the accumulators and every operand in flight.
+// At D = 128 three workgroups share a CU (52 KB of LDS each), and the launch
+// bounds hold the kernel to the 168 registers that three waves per SIMD allow;
+// at D = 64, four.
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,

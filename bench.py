@@ -60,7 +60,8 @@ METRIC = "attn fwd+bwd effective TFLOP/s & % bf16 MFMA peak, T=2048 H=4 D=128 SS
 # the method's other single-GPU configurations, then the shorter sequences and
 # other window patterns of the pages' tuning space
 EXTRA_WORKLOADS = ("s_layer", "l_layer", "long", "t512_sssl_stack", "t1024_sssl_stack", "l_stack",
-                   "slll_stack", "d256_sssl_stack", "gqa_sssl_stack", "rope_sssl_stack", "ve_sssl_stack")
+                   "slll_stack", "sl_stack", "ssss_stack", "d256_sssl_stack", "d64_sssl_stack", "gqa_sssl_stack",
+                   "rope_sssl_stack", "ve_sssl_stack")
 MAX_POOL = 16                 # host worker processes at most (one GPU's share of the host)
 
 # algorithmic work credited to each kernel, per visible pair (FLOPs = c * D * N_vis)

@@ -530,7 +530,9 @@ def test_single_layer_workloads(torch_dev, name):
                                         ("ve_sssl_stack", 0), ("ve_sssl_stack", 3),
                                         ("d256_sssl_stack", 0), ("d256_sssl_stack", 3),
                                         ("t512_sssl_stack", 0), ("t512_sssl_stack", 7),
-                                        ("t1024_sssl_stack", 0), ("slll_stack", 0), ("l_stack", 0)])
+                                        ("t1024_sssl_stack", 0), ("slll_stack", 0), ("l_stack", 0),
+                                        ("sl_stack", 1), ("ssss_stack", 0), ("ssss_stack", 7),
+                                        ("d64_sssl_stack", 0), ("d64_sssl_stack", 3)])
 def test_stack_and_long_workloads_sampled(torch_dev, name, layer):
     import sliding_window_causal_qk_amd as sw
     wl = workload(name)

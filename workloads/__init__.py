@@ -142,6 +142,12 @@ WORKLOADS: List[Workload] = [
              notes="pattern L: every layer full causal"),
     Workload("slll_stack", B=64, T=2048, H=4, D=128, pattern="SLLL", n_layer=8, seed0=7300,
              notes="pattern SLLL: one sliding-window layer in four"),
+    Workload("sl_stack", B=64, T=2048, H=4, D=128, pattern="SL", n_layer=8, seed0=7400,
+             notes="pattern SL: sliding-window and full-causal layers alternate"),
+    Workload("ssss_stack", B=64, T=2048, H=4, D=128, pattern="SSSS", n_layer=8, seed0=7500,
+             notes="pattern SSSS: sliding window everywhere but the last layer, which is full"),
+    Workload("d64_sssl_stack", B=64, T=2048, H=8, D=64, pattern="SSSL", n_layer=8, seed0=7600,
+             notes="the SSSL stack at head size 64 (same n_embd = 512: 8 heads)"),
 ]
 
 

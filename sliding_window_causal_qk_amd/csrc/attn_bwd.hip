@@ -50,7 +50,8 @@ __device__ __forceinline__ int tr_off(int lane, int P) {
 }
 
 // ------------------------------------------------------------------ dK / dV
-// Persistent: one workgroup per CU walks a list of key tiles of 128 keys.  In
+// Persistent: one workgroup per CU (two at head size 64, whose registers and
+// LDS fit twice) walks a list of key tiles of 128 keys.  In
 // a tile, wave w owns keys j0 + 32 w + c; query blocks of 32 rows (q_hat, dO
 // and their lse, Delta) stream through three LDS buffers filled by
 // direct-to-LDS loads one step ahead, and the stream runs on across tile
@@ -79,7 +80,9 @@ struct DkdvCfg {
   static constexpr int NBUF = 3;
   static constexpr int KS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int P = D + 24;      // q_hat / dO row pitch (bf16): odd multiple of 16 bytes
+  // q_hat / dO row pitch (bf16): an odd multiple of 16 bytes; at D = 64 the
+  // narrower pitch keeps the workgroup within half the LDS
+  static constexpr int P = D + (D <= 64 ? 8 : 24);
   static constexpr int PK = D + 8;      // K / V row pitch in the prefetch region
   using Tile = DmaTileV<BMQ * P / 8, 4, 1 + GROUPED + 2 * ROPE>;
   using KVTile = DmaTileV<BNK * PK / 8, 4, 1 + GROUPED + 2 * ROPE>;
@@ -93,7 +96,7 @@ struct DkdvCfg {
   static constexpr int LDS_BYTES = XO_B + 2 * OUT_SLOT;
   static constexpr int NSTORE = 2 * (32 * D / 8 / 64);    // epilogue stores per lane (dK and dV)
   static_assert(2 * OUT_SLOT <= STAGE, "waves 0 and 1 stage their outputs in a freed step buffer");
-  static_assert(LDS_BYTES <= 160 * 1024, "fits the LDS of one CU");
+  static_assert(LDS_BYTES <= (D <= 64 ? 80 : 160) * 1024, "fits the LDS of one CU (half of it at D = 64)");
   static_assert(D <= 128, "head size 256 takes bwd_dkdv_split_kernel");
 };
 
@@ -103,8 +106,10 @@ struct DkdvCfg {
 // With the value-embedding gate (ve not null), v holds v + gate ve and the
 // epilogue also writes dve = gate dV and dz = (dV . ve) gate (1 - gate / 2),
 // the gradient of the gate's pre-sigmoid input ([B, T, Hkv]).
+// At D = 128 a wave holds its accumulators and K / V rows in 512 registers, one
+// wave per SIMD; at D = 64 they fit in 256, and two workgroups share a CU.
 template <int D, bool GROUPED, bool ROPE>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ qhat, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -378,9 +383,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     stage_b(b0, 0, masked);
 
     // One pipelined step: A(it+1), C(it), B(it+1), then the hand-off of the
-    // buffers.  One wave per SIMD issues in order, so a VALU, scalar or memory
-    // instruction costs nothing only in the shadow of a product it does not
-    // depend on.  Left to itself the compiler issued each LDS read right before
+    // buffers.  At D = 128 one wave per SIMD issues in order, so a VALU,
+    // scalar or memory instruction costs nothing only in the shadow of a
+    // product it does not depend on.  Left to itself the compiler issued each LDS read right before
     // its product and waited for it there, and sank the softmax next to C's
     // products alone; the order is therefore written out in regions fenced with
     // scheduling barriers:
@@ -1248,8 +1253,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_split_kernel(
 //   B(i): dS' = exp2(S^T kscale - lse log2 e) (dP^T - Delta) kscale      (VALU)
 //   C(i): dQ^T += K^T dS'^T   (K^T read transposed from the row-major K tile)
 // As in the dK/dV kernel the loop issues A(i+1), C(i), then B(i+1).  The
-// kernel fits two waves per SIMD, so the hardware also overlaps two
-// workgroups' phases.
+// kernel fits two waves per SIMD (three at D = 64), so the hardware also
+// overlaps several workgroups' phases.
 template <int D, bool ROPE>
 struct DqCfg {
   static constexpr int BM = 128;   // queries per workgroup (32 per wave)
@@ -1269,7 +1274,7 @@ struct DqCfg {
 // ROPE: k holds the rotated keys; the queries are rotated in the prologue and
 // dQ goes back through the transposed rotation in the epilogue.
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse,
@@ -1538,13 +1543,14 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void bwd_dq_kernel(
     b2 = t;
   };
 
-  // steps visible in full to every query of the workgroup: keys kv0 .. kv0 + 31
-  // with kv0 + 31 <= i0 and (i0 + BM - 1) - kv0 <= W (and all inside T)
+  // steps visible in full to every query of this wave: keys kv0 .. kv0 + 31
+  // with kv0 + 31 <= qw0 and (qw0 + 31) - kv0 <= W (and all inside T).  The
+  // ranges differ between the waves, which pass the same number of barriers.
   int full_lo = nsteps, full_hi = -1;
-  if (nsteps > 0 && i0 + C::BM - 1 < T) {
-    const int lo_kv = i0 + C::BM - 1 - W;                  // first key visible to every query
+  if (nsteps > 0 && qw0 + 31 < T) {
+    const int lo_kv = qw0 + 31 - W;                        // first key visible to every query
     full_lo = imax(0, (lo_kv + C::BN - 1) / C::BN - jb0);
-    full_hi = (i0 - (C::BN - 1)) >= 0 ? (i0 - (C::BN - 1)) / C::BN - jb0 : -1;
+    full_hi = (qw0 - (C::BN - 1)) >= 0 ? (qw0 - (C::BN - 1)) / C::BN - jb0 : -1;
     full_hi = imin(full_hi, nsteps - 1);
   }
   const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // body it prepares B(it + 1)
@@ -1791,7 +1797,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
       if (attr != hipSuccess) return attr;
       const int nkt = (a.T + C::BNK - 1) / C::BNK;
       const int ntiles = nkt * a.B * a.Hkv;
-      const int grid = imin(ncu, ntiles);   // persistent: one workgroup per CU
+      const int grid = imin(D <= 64 ? 2 * ncu : ncu, ntiles);   // persistent: workgroups per CU as fit
       ProfToken t1 = prof_begin(K_BWD_DKDV, stream);
       hipLaunchKernelGGL((G == 1 ? bwd_dkdv_kernel<D, false, ROPE> : bwd_dkdv_kernel<D, true, ROPE>),
                          dim3(grid), dim3(256), C::LDS_BYTES, stream,

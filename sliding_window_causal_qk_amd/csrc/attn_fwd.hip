@@ -37,7 +37,8 @@
 //  * Loads go through buffer descriptors rebased per tile: rows past T read as
 //    zero, so ragged tails need no branches; stores past T are dropped.
 //  * Band-aware tile loop: a query tile visits only the key blocks that
-//    intersect its window; fully visible blocks skip the mask.
+//    intersect its window; a block visible in full to a wave's 32 queries
+//    skips the mask in that wave.
 #include <type_traits>
 
 #include "common.h"
@@ -352,13 +353,14 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
     b2 = t;
   };
 
-  // steps visible in full to every query of the workgroup: keys kv0 .. kv0 + 31
-  // with kv0 + 31 <= i0 and (i0 + BM - 1) - kv0 <= W (and all inside T)
+  // steps visible in full to every query of this wave: keys kv0 .. kv0 + 31
+  // with kv0 + 31 <= qw0 and (qw0 + 31) - kv0 <= W (and all inside T).  The
+  // ranges differ between the waves, which pass the same number of barriers.
   int full_lo = nsteps, full_hi = -1;
-  if (nsteps > 0 && i0 + C::BM - 1 < T) {
-    const int lo_kv = i0 + C::BM - 1 - W;                  // first key visible to every query
+  if (nsteps > 0 && qw0 + 31 < T) {
+    const int lo_kv = qw0 + 31 - W;                        // first key visible to every query
     full_lo = imax(0, (lo_kv + C::BN - 1) / C::BN - jb0);
-    full_hi = (i0 - (C::BN - 1)) >= 0 ? (i0 - (C::BN - 1)) / C::BN - jb0 : -1;
+    full_hi = (qw0 - (C::BN - 1)) >= 0 ? (qw0 - (C::BN - 1)) / C::BN - jb0 : -1;
     full_hi = imin(full_hi, nsteps - 1);
   }
   const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // body it prepares B(it + 1)

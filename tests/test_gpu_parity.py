@@ -228,20 +228,21 @@ def test_gqa_autograd(torch_dev):
 
 
 # The persistent dK/dV kernel runs one workgroup per compute unit (256 on
-# MI355X) over B * H_kv * ceil(T / 128) key tiles.  These cases have more
-# tiles than that, so workgroups run two or more tiles in a row: the stream of
+# MI355X; two per unit at D = 64) over B * H_kv * ceil(T / BNK) key tiles
+# (BNK = 128 keys, 64 at D = 256).  These cases have more tiles than
+# workgroups, so some workgroups run two or more tiles in a row: the stream of
 # query blocks that carries on across tiles and the prefetch of the next
 # tile's K and V rows are compared element by element.
 MULTI_TILE = [
     # (B, T, H, H_kv, D, W, rope, gate C or 0, reuse, seed)
-    (8, 1024, 8, 8, 64, 512, False, 0, True, 7001),
+    (16, 768, 8, 8, 64, 300, False, 0, True, 7001),
     (8, 1024, 8, 8, 128, 300, False, 0, True, 7002),
     (8, 1024, 8, 8, 256, 400, False, 0, True, 7003),
     (9, 1000, 8, 4, 128, 333, False, 0, True, 7004),     # grouped heads, ragged T
     (9, 1000, 8, 4, 128, -1, True, 0, True, 7005),       # rotary embedding, full causal
     (9, 1000, 8, 4, 128, 200, False, 64, True, 7006),    # value-embedding gate
     (3, 1100, 11, 11, 128, 129, False, 0, False, 7007),  # tile count not a multiple of 8
-    (8, 1024, 8, 8, 64, 0, False, 0, False, 7008),
+    (16, 768, 8, 8, 64, 0, False, 0, False, 7008),
 ]
 N_CU = 256
 
@@ -251,7 +252,8 @@ N_CU = 256
                               for c in MULTI_TILE])
 def test_multi_tile_full_parity(torch_dev, B, T, H, H_kv, D, W, rope, C, reuse, seed):
     torch = torch_dev
-    assert B * H_kv * -(-T // 128) > N_CU, "the case must give some workgroup a second key tile"
+    bnk, grid = (64 if D == 256 else 128), N_CU * (2 if D <= 64 else 1)
+    assert B * H_kv * -(-T // bnk) > grid, "the case must give some workgroup a second key tile"
     assert torch.cuda.get_device_properties(0).multi_processor_count <= N_CU
     _say(f"[parity] multi-tile B={B} T={T} H={H} H_kv={H_kv} D={D} W={W} rope={rope} C={C} seed={seed}")
     inp = make_layer_inputs(B, T, H, D, seed, H_kv=H_kv)

@@ -1555,15 +1555,42 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
   }
   const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // body it prepares B(it + 1)
   const int nloop = nsteps - 1;
+  // At D <= 128 (two or three waves per SIMD) a wave passes over the blocks
+  // none of its queries sees (keys after its last query, or before its first
+  // query's window) with only the step's wait, barrier and loads, and the
+  // other waves on the SIMD take the issue slots.  Blocks sv_lo .. sv_hi may
+  // be seen.  A skipped step has blocks it and it + 1 both unseen: the dS of
+  // an unseen block is zero (its P is masked), so C adds nothing for it.  The
+  // steps on either side of the skipped runs take the masked body, whose C or
+  // A and B then work on an unseen block and add zeros.
+  int sv_lo = 0, sv_hi = nsteps - 1;
+  if constexpr (D <= 128) {
+    const int lo = qw0 - W - (C::BN - 1);           // a block starting below lo is unseen
+    sv_lo = imax(0, (lo > 0 ? (lo + C::BN - 1) / C::BN : 0) - jb0);
+    sv_hi = imin(nsteps - 1, (qw0 + 31) / C::BN - jb0);
+  }
+  const int h_end = imin(imax(sv_lo - 1, 0), imax(nloop, 0));   // steps [0, h_end) skipped
+  const int t_beg = imax(imin(sv_hi + 1, nloop), h_end);        // steps [t_beg, nloop) skipped
+  auto skip_step = [&](int it) {
+    wait_vmcnt<0>();            // step it + 2 landed
+    __syncthreads();
+    if (it + 3 < nsteps) issue_step(it + 3, b0);   // buffer of step it, consumed
+    const int t = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = t;
+  };
   int it = 0;
-  for (; it < imin(u0, nloop); ++it) step_body(it, masked);
-  for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
-  for (; it < nloop; ++it) step_body(it, masked);
+  for (; it < h_end; ++it) skip_step(it);
+  for (; it < imin(u0, t_beg); ++it) step_body(it, masked);
+  for (; it <= u1 && it < t_beg; ++it) step_body(it, unmasked);
+  for (; it < t_beg; ++it) step_body(it, masked);
+  for (; it < nloop; ++it) skip_step(it);
   // the raw q rows for the epilogue's RMSNorm backward, in flight with the
   // last block's products
   u32x4 qrow[RS::NCHUNK];
   RS::load_regs(qrow, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
-  if (nsteps > 0) stage_c(b0);
+  if (nsteps > 0 && nsteps - 1 <= sv_hi) stage_c(b0);
 
   // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past
   // T dropped).  The raw q rows come in and dq goes out through LDS (the step

@@ -243,6 +243,8 @@ MULTI_TILE = [
     (9, 1000, 8, 4, 128, 200, False, 64, True, 7006),    # value-embedding gate
     (3, 1100, 11, 11, 128, 129, False, 0, False, 7007),  # tile count not a multiple of 8
     (16, 768, 8, 8, 64, 0, False, 0, False, 7008),
+    (24, 768, 8, 4, 64, 200, False, 0, True, 7009),      # D = 64 (two workgroups per CU), grouped heads
+    (28, 640, 4, 4, 64, 150, True, 64, True, 7010),      # D = 64, rotary embedding and gate
 ]
 N_CU = 256
 

@@ -85,6 +85,11 @@ __global__ __launch_bounds__(256) void key_prep_kernel(const uint16_t* __restric
       bstore16(kv[i], rkr, ((threadIdx.x / LPR + RPB * i) * D + part * 8) * 2);
     }
   }
+  // The block's RPB * KR scales go out through LDS, one row per thread of its
+  // first RPB * KR threads: the rows of one key/value head are consecutive
+  // positions, so a wave's stores form runs of neighbouring words instead of
+  // one isolated word per row.
+  __shared__ float ks[RPB * KR];
 #pragma unroll
   for (int i = 0; i < KR; ++i) {
     float ss = 0.f;
@@ -95,11 +100,13 @@ __global__ __launch_bounds__(256) void key_prep_kernel(const uint16_t* __restric
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, LPR);
-    const int row = row0 + RPB * i;
-    if (row < nrows && part == 0) {
-      const int h = row % H, bt = row / H, t = bt % T, b = bt / T;
-      kscale[((size_t)b * H + h) * T + t] = (1.0f / sqrtf(ss * (1.0f / D) + eps)) * (kLog2e / sqrtf((float)D));
-    }
+    if (part == 0) ks[threadIdx.x / LPR + RPB * i] = (1.0f / sqrtf(ss * (1.0f / D) + eps)) * (kLog2e / sqrtf((float)D));
+  }
+  __syncthreads();
+  const int row = rb + threadIdx.x;
+  if (threadIdx.x < RPB * KR && row < nrows) {
+    const int h = row % H, bt = row / H, t = bt % T, b = bt / T;
+    kscale[((size_t)b * H + h) * T + t] = ks[threadIdx.x];
   }
 }
 

@@ -1364,6 +1364,16 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
   kv_range(i0, i0 + C::BM - 1, T, W, &kv_lo, &kv_hi);
   const int jb0 = kv_lo / C::BN;
   const int nsteps = kv_hi / C::BN - jb0 + 1;
+  // Step i visits key block blk(i) = jb0 + ((i - jb0) mod nsteps): the band
+  // rotated so that the query tiles of one (batch, head) whose bands have the
+  // same length, which run at the same time, read the same key block at
+  // about the same time (most reads then hit in L2).  dQ sums over the blocks
+  // in that order.
+  const int rot = nsteps > 0 ? (nsteps - jb0 % nsteps) % nsteps : 0;
+  auto blk = [&](int i) {   // 0 <= i < nsteps
+    const int x = i + rot;
+    return jb0 + (x >= nsteps ? x - nsteps : x);
+  };
 
   // ---- direct-to-LDS staging of one key step
   typename C::Tile tile;
@@ -1374,7 +1384,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
   // remaining bytes of the key slices from row r0 on, below 2^32 (unsigned arithmetic)
   const uint32_t kbytes_u = (uint32_t)kslice_bytes, krow_u = (uint32_t)rsb_kv;
   auto issue_step = [&](int step, int base) {
-    const int r0 = (jb0 + step) * C::BN;
+    const int r0 = blk(step) * C::BN;
     const uint32_t nb = kbytes_u - (uint32_t)r0 * krow_u;
     tile.issue(make_desc_u(k_s + (size_t)r0 * rs_kv, nb), smem, base, w);
     tile.issue(make_desc_u(v_s + (size_t)r0 * rs_kv, nb), smem, base + C::V_B, w);
@@ -1402,7 +1412,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
   auto stage_b = [&](int base, int step, auto masked_c) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const int vk = base + k_off;
-    const int t0 = (jb0 + step) * C::BN + 4 * g + W - qi;  // kv visible iff 0 <= kv - (qi - W) <= W
+    const int t0 = blk(step) * C::BN + 4 * g + W - qi;  // kv visible iff 0 <= kv - (qi - W) <= W
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const f32x4 k4 = lds16f(smem, vk + 32 * q4);
@@ -1490,7 +1500,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
       }
       // B(it+1) element r (register r: key j0 + 8 (r / 4) + 4 g + r % 4, query
       // qi), as stage_b computes it, each value pinned where it is made
-      const int t0 = (jb0 + it + 1) * C::BN + 4 * g + W - qi;
+      const int t0 = blk(it + 1) * C::BN + 4 * g + W - qi;
       float pe[16], de[16];
       auto p_elem = [&](int r) {
         const int q4 = r >> 2, i = r & 3;
@@ -1553,7 +1563,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
     full_hi = (qw0 - (C::BN - 1)) >= 0 ? (qw0 - (C::BN - 1)) / C::BN - jb0 : -1;
     full_hi = imin(full_hi, nsteps - 1);
   }
-  const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // body it prepares B(it + 1)
   const int nloop = nsteps - 1;
   // At D <= 128 (two or three waves per SIMD) a wave passes over the blocks
   // none of its queries sees (keys after its last query, or before its first
@@ -1569,8 +1578,6 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
     sv_lo = imax(0, (lo > 0 ? (lo + C::BN - 1) / C::BN : 0) - jb0);
     sv_hi = imin(nsteps - 1, (qw0 + 31) / C::BN - jb0);
   }
-  const int h_end = imin(imax(sv_lo - 1, 0), imax(nloop, 0));   // steps [0, h_end) skipped
-  const int t_beg = imax(imin(sv_hi + 1, nloop), h_end);        // steps [t_beg, nloop) skipped
   auto skip_step = [&](int it) {
     wait_vmcnt<0>();            // step it + 2 landed
     __syncthreads();
@@ -1580,17 +1587,31 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
     b1 = b2;
     b2 = t;
   };
-  int it = 0;
-  for (; it < h_end; ++it) skip_step(it);
-  for (; it < imin(u0, t_beg); ++it) step_body(it, masked);
-  for (; it <= u1 && it < t_beg; ++it) step_body(it, unmasked);
-  for (; it < t_beg; ++it) step_body(it, masked);
-  for (; it < nloop; ++it) skip_step(it);
+  // Body it works on A and B of block b = blk(it + 1) - jb0 (relative) and C
+  // of the block before it.  In band order (b rising) the bodies run: skipped
+  // while b < sv_lo, masked while b < full_lo, unmasked up to full_hi, masked
+  // up to sv_hi + 1 (C of block sv_hi), skipped after.  The rotation splits
+  // the steps into two such runs: b = rot + 1 .. nsteps - 1, then b = 0 ..
+  // rot - 1, whose first step (b = 0) takes C of block nsteps - 1 and runs
+  // masked unless that block is unseen too.
+  for (int pass = 0; pass < 2; ++pass) {
+    const int b_lo = pass == 0 ? rot + 1 : 0, b_hi = pass == 0 ? nsteps - 1 : rot - 1;
+    const int off = pass == 0 ? -rot : nsteps - rot;   // it = b - 1 + off
+    const int w0 = (pass == 1 && sv_hi >= nsteps - 1) ? 1 : 0;
+    const int it_end = b_hi + off;
+    int it = b_lo - 1 + off;
+    for (; it < imin(b_lo - 1 + off + w0, it_end); ++it) step_body(it, masked);
+    for (; it < imin(sv_lo - 1 + off, it_end); ++it) skip_step(it);
+    for (; it < imin(full_lo - 1 + off, it_end); ++it) step_body(it, masked);
+    for (; it < imin(full_hi + off, it_end); ++it) step_body(it, unmasked);
+    for (; it < imin(sv_hi + 1 + off, it_end); ++it) step_body(it, masked);
+    for (; it < it_end; ++it) skip_step(it);
+  }
   // the raw q rows for the epilogue's RMSNorm backward, in flight with the
   // last block's products
   u32x4 qrow[RS::NCHUNK];
   RS::load_regs(qrow, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
-  if (nsteps > 0 && nsteps - 1 <= sv_hi) stage_c(b0);
+  if (nsteps > 0 && blk(nsteps - 1) - jb0 >= sv_lo && blk(nsteps - 1) - jb0 <= sv_hi) stage_c(b0);
 
   // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past
   // T dropped).  The raw q rows come in and dq goes out through LDS (the step

@@ -137,6 +137,17 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
   kv_range(i0, i0 + C::BM - 1, T, W, &kv_lo, &kv_hi);
   const int jb0 = kv_lo / C::BN;
   const int nsteps = kv_hi / C::BN - jb0 + 1;
+  // Step i visits key block blk(i) = jb0 + ((i - jb0) mod nsteps): the band
+  // rotated so that every query tile whose band has the same length visits
+  // block j at step j mod nsteps.  The tiles of one (batch, head) run at the
+  // same time, and with the rotation they read the same key block at about
+  // the same time, so most of their reads hit in L2.  (The softmax shift is
+  // fixed, so the order of the blocks changes nothing but rounding.)
+  const int rot = nsteps > 0 ? (nsteps - jb0 % nsteps) % nsteps : 0;
+  auto blk = [&](int i) {   // 0 <= i < nsteps
+    const int x = i + rot;
+    return jb0 + (x >= nsteps ? x - nsteps : x);
+  };
 
   // ---- direct-to-LDS staging of one key step
   typename C::KTile ktile;
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
   // remaining bytes of the slices from key j0 on, below 2^32 (unsigned arithmetic)
   const uint32_t kbytes_u = (uint32_t)kslice_bytes, krow_u = (uint32_t)rsb_kv;
   auto issue_step = [&](int step, int base) {
-    const int j0 = (jb0 + step) * C::BN;
+    const int j0 = blk(step) * C::BN;
     const uint32_t nb = kbytes_u - (uint32_t)j0 * krow_u;
     ktile.issue(make_desc_u(k_s + (size_t)j0 * rs_kv, nb), smem, base, w);
     vtile.issue(make_desc_u(v_s + (size_t)j0 * rs_kv, nb), smem, base + C::V_B, w);
@@ -191,7 +202,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
   auto stage_b = [&](int base, int step, auto masked_c) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const int vk = base + k_off;
-    const int t0 = (jb0 + step) * C::BN + 4 * g + W - qi;  // key kv visible iff 0 <= kv - (qi - W) <= W
+    const int t0 = blk(step) * C::BN + 4 * g + W - qi;  // key kv visible iff 0 <= kv - (qi - W) <= W
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const f32x4 k4 = lds16f(smem, vk + 32 * q4);
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int t0 = (jb0 + it + 1) * C::BN + 4 * g + W - qi;   // key kv visible iff 0 <= kv - (qi - W) <= W
+    const int t0 = blk(it + 1) * C::BN + 4 * g + W - qi;   // key kv visible iff 0 <= kv - (qi - W) <= W
     float pe[16];
     u32x4 pn[2];
 #pragma unroll
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
       return;
     }
     constexpr bool MASKED = decltype(masked_c)::value && D <= 128;
-    const int kb = (jb0 + it + 1) * C::BN;
+    const int kb = blk(it + 1) * C::BN;
     const bool seen = !MASKED || (kb <= qw0 + 31 && kb + C::BN - 1 >= qw0 - W);
     if (seen) {
       stage_a(b1);
@@ -363,11 +374,24 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
     full_hi = (qw0 - (C::BN - 1)) >= 0 ? (qw0 - (C::BN - 1)) / C::BN - jb0 : -1;
     full_hi = imin(full_hi, nsteps - 1);
   }
-  const int u0 = imax(full_lo - 1, 0), u1 = full_hi - 1;   // body it prepares B(it + 1)
+  // Body it prepares B(it + 1), unmasked iff block blk(it + 1) lies in that
+  // range.  With the rotation those bodies form at most two runs: j = it + 1
+  // in [full_lo - rot, full_hi - rot] (the part at or above 1) and the same
+  // range moved up by nsteps (the part below nsteps).
   const int nloop = nsteps - 1;
+  int ua0 = nloop, ua1 = nloop - 1, ub0 = nloop, ub1 = nloop - 1;
+  if (full_lo <= full_hi) {
+    const int a0 = full_lo - rot, a1 = full_hi - rot;
+    ua0 = imax(a0, 1) - 1;
+    ua1 = imin(a1, nsteps - 1) - 1;
+    ub0 = imax(a0 + nsteps, 1) - 1;
+    ub1 = imin(a1 + nsteps, nsteps - 1) - 1;
+  }
   int it = 0;
-  for (; it < imin(u0, nloop); ++it) step_body(it, masked);
-  for (; it <= u1 && it < nloop; ++it) step_body(it, unmasked);
+  for (; it < imin(ua0, nloop); ++it) step_body(it, masked);
+  for (; it <= ua1 && it < nloop; ++it) step_body(it, unmasked);
+  for (; it < imin(ub0, nloop); ++it) step_body(it, masked);
+  for (; it <= ub1 && it < nloop; ++it) step_body(it, unmasked);
   for (; it < nloop; ++it) step_body(it, masked);
   if (nsteps > 0 && !c_zero) stage_c(b0);
 

@@ -1607,19 +1607,17 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
     for (; it < imin(sv_hi + 1 + off, it_end); ++it) step_body(it, masked);
     for (; it < it_end; ++it) skip_step(it);
   }
-  // the raw q rows for the epilogue's RMSNorm backward, in flight with the
-  // last block's products
-  u32x4 qrow[RS::NCHUNK];
-  RS::load_regs(qrow, make_rsrc(q + sbase + (size_t)qw0 * rs, slice_bytes - qw0 * rsb), rs, lane);
   if (nsteps > 0 && blk(nsteps - 1) - jb0 >= sv_lo && blk(nsteps - 1) - jb0 <= sv_hi) stage_c(b0);
 
   // ---- epilogue: dq_hat = acc / log2(e); RMSNorm backward of q (stores past
-  // T dropped).  The raw q rows come in and dq goes out through LDS (the step
-  // buffers, free once every wave is past its last product), so global memory
-  // sees whole rows.
+  // T dropped).  The norm's output x_hat is the bf16 q_hat that fed the S
+  // products (qf); it moves from the fragment layout (d = 16 ks + 8 g + j) to
+  // the accumulators' (d = 32 n + 8 q4 + 4 g + e) through the wave's LDS slot,
+  // and dq goes out through the same slot (the step buffers, free once every
+  // wave is past its last product), so global memory sees whole rows.
   const float r = r_q;
   // rotary tables of query qi (channels 32 n + 8 q4 + 4 g + e, n < NB / 2,
-  // pair with n + NB / 2), in flight with the reload of the q rows
+  // pair with n + NB / 2), in flight with the last products
   u32x2 tc[C::NB / 2][4], tsn[C::NB / 2][4];
   if constexpr (ROPE) {
     const long long tb = (long long)(T - qw0) * D;
@@ -1636,25 +1634,24 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
   }
   __syncthreads();
   const int slot = RS::BYTES * w;
-  RS::put_regs(smem, slot, qrow, lane);
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    RS::put(smem, slot, c, 16 * ks + 8 * g, u32x2{qf[ks][0], qf[ks][1]});
+    RS::put(smem, slot, c, 16 * ks + 8 * g + 4, u32x2{qf[ks][2], qf[ks][3]});
+  }
   float dot = 0.f;
   f32x16 xh[C::NB];
   if constexpr (ROPE) {
-    // the norm's input is the rotated q; the table entries serve the way back too
+    // the norm's input is the rotated q (x_hat is its normalised form); the
+    // table entries take the gradient back through the rotation
 #pragma unroll
-    for (int n = 0; n < C::NB / 2; ++n)
+    for (int n = 0; n < C::NB; ++n)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const u32x2 q1 = RS::get(smem, slot, c, 32 * n + 8 * q4 + 4 * g);
-        const u32x2 q2 = RS::get(smem, slot, c, 32 * (n + C::NB / 2) + 8 * q4 + 4 * g);
-        float x1[4] = {bf_lo(q1[0]), bf_hi(q1[0]), bf_lo(q1[1]), bf_hi(q1[1])};
-        float x2[4] = {bf_lo(q2[0]), bf_hi(q2[0]), bf_lo(q2[1]), bf_hi(q2[1])};
-        rope4(x1, x2, tc[n][q4], tsn[n][q4]);
+        const u32x2 qq = RS::get(smem, slot, c, 32 * n + 8 * q4 + 4 * g);
+        const float x[4] = {bf_lo(qq[0]), bf_hi(qq[0]), bf_lo(qq[1]), bf_hi(qq[1])};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xh[n][4 * q4 + e] = x1[e] * r;
-          xh[n + C::NB / 2][4 * q4 + e] = x2[e] * r;
-        }
+        for (int e = 0; e < 4; ++e) xh[n][4 * q4 + e] = x[e];
       }
 #pragma unroll
     for (int n = 0; n < C::NB; ++n)
@@ -1689,7 +1686,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
       const float x[4] = {bf_lo(qq[0]), bf_hi(qq[0]), bf_lo(qq[1]), bf_hi(qq[1])};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        xh[n][4 * q4 + e] = x[e] * r;
+        xh[n][4 * q4 + e] = x[e];
         acc[n][4 * q4 + e] *= (1.0f / kLog2e);
         dot += acc[n][4 * q4 + e] * xh[n][4 * q4 + e];
       }

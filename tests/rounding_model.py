@@ -24,7 +24,8 @@ rounding points are the kernels' documented ones:
              in fp32; dV += bf16(P)^T dO; dS = P (dP - Delta) rounded to bf16
              for dK_hat += dS^T q_hat; dQ takes bf16(P (dP - Delta) kscale) times
              the raw K; the RMSNorm backward of q and k runs in fp32 on the
-             fp32 accumulators and is rounded to bf16 once
+             fp32 accumulators and is rounded to bf16 once; for q its x_hat is
+             the bf16 q_hat of the products, for k the raw K times r_k
   rotary:    the rotated keys are stored in bf16 (the K of the products); the
              rotated queries go to the norm unrounded; the gradients are
              rotated back in fp32
@@ -162,7 +163,7 @@ def backward(q, k, v, o, lse, do, window: int, eps: float = 1e-6, cos=None, sin=
             acc_dv[b, :, hk] += bf16(p).T @ do[b, :, h]
             acc_dk[b, :, hk] += bf16(p * dpd).T @ qh[b, :, h]
             dqh = (bf16(p * dpd * ksc[b, :, hk][None, :]) @ kk[b, :, hk]) * (F32(1.0) / LOG2E)
-            xh = qx[b, :, h] * rq[b, :, h][:, None]
+            xh = qh[b, :, h]   # the bf16 q_hat of the products is the norm's output
             mean = np.sum(dqh * xh, axis=1, dtype=np.float32) * F32(1.0 / D)
             y = rq[b, :, h][:, None] * (dqh - xh * mean[:, None])
             if cos is not None:

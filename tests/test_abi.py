@@ -193,7 +193,9 @@ def test_reuse_partial_overlap_rejected(kind):
 
 
 @pytest.mark.parametrize("kw", [dict(D=96), dict(D=512), dict(D=32), dict(causal=0),
-                                dict(B=1 << 12, T=1 << 12, H=8, D=128)])
+                                dict(B=1 << 12, T=1 << 12, H=8, D=128),
+                                dict(B=1, T=1 << 24, H=1, D=128),     # 2^31 elements: one past the largest
+                                dict(B=1, T=1 << 23, H=1, D=256)])
 def test_unsupported(kw):
     assert _fwd(**kw) == _lib.ATTN_ERR_UNSUPPORTED
     assert _bwd(**kw) == _lib.ATTN_ERR_UNSUPPORTED

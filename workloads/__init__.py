@@ -185,7 +185,8 @@ def make_layer_inputs_device(B: int, T: int, H: int, D: int, seed: int,
     """Same recipe drawn on the GPU (torch's Philox stream, not numpy's): N(0, sigma^2)
     in fp32, rounded to bf16 (round to nearest even), Q, K, V then dO from one
     generator seeded with `seed`.  For timing runs, where only the distribution
-    matters; the parity tests use make_layer_inputs, which the oracle also reads."""
+    matters, and for problems too large to draw on the host; the other parity
+    tests use make_layer_inputs, which the oracle also reads."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(seed)

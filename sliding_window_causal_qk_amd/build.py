@@ -34,6 +34,13 @@ def flags(extra=()):
     ]
 
 
+# per-source compiler options: the backward kernels are scheduled with the
+# ILP-maximising machine scheduler (measured: dQ 1-2.5% faster; dK/dV, whose
+# step order is fenced with scheduling barriers, unchanged), the forward with
+# the default one (1-4% slower under max-ilp)
+PER_SOURCE = {"attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -59,7 +66,8 @@ def build(verbose: bool = False, csrc: str | None = None, out: str | None = None
         objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
         jobs = min(len(srcs), os.cpu_count() or 1, 16)
         with ThreadPoolExecutor(jobs) as ex:
-            list(ex.map(lambda so: _run([hipcc(), *flags(), "-c", so[0], "-o", so[1]], verbose),
+            list(ex.map(lambda so: _run([hipcc(), *flags(PER_SOURCE.get(os.path.basename(so[0]), ())),
+                                         "-c", so[0], "-o", so[1]], verbose),
                         zip(srcs, objs)))
         tmp = out + ".tmp"
         _run([hipcc(), *flags(), "-shared", *objs, "-o", tmp], verbose)

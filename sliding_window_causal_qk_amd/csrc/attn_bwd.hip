@@ -1280,14 +1280,15 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
     const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ kscale, const uint16_t* __restrict__ rcos,
     const uint16_t* __restrict__ rsin, uint16_t* __restrict__ qhat, float* __restrict__ delta,
-    float* __restrict__ lse2, uint16_t* __restrict__ dq, int T, int H, int G, int W, float eps) {
+    float* __restrict__ lse2, uint16_t* __restrict__ dq, int T, int H, int G, int W, float eps,
+    int tile_group) {
   using C = DqCfg<D, ROPE>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int nqt = (T + C::BM - 1) / C::BM;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, qt;
-  query_tile_of(lid, nqt, gridDim.x / nqt, kTileGroupDq, &bh, &qt);
+  query_tile_of(lid, nqt, gridDim.x / nqt, tile_group, &bh, &qt);
   const int b = bh / H, h = bh % H;
   const int i0 = qt * C::BM;
 
@@ -1814,6 +1815,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     if (ep != hipSuccess) return ep;
   }
   const int W = eff_window(a.T, a.window);
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+    return hipErrorInvalidDevice;
   {
     // dQ first: it also writes q_hat, Delta and lse log2(e) for dK/dV
     using C = DqCfg<D, ROPE>;
@@ -1822,19 +1827,19 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int nqt = (a.T + C::BM - 1) / C::BM;
+    // slices per group of the heaviest-first order: wider when the grid fills
+    // the CUs' workgroup slots only a few times over
+    const long long slots = (long long)ncu * (D >= 256 ? 1 : (D <= 64 ? 3 : 2));
+    const int tile_group = (long long)nqt * a.B * a.H <= kDqFewWaves * slots ? kTileGroupDqFew : kTileGroupDq;
     ProfToken t2 = prof_begin(K_BWD_DQ, stream);
     hipLaunchKernelGGL((bwd_dq_kernel<D, ROPE>), dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.o, kk, vv,
                        (const uint16_t*)a.dout, a.lse, (const float*)a.kscale,
                        (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.qhat, a.delta,
-                       a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps);
+                       a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps, tile_group);
     prof_end(t2);
   }
   {
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
-      return hipErrorInvalidDevice;
     if constexpr (D <= 128) {
       using C = DkdvCfg<D, false, ROPE>;
       static_assert(C::LDS_BYTES == DkdvCfg<D, true, ROPE>::LDS_BYTES, "one LDS size for both versions");

@@ -67,9 +67,14 @@ struct BwdArgs {
 };
 
 // (batch, head) slices per group of the query-tiled kernels' heaviest-first
-// order (see query_tile_of); measured best on the SSSL stack's layers
+// order (see query_tile_of); measured best on the SSSL stack's layers.  dQ
+// takes wider groups when its grid is at most kDqFewWaves times the
+// workgroups the CUs hold at once: measured faster on the B = 8 layers (by
+// 16% at W = 2048) and on the T = 8192 stack, slower (2%) at eight times.
 constexpr int kTileGroupFwd = 4;
 constexpr int kTileGroupDq = 2;
+constexpr int kTileGroupDqFew = 4;
+constexpr int kDqFewWaves = 4;
 
 // tokens per block of the first pass of the gate's weight-gradient reduction
 constexpr int kGateTokens = 64;

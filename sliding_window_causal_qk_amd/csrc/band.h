@@ -62,4 +62,32 @@ SW_HD int tile_class(int q_lo, int q_hi, int kv_lo, int kv_hi, int T, int W) {
   return TILE_PARTIAL;
 }
 
+// Schedule of the persistent dK/dV kernels.  The n8 key tiles of one XCD's
+// range (consecutive tiles of its (batch, head) slices, nkt per slice) go to
+// its g8 workgroups in rounds of g8 consecutive tiles; in round i workgroup s
+// takes tile i g8 + x, or none past the range (-1).  x = (s + 7 i) mod g8
+// rotates the light tiles of the causal tail through the workgroups: when the
+// number of rounds R is a multiple of nkt (and nkt divides g8), every
+// workgroup meets every tile position of a slice equally often.  Otherwise,
+// with R even, round i >= R / 2 takes the mirror g8 - 1 - x of round i - R / 2:
+// mirrored positions of a causal band have band lengths that sum to about a
+// constant, so each workgroup's pairs of rounds carry about equal work.
+// mirror_from() is the first mirrored round (the number of rounds when none
+// is); it divides, so a kernel computes it once.
+SW_HD int mirror_from(int g8, int n8, int nkt) {
+  const int rounds = (n8 + g8 - 1) / g8;
+  return ((rounds & 1) == 0 && rounds % nkt != 0) ? rounds / 2 : rounds;
+}
+SW_HD int schedule_tile(int i, int s, int g8, int n8, int half) {
+  if (i * g8 >= n8) return -1;
+  const bool m = i >= half;
+  const int x0 = (s + 7 * (m ? i - half : i)) % g8;
+  const int r = i * g8 + (m ? g8 - 1 - x0 : x0);
+  return r < n8 ? r : -1;
+}
+
+SW_HD int persistent_tile(int i, int s, int g8, int n8, int nkt) {
+  return schedule_tile(i, s, g8, n8, mirror_from(g8, n8, nkt));
+}
+
 }  // namespace swattn

@@ -417,4 +417,14 @@ __device__ __forceinline__ float normalise_query(u32x4* qf, const uint16_t* rcos
   return r;
 }
 
+// A-operand of a 32x32x16 MFMA whose k index runs along the rows of a row-major
+// LDS tile (two transposing reads): lane (g, c) gets column col0 + c of rows
+// row0 + 4 g + {0,1,2,3} and row0 + 8 + 4 g + {0,1,2,3}, i.e. element j is row
+// row0 + 4 g + (j % 4) + 8 (j / 4) -- the k order of probabilities held in the
+// C layout of a previous product.  `off` is the per-lane part from tr_off().
+__device__ __forceinline__ int tr_off(int lane, int P) {
+  const int li = lane & 15, g = lane >> 5;
+  return (4 * g + (li >> 2)) * P + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+}
+
 }  // namespace swattn

@@ -102,5 +102,10 @@ struct KeyPrepArgs {
 hipError_t launch_key_prep(const KeyPrepArgs& a, int prof_kernel, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// The dQ kernel of the backward (attn_bwd_dq.hip), launched by launch_bwd
+// first: kk, vv are the keys and values the products read (rotated keys, gated
+// values), W the window as eff_window gives it, ncu the device's CU count.
+hipError_t launch_bwd_dq(const BwdArgs& a, const uint16_t* kk, const uint16_t* vv, int W, int ncu,
+                         hipStream_t stream);
 
 }  // namespace swattn

@@ -51,12 +51,12 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D <= 64 ? 3 : 2)) void bwd_dq_
     const float* __restrict__ kscale, const uint16_t* __restrict__ rcos,
     const uint16_t* __restrict__ rsin, uint16_t* __restrict__ qhat, float* __restrict__ delta,
     float* __restrict__ lse2, uint16_t* __restrict__ dq, int T, int H, int G, int W, float eps,
-    int tile_group) {
+    int tile_group, int cpx) {
   using C = DqCfg<D, ROPE>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int nqt = (T + C::BM - 1) / C::BM;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int lid = xcd_remap_paired(blockIdx.x, gridDim.x, cpx);
   int bh, qt;
   query_tile_of(lid, nqt, gridDim.x / nqt, tile_group, &bh, &qt);
   const int b = bh / H, h = bh % H;
@@ -491,13 +491,16 @@ static hipError_t launch_bwd_dq_d(const BwdArgs& a, const uint16_t* kk, const ui
   // slices per group of the heaviest-first order: wider when the grid fills
   // the CUs' workgroup slots only a few times over
   const long long slots = (long long)ncu * (D >= 256 ? 1 : (D <= 64 ? 3 : 2));
-  const int tile_group = (long long)nqt * a.B * a.H <= kDqFewWaves * slots ? kTileGroupDqFew : kTileGroupDq;
+  const long long nblk = (long long)nqt * a.B * a.H;
+  const int tile_group = nblk <= kDqFewWaves * slots ? kTileGroupDqFew : kTileGroupDq;
+  // a grid that the CUs hold at once pairs heavy with light tiles per CU
+  const int cpx = (nblk <= slots && ncu % 8 == 0) ? ncu / 8 : 0;
   ProfToken t2 = prof_begin(K_BWD_DQ, stream);
   hipLaunchKernelGGL((bwd_dq_kernel<D, ROPE>), dim3(nqt * a.B * a.H), dim3(256), C::LDS_BYTES, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.o, kk, vv,
                      (const uint16_t*)a.dout, a.lse, (const float*)a.kscale,
                      (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.qhat, a.delta,
-                     a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps, tile_group);
+                     a.lse2, (uint16_t*)a.dq, a.T, a.H, G, W, a.eps, tile_group, cpx);
   prof_end(t2);
   return hipGetLastError();
 }

@@ -92,12 +92,13 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : (D >= 128 ? 3 : 4)) void attn_f
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ kscale,
     const uint16_t* __restrict__ rcos, const uint16_t* __restrict__ rsin,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int G, int W, float eps) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H, int G, int W, float eps,
+    int cpx) {
   using C = FwdCfg<D, ROPE>;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int nqt = (T + C::BM - 1) / C::BM;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int lid = xcd_remap_paired(blockIdx.x, gridDim.x, cpx);
   int bh, qt;
   query_tile_of(lid, nqt, gridDim.x / nqt, kTileGroupFwd, &bh, &qt);
   const int b = bh / H, h = bh % H;
@@ -430,6 +431,13 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.T + C::BM - 1) / C::BM;
   const int nblk = nqt * a.B * a.H;
   const int W = eff_window(a.T, a.window);
+  // a grid that the CUs hold at once pairs heavy with light tiles per CU
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+    return hipErrorInvalidDevice;
+  const long long slots = (long long)ncu * (D >= 256 ? 1 : (D >= 128 ? 3 : 4));
+  const int cpx = (nblk <= slots && ncu % 8 == 0) ? ncu / 8 : 0;
   // more than 64 KiB of dynamic LDS must be opted into, once per kernel
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(attn_fwd_kernel<D, ROPE>),
@@ -440,7 +448,7 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.q, (const uint16_t*)(ROPE ? a.kr : a.k),
                      (const uint16_t*)(a.ve ? a.vr : a.v), (const float*)a.kscale,
                      (const uint16_t*)a.rcos, (const uint16_t*)a.rsin, (uint16_t*)a.o, a.lse, a.T, a.H,
-                     a.H / a.Hkv, W, a.eps);
+                     a.H / a.Hkv, W, a.eps, cpx);
   prof_end(t1);
   return hipGetLastError();
 }

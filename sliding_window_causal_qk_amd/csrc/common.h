@@ -360,6 +360,22 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return (bid & 7) * (nblk >> 3) + (bid >> 3);
 }
 
+// The same for a grid that the CUs hold all at once (cpx = CUs per XCD; 0:
+// plain xcd_remap).  An XCD's k-th workgroup then lands, round by round, on
+// CU k mod cpx, so round j = k / cpx takes the logical ids of its range in
+// reverse when j is odd: with the ids in heaviest-first order, the CU that
+// gets the heaviest tile of round 0 gets the lightest of round 1.
+__device__ __forceinline__ int xcd_remap_paired(int bid, int nblk, int cpx) {
+  if ((nblk & 7) != 0) return bid;
+  const int per = nblk >> 3;
+  int k = bid >> 3;
+  if (cpx > 0) {
+    const int j = k / cpx, c = k - j * cpx;
+    if (j & 1) k = j * cpx + (min(cpx, per - j * cpx) - 1 - c);
+  }
+  return (bid & 7) * per + k;
+}
+
 // Query tile of logical workgroup `lid` for the query-tiled kernels (forward,
 // dQ), heaviest first: the nbh (batch, head) slices go in groups of gb; inside
 // a group, tile rank r (0 = the last, heaviest query tile) of every slice

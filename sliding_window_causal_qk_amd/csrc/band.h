@@ -73,7 +73,8 @@ SW_HD int tile_class(int q_lo, int q_hi, int kv_lo, int kv_hi, int T, int W) {
 // mirrored positions of a causal band have band lengths that sum to about a
 // constant, so each workgroup's pairs of rounds carry about equal work.
 // mirror_from() is the first mirrored round (the number of rounds when none
-// is); it divides, so a kernel computes it once.
+// is); the launcher computes it and passes it to the kernels, which compile the
+// mirrored schedule only when some round is mirrored.
 SW_HD int mirror_from(int g8, int n8, int nkt) {
   const int rounds = (n8 + g8 - 1) / g8;
   return ((rounds & 1) == 0 && rounds % nkt != 0) ? rounds / 2 : rounds;

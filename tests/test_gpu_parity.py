@@ -546,6 +546,20 @@ def test_stack_and_long_workloads_sampled(torch_dev, name, layer):
     _sampled_check(torch_dev, wl, layer, window, slices)
 
 
+
+def test_partial_schedule_rounds(torch_dev):
+    """37 query tiles and 37 key tiles per (batch, head), 8 heads: 296 of each,
+    so the forward and dQ grids fit the CUs at once with a last, partial round
+    of 5 workgroups per XCD whose order is reversed, and the persistent dK/dV
+    kernel runs two rounds, the second mirrored and partial (5 of 32 tiles per
+    XCD).  Every element of one (batch, head) slice; sampled rows and keys
+    (one key in every key tile) of two more."""
+    from workloads import Workload
+    wl = Workload("partial_rounds", B=1, T=37 * 128, H=8, D=128, pattern="W", n_layer=1, seed0=777,
+                  explicit_window=300)
+    _say(f"[parity] B={wl.B} T={wl.T} H={wl.H} D={wl.D} W=300: partial schedule rounds")
+    _sampled_check(torch_dev, wl, 0, 300, [(0, 0), (0, 7)], whole=[(0, 3)])
+
 # ------------------------------------------------------------ structured probes
 
 def test_probe_one_hot_value_marks_window_edge(torch_dev):
